@@ -201,35 +201,41 @@ void kpo_scores(const int32_t* cu, int32_t num_docs, const int32_t* cu_pools, in
                 const uint8_t* k_codes, const float* k_scales,
                 const float* q_rot, const float* k_rot, int32_t mode,
                 const float* w, int32_t h_idx, int32_t d_idx, float* scores) {
-#pragma omp parallel for schedule(dynamic, 1)
+    double dec[256];                    /* the value of every E4M3 code */
+    for (int c = 0; c < 256; ++c) dec[c] = (double)kpo_e4m3_decode((uint8_t)c);
+    int32_t* lo = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_q + 1));
+    int32_t* nv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_q + 1));
     for (int32_t i = 0; i < num_q; ++i) {
+        int32_t ts = 0;
         int32_t t = q_pos ? q_pos[i] : i;
-        int32_t pool_lo = 0, n_vis = 0, tail_start = 0;
-        float* row = scores + (int64_t)i * max_pools;
-        for (int32_t p = 0; p < max_pools; ++p) row[p] = -INFINITY;
-        if (kpo_query_info(cu, num_docs, cu_pools, kpool, t, &pool_lo, &n_vis, &tail_start) < 0) continue;
-        for (int32_t j = 0; j < n_vis; ++j) {
-            int32_t p = pool_lo + j;
+        lo[i] = 0;
+        nv[i] = 0;
+        kpo_query_info(cu, num_docs, cu_pools, kpool, t, &lo[i], &nv[i], &ts);
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t i = 0; i < num_q; ++i) {
+        for (int32_t p = 0; p < max_pools; ++p) {
+            float* out = scores + (int64_t)i * max_pools + p;
+            if (p < lo[i] || p >= lo[i] + nv[i]) { *out = -INFINITY; continue; }
             double acc = 0.0;
             for (int32_t h = 0; h < h_idx; ++h) {
                 int64_t qo = ((int64_t)i * h_idx + h) * d_idx, ko = (int64_t)p * d_idx;
-                double v;
+                double v, dot = 0.0;
                 if (mode == 0) {
-                    double dot = 0.0;
-                    for (int32_t c = 0; c < d_idx; ++c)
-                        dot += (double)kpo_e4m3_decode(q_codes[qo + c]) * (double)kpo_e4m3_decode(k_codes[ko + c]);
+                    for (int32_t c = 0; c < d_idx; ++c) dot += dec[q_codes[qo + c]] * dec[k_codes[ko + c]];
                     v = (double)q_scales[(int64_t)i * h_idx + h] * (double)k_scales[p] * dot;
                 } else {
-                    double dot = 0.0;
                     for (int32_t c = 0; c < d_idx; ++c) dot += (double)q_rot[qo + c] * (double)k_rot[ko + c];
                     v = dot;
                 }
                 if (v < 0.0) v = 0.0;
                 acc += (double)w[(int64_t)i * h_idx + h] * v;
             }
-            row[p] = (float)acc;
+            *out = (float)acc;
         }
     }
+    free(lo);
+    free(nv);
 }
 
 /* ----------------------------------------------------------------- top-k -- */
@@ -285,7 +291,7 @@ void kpo_topk(const int32_t* cu, int32_t num_docs, const int32_t* cu_pools, int3
  * reference path of [P1-AB] with the index row as its mask. */
 void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t num_q,
                     int32_t num_kv, int32_t heads, int32_t d_latent, int32_t row_width,
-                    float scale, float* out, float* lse) {
+                    float scale, float* out, float* lse, float* out_abs) {
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int32_t i = 0; i < num_q; ++i) {
         for (int32_t h = 0; h < heads; ++h) {
@@ -293,6 +299,7 @@ void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indice
             const uint16_t* qh = q + ((int64_t)i * heads + h) * d_latent;
             double* s = (double*)malloc(sizeof(double) * (size_t)row_width + 1);
             double* o = (double*)calloc((size_t)d_latent, sizeof(double));
+            double* oa = (double*)calloc((size_t)d_latent, sizeof(double));
             double m = -INFINITY;
             for (int32_t j = 0; j < row_width; ++j) {
                 int32_t r = row[j];
@@ -304,8 +311,10 @@ void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indice
                 if (s[j] > m) m = s[j];
             }
             float* oh = out + ((int64_t)i * heads + h) * d_latent;
+            float* oah = out_abs ? out_abs + ((int64_t)i * heads + h) * d_latent : NULL;
             if (m == -INFINITY) {
                 for (int32_t c = 0; c < d_latent; ++c) oh[c] = 0.0f;
+                if (oah) for (int32_t c = 0; c < d_latent; ++c) oah[c] = 0.0f;
                 if (lse) lse[(int64_t)i * heads + h] = -INFINITY;
             } else {
                 double den = 0.0;
@@ -314,13 +323,19 @@ void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indice
                     if (r < 0 || r >= num_kv) continue;
                     double p = exp(s[j] - m);
                     den += p;
-                    for (int32_t c = 0; c < d_latent; ++c) o[c] += p * bf16_value(kv[(int64_t)r * d_latent + c]);
+                    for (int32_t c = 0; c < d_latent; ++c) {
+                        double v = bf16_value(kv[(int64_t)r * d_latent + c]);
+                        o[c] += p * v;
+                        oa[c] += p * fabs(v);
+                    }
                 }
                 for (int32_t c = 0; c < d_latent; ++c) oh[c] = (float)(o[c] / den);
+                if (oah) for (int32_t c = 0; c < d_latent; ++c) oah[c] = (float)(oa[c] / den);
                 if (lse) lse[(int64_t)i * heads + h] = (float)(m + log(den));
             }
             free(s);
             free(o);
+            free(oa);
         }
     }
 }

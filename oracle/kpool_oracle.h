@@ -93,10 +93,12 @@ void kpo_topk(const int32_t* cu_seqlens, int32_t num_docs, const int32_t* cu_poo
 /* Sparse MLA forward [P4-S2, P2-CL, P1-AB], as dense attention of each query
  * over the rows its index row names (K = V = latent):
  *   o[t,h,:] = softmax_j(scale <q[t,h], kv[idx_j]>) . kv[idx_j],  lse natural log.
- * Entries outside [0, num_kv) are masked; an empty row gives o = 0, lse = -inf. */
+ * Entries outside [0, num_kv) are masked; an empty row gives o = 0, lse = -inf.
+ * out_abs (NULLABLE) receives sum_j softmax_j |kv[idx_j]|, the magnitude of
+ * the terms each output element sums (the scale of its rounding error). */
 void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t num_q,
                     int32_t num_kv, int32_t heads, int32_t d_latent, int32_t row_width,
-                    float scale, float* out, float* lse);
+                    float scale, float* out, float* lse, float* out_abs);
 
 /* Threads the OpenMP runtime will use (for reporting). */
 int32_t kpo_num_threads(void);

@@ -48,7 +48,7 @@ def lib():
         L.kpo_scores.restype = None
         L.kpo_topk.argtypes = [P, i32, P, i32, P, i32, i32, P, i32, i32, P, P]
         L.kpo_topk.restype = None
-        L.kpo_sparse_mla.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P]
+        L.kpo_sparse_mla.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, P]
         L.kpo_sparse_mla.restype = None
         L.kpo_num_threads.argtypes = []
         L.kpo_num_threads.restype = i32
@@ -201,17 +201,19 @@ def topk(cu, cu_pools, kpool, q_pos, scores_, topk_, row_width):
     return idx, nv
 
 
-def sparse_mla(q, kv, indices, scale: float):
-    """(out [Tq,H,D] f32, lse [Tq,H] f32) of absorbed sparse MLA over the index rows."""
+def sparse_mla(q, kv, indices, scale: float, with_abs: bool = False):
+    """(out [Tq,H,D] f32, lse [Tq,H] f32) of absorbed sparse MLA over the index rows;
+    with_abs adds out_abs = sum_j softmax_j |kv_j| (the error scale of each output)."""
     q = _c(q, np.uint16)
     kv = _c(kv, np.uint16)
     indices = _c(indices, np.int32)
     Tq, H, D = q.shape
     out = np.zeros((Tq, H, D), np.float32)
     lse = np.zeros((Tq, H), np.float32)
+    oabs = np.zeros((Tq, H, D), np.float32) if with_abs else None
     lib().kpo_sparse_mla(_p(q), _p(kv), _p(indices), Tq, kv.shape[0], H, D, indices.shape[1],
-                         float(scale), _p(out), _p(lse))
-    return out, lse
+                         float(scale), _p(out), _p(lse), _p(oabs))
+    return (out, lse, oabs) if with_abs else (out, lse)
 
 
 # ------------------------------------------------------------- pipeline -----

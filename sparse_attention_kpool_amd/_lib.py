@@ -1,0 +1,226 @@
+"""ctypes binding of libkpool.so: the C ABI of include/kpool.h with torch
+tensors for device memory and the current torch stream.
+
+Argument marshalling only: each wrapper checks dtypes, devices and shapes,
+allocates its outputs with ``torch.empty`` and calls one C entry point. Every
+step of the computation runs in the HIP kernels. There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkpool.so")
+
+KP_OK, KP_ERR_INVALID_ARG, KP_ERR_UNSUPPORTED, KP_ERR_HIP = 0, 1, 2, 3
+_STATUS = {0: "KP_OK", 1: "KP_ERR_INVALID_ARG", 2: "KP_ERR_UNSUPPORTED", 3: "KP_ERR_HIP"}
+
+# (name, restype, argtypes) of every exported entry point, in header order.
+_P, _I, _F, _Z = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+SIGNATURES = [
+    ("kp_last_error", C.c_char_p, []),
+    ("kp_version", _I, []),
+    ("kp_row_width", _I, [_I, _I]),
+    ("kpool_build", _I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    ("indexer_rotate_quant", _I, [_P, _I, _I, _I, _P, _P, _P]),
+    ("kp_indexer_workspace_bytes", _Z, [_I, _I, _I, _I]),
+    ("indexer_score_topk", _I, [_P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                _P, _P, _P, _P, _Z, _P]),
+    ("indexer_topk_from_scores", _I, [_P, _I, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
+    ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    ("kp_check_inputs", _I, [_P, _I, _I, _P, _I, _P]),
+]
+
+
+class KpoolError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libkpool.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_attention_kpool_amd.build` (hipcc, gfx950)")
+        L = C.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != KP_OK:
+        raise KpoolError(status, lib().kp_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ helpers ---
+def kp_row_width(kpool: int, topk_pools: int) -> int:
+    return int(lib().kp_row_width(kpool, topk_pools))
+
+
+def kp_version() -> int:
+    return int(lib().kp_version())
+
+
+def kp_indexer_workspace_bytes(num_q: int, max_pools: int, h_idx: int, d_idx: int) -> int:
+    return int(lib().kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx))
+
+
+# -------------------------------------------------------------- entry points --
+def kpool_build(cu_seqlens: torch.Tensor, k_idx: torch.Tensor, gate: torch.Tensor, ape: torch.Tensor,
+                kpool: int = 4, with_f32: bool = False):
+    """Pool layout and rotated FP8 pooled keys.
+    Returns (cu_pools, pool_start, pooled_k_fp8, pooled_k_scale, pooled_k_f32 or None)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(gate, "gate", torch.bfloat16, 2)
+    _need(ape, "ape", torch.float32, 2)
+    T, d = k_idx.shape
+    if gate.shape != k_idx.shape or ape.shape != (kpool, d):
+        raise ValueError("gate must match k_idx and ape must be [kpool, d_idx]")
+    B = cu_seqlens.shape[0] - 1
+    dev = k_idx.device
+    cap = T // kpool
+    cu_pools = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    pool_start = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)[:cap]
+    k8 = torch.empty((max(cap, 1), d), dtype=torch.uint8, device=dev)[:cap]
+    ks = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)[:cap]
+    kf = torch.empty((max(cap, 1), d), dtype=torch.float32, device=dev)[:cap] if with_f32 else None
+    _check(lib().kpool_build(_ptr(cu_seqlens), B, T, _ptr(k_idx), _ptr(gate), _ptr(ape), d, kpool,
+                             _ptr(cu_pools), _ptr(pool_start), _ptr(k8), _ptr(ks), _ptr(kf), _stream(dev)))
+    return cu_pools, pool_start, k8, ks, kf
+
+
+def indexer_rotate_quant(q_idx: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Rotated FP8 indexer queries: (codes uint8 [Tq,H_I,D_I], scales f32 [Tq,H_I])."""
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    Tq, h, d = q_idx.shape
+    codes = torch.empty((Tq, h, d), dtype=torch.uint8, device=q_idx.device)
+    scales = torch.empty((Tq, h), dtype=torch.float32, device=q_idx.device)
+    _check(lib().indexer_rotate_quant(_ptr(q_idx), Tq, h, d, _ptr(codes), _ptr(scales), _stream(q_idx.device)))
+    return codes, scales
+
+
+def indexer_score_topk(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, pooled_k_fp8: torch.Tensor,
+                       pooled_k_scale: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,
+                       num_tokens: int, kpool: int = 4, topk_pools: int = 512,
+                       row_width: Optional[int] = None, q_pos: Optional[torch.Tensor] = None,
+                       return_scores: bool = False, workspace: Optional[torch.Tensor] = None):
+    """FP8 indexer scoring and top-k index rows.
+    Returns (indices int32 [Tq,W], num_valid int32 [Tq], scores f32 [Tq,max_pools] or None)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(cu_pools, "cu_pools", torch.int32, 1)
+    _need(pooled_k_fp8, "pooled_k_fp8", torch.uint8, 2)
+    _need(pooled_k_scale, "pooled_k_scale", torch.float32, 1)
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(w_idx, "w_idx", torch.float32, 2)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, 1)
+    Tq, h, d = q_idx.shape
+    dev = q_idx.device
+    max_pools = num_tokens // kpool
+    W = row_width if row_width is not None else kp_row_width(kpool, topk_pools)
+    indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
+    num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
+    scores = torch.empty((Tq, max_pools), dtype=torch.float32, device=dev) if return_scores else None
+    need = kp_indexer_workspace_bytes(Tq, max_pools, h, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().indexer_score_topk(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, num_tokens, _ptr(cu_pools),
+                                    max_pools, _ptr(pooled_k_fp8), _ptr(pooled_k_scale), _ptr(q_pos), Tq,
+                                    _ptr(q_idx), _ptr(w_idx), h, d, kpool, topk_pools, W, _ptr(indices),
+                                    _ptr(num_valid), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                    _stream(dev)))
+    return indices, num_valid, scores
+
+
+def indexer_topk_from_scores(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, scores: torch.Tensor,
+                             num_tokens: int, kpool: int = 4, topk_pools: int = 512,
+                             row_width: Optional[int] = None, q_pos: Optional[torch.Tensor] = None):
+    """Top-k index rows of a given score tensor [Tq, num_tokens // kpool]."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(cu_pools, "cu_pools", torch.int32, 1)
+    _need(scores, "scores", torch.float32, 2)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, 1)
+    Tq, max_pools = scores.shape
+    dev = scores.device
+    W = row_width if row_width is not None else kp_row_width(kpool, topk_pools)
+    indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
+    num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
+    _check(lib().indexer_topk_from_scores(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, num_tokens,
+                                          _ptr(cu_pools), max_pools, _ptr(q_pos), Tq, _ptr(scores), kpool,
+                                          topk_pools, W, _ptr(indices), _ptr(num_valid), _stream(dev)))
+    return indices, num_valid
+
+
+def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, softmax_scale: float,
+                   return_lse: bool = True, out: Optional[torch.Tensor] = None):
+    """Absorbed sparse latent attention: (out bf16 [Tq,H,D], lse f32 [Tq,H] or None)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv, "kv", torch.bfloat16, 2)
+    _need(indices, "indices", torch.int32, 2)
+    Tq, H, D = q.shape
+    if kv.shape[1] != D or indices.shape[0] != Tq:
+        raise ValueError("kv must be [num_kv, d_latent] and indices [num_q, row_width]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+    lse = torch.empty((Tq, H), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), Tq, kv.shape[0], H, D, indices.shape[1],
+                                float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def kp_check_inputs(cu_seqlens: torch.Tensor, num_tokens: int, q_pos: Optional[torch.Tensor] = None) -> None:
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    nq = 0 if q_pos is None else q_pos.shape[0]
+    _check(lib().kp_check_inputs(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, num_tokens, _ptr(q_pos), nq,
+                                 _stream(cu_seqlens.device)))
+
+
+def dsa_forward(cu_seqlens, k_idx, gate, ape, q_idx, w_idx, q, kv, *, kpool=4, topk_pools=512,
+                softmax_scale, q_pos=None, workspace=None):
+    """One KPool-DSA forward: kpool_build, indexer_score_topk, sparse_mla_fwd."""
+    cu_pools, _, k8, ks, _ = kpool_build(cu_seqlens, k_idx, gate, ape, kpool)
+    idx, nv, _ = indexer_score_topk(cu_seqlens, cu_pools, k8, ks, q_idx, w_idx, k_idx.shape[0], kpool,
+                                    topk_pools, q_pos=q_pos, workspace=workspace)
+    out, lse = sparse_mla_fwd(q, kv, idx, softmax_scale)
+    return out, lse, idx, nv

@@ -1,0 +1,265 @@
+// C ABI of libkpool (declared in include/kpool.h): host-side argument checks,
+// the gfx950 device check, workspace carving, and kernel launches.
+#include "kpool.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kp_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kp_status fail(kp_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+kp_status ok() { return KP_OK; }
+
+kp_status hip_fail(hipError_t e, const char* where) {
+    return fail(KP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::mutex g_dev_mu;
+int g_dev_ok[64];
+
+kp_status device_check() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(KP_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (g_dev_ok[dev] == 2) g_err = std::string("device is ") + prop.gcnArchName + ", not gfx950";
+    }
+    if (g_dev_ok[dev] != 1) return fail(KP_ERR_UNSUPPORTED, "libkpool runs on gfx950 (MI355X) only");
+    return KP_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool pow2_idx(int d) { return d == 32 || d == 64 || d == 128; }
+
+float hadamard_norm(int n) { return (float)(1.0 / std::sqrt((double)n)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kp_last_error(void) { return g_err.c_str(); }
+
+int32_t kp_version(void) { return 100; }
+
+int32_t kp_row_width(int32_t kpool, int32_t topk_pools) {
+    if (kpool < 1 || topk_pools < 0) return -1;
+    long long raw = (long long)kpool * topk_pools + kpool - 1;
+    long long w = (raw + 127) / 128 * 128;
+    if (w > 0x7FFFFFFFLL) return -1;
+    return (int32_t)w;
+}
+
+kp_status kpool_build(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                      const uint16_t* k_idx, const uint16_t* gate, const float* ape,
+                      int32_t d_idx, int32_t kpool,
+                      int32_t* cu_pools, int32_t* pool_start,
+                      uint8_t* pooled_k_fp8, float* pooled_k_scale, float* pooled_k_f32,
+                      hipStream_t stream) {
+    g_err.clear();
+    if (num_docs < 0 || num_tokens < 0) return fail(KP_ERR_INVALID_ARG, "negative size");
+    if (kpool < 1 || kpool > 16) return fail(KP_ERR_UNSUPPORTED, "kpool must be in 1..16 (got %d)", kpool);
+    if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+    if (!cu_seqlens || !cu_pools) return fail(KP_ERR_INVALID_ARG, "cu_seqlens and cu_pools are required");
+    if (num_tokens == 0 && num_docs == 0) return ok();
+    if (num_docs == 0) return fail(KP_ERR_INVALID_ARG, "num_tokens > 0 needs at least one document");
+    const int pool_cap = num_tokens / kpool;
+    if (pool_cap > 0 && (!k_idx || !gate || !ape || !pool_start || !pooled_k_fp8 || !pooled_k_scale))
+        return fail(KP_ERR_INVALID_ARG, "k_idx, gate, ape, pool_start, pooled_k_fp8 and pooled_k_scale are required");
+    kp_status st = device_check();
+    if (st != KP_OK) return st;
+    hipError_t e = kp::launch_layout_pool(cu_seqlens, num_docs, num_tokens, k_idx, gate, ape, d_idx, kpool,
+                                          hadamard_norm(d_idx), cu_pools, pool_start, pooled_k_fp8,
+                                          pooled_k_scale, pooled_k_f32, stream);
+    if (e != hipSuccess) return hip_fail(e, "kpool_build launch");
+    return ok();
+}
+
+kp_status indexer_rotate_quant(const uint16_t* q_idx, int32_t num_q, int32_t h_idx, int32_t d_idx,
+                               uint8_t* codes, float* scales, hipStream_t stream) {
+    g_err.clear();
+    if (num_q < 0 || h_idx < 1) return fail(KP_ERR_INVALID_ARG, "num_q must be >= 0 and h_idx >= 1");
+    if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+    if (num_q == 0) return ok();
+    if (!q_idx || !codes || !scales) return fail(KP_ERR_INVALID_ARG, "q_idx, codes and scales are required");
+    kp_status st = device_check();
+    if (st != KP_OK) return st;
+    hipError_t e = kp::launch_rotate_quant(q_idx, (long long)num_q * h_idx, d_idx, hadamard_norm(d_idx), codes,
+                                           scales, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer_rotate_quant launch");
+    return ok();
+}
+
+size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx) {
+    if (num_q <= 0 || max_pools < 0 || h_idx < 1 || d_idx < 1) return 0;
+    size_t q8 = align256((size_t)num_q * h_idx * d_idx);
+    size_t sq = align256((size_t)num_q * h_idx * sizeof(float));
+    size_t sc = align256((size_t)num_q * (size_t)max_pools * sizeof(float));
+    return q8 + sq + sc;
+}
+
+static kp_status check_topk_args(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                 const int32_t* cu_pools, int32_t max_pools, const int32_t* q_pos,
+                                 int32_t num_q, int32_t kpool, int32_t topk_pools, int32_t row_width,
+                                 const int32_t* indices) {
+    if (num_docs < 0 || num_tokens < 0 || num_q < 0 || max_pools < 0)
+        return fail(KP_ERR_INVALID_ARG, "negative size");
+    if (kpool < 1 || kpool > 16) return fail(KP_ERR_UNSUPPORTED, "kpool must be in 1..16 (got %d)", kpool);
+    if (topk_pools < 0) return fail(KP_ERR_INVALID_ARG, "topk_pools must be >= 0");
+    if (max_pools != num_tokens / kpool)
+        return fail(KP_ERR_INVALID_ARG, "max_pools must equal num_tokens / kpool (%d)", num_tokens / kpool);
+    const long long need = (long long)kpool * topk_pools + kpool - 1;
+    if (row_width % 128 != 0 || row_width < need || row_width < 128)
+        return fail(KP_ERR_INVALID_ARG, "row_width %d must be a multiple of 128 and >= %lld", row_width, need);
+    if (num_q == 0) return KP_OK;
+    if (num_docs == 0 || num_tokens == 0) return fail(KP_ERR_INVALID_ARG, "queries need a non-empty row");
+    if (!q_pos && num_q != num_tokens) return fail(KP_ERR_INVALID_ARG, "q_pos == NULL requires num_q == num_tokens");
+    if (!cu_seqlens || !cu_pools || !indices)
+        return fail(KP_ERR_INVALID_ARG, "cu_seqlens, cu_pools and indices are required");
+    return KP_OK;
+}
+
+kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                             const int32_t* cu_pools, int32_t max_pools,
+                             const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
+                             const int32_t* q_pos, int32_t num_q,
+                             const uint16_t* q_idx, const float* w_idx,
+                             int32_t h_idx, int32_t d_idx, int32_t kpool,
+                             int32_t topk_pools, int32_t row_width,
+                             int32_t* indices, int32_t* num_valid, float* scores,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    kp_status st = check_topk_args(cu_seqlens, num_docs, num_tokens, cu_pools, max_pools, q_pos, num_q, kpool,
+                                   topk_pools, row_width, indices);
+    if (st != KP_OK) return st;
+    if (h_idx < 1 || h_idx > 64) return fail(KP_ERR_UNSUPPORTED, "h_idx must be in 1..64 (got %d)", h_idx);
+    if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+    if (num_q == 0) return ok();
+    if (!q_idx || !w_idx) return fail(KP_ERR_INVALID_ARG, "q_idx and w_idx are required");
+    if (max_pools > 0 && (!pooled_k_fp8 || !pooled_k_scale))
+        return fail(KP_ERR_INVALID_ARG, "pooled_k_fp8 and pooled_k_scale are required");
+    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx);
+    if (!workspace || workspace_bytes < need)
+        return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    st = device_check();
+    if (st != KP_OK) return st;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* q8 = ws;
+    float* sq = reinterpret_cast<float*>(ws + align256((size_t)num_q * h_idx * d_idx));
+    float* sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4));
+    if (scores) sc = scores;
+
+    hipError_t e = kp::launch_rotate_quant(q_idx, (long long)num_q * h_idx, d_idx, hadamard_norm(d_idx), q8, sq,
+                                           stream);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    if (scores) {
+        e = kp::launch_fill_f32(scores, (size_t)num_q * max_pools, -INFINITY, stream);
+        if (e != hipSuccess) return hip_fail(e, "score fill launch");
+    }
+    e = kp::launch_score(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w_idx, h_idx, d_idx,
+                         pooled_k_fp8, pooled_k_scale, max_pools, sc, stream);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
+    e = kp::launch_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, sc, max_pools, topk_pools, row_width,
+                        indices, num_valid, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return ok();
+}
+
+kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                   const int32_t* cu_pools, int32_t max_pools,
+                                   const int32_t* q_pos, int32_t num_q, const float* scores,
+                                   int32_t kpool, int32_t topk_pools, int32_t row_width,
+                                   int32_t* indices, int32_t* num_valid, hipStream_t stream) {
+    g_err.clear();
+    kp_status st = check_topk_args(cu_seqlens, num_docs, num_tokens, cu_pools, max_pools, q_pos, num_q, kpool,
+                                   topk_pools, row_width, indices);
+    if (st != KP_OK) return st;
+    if (num_q == 0) return ok();
+    if (!scores) return fail(KP_ERR_INVALID_ARG, "scores is required");
+    st = device_check();
+    if (st != KP_OK) return st;
+    hipError_t e = kp::launch_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, scores, max_pools,
+                                   topk_pools, row_width, indices, num_valid, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return ok();
+}
+
+kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
+                         int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_latent,
+                         int32_t row_width, float softmax_scale,
+                         uint16_t* out, float* lse, hipStream_t stream) {
+    g_err.clear();
+    if (num_q < 0 || num_kv < 0 || row_width < 1) return fail(KP_ERR_INVALID_ARG, "bad size");
+    if (heads < 1 || heads > 64) return fail(KP_ERR_UNSUPPORTED, "heads must be in 1..64 (got %d)", heads);
+    if (d_latent != 512 && d_latent != 64)
+        return fail(KP_ERR_UNSUPPORTED, "d_latent must be 512 or 64 (got %d)", d_latent);
+    if (row_width > kp::sparse_mla_max_row_width())
+        return fail(KP_ERR_UNSUPPORTED, "row_width above %d (got %d)", kp::sparse_mla_max_row_width(), row_width);
+    if (!std::isfinite(softmax_scale)) return fail(KP_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (num_q == 0) return ok();
+    if (!q || !indices || !out || (num_kv > 0 && !kv))
+        return fail(KP_ERR_INVALID_ARG, "q, kv, indices and out are required");
+    kp_status st = device_check();
+    if (st != KP_OK) return st;
+    const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    hipError_t e = kp::launch_sparse_mla(q, kv, indices, num_q, num_kv, heads, d_latent, row_width, scale_log2,
+                                         out, lse, stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
+    return ok();
+}
+
+kp_status kp_check_inputs(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                          const int32_t* q_pos, int32_t num_q, hipStream_t stream) {
+    g_err.clear();
+    if (num_docs < 0 || num_tokens < 0 || num_q < 0) return fail(KP_ERR_INVALID_ARG, "negative size");
+    if (!cu_seqlens) return fail(KP_ERR_INVALID_ARG, "cu_seqlens is required");
+    std::vector<int32_t> cu((size_t)num_docs + 1), qp((size_t)num_q);
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    e = hipMemcpy(cu.data(), cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy cu_seqlens");
+    if (cu[0] != 0) return fail(KP_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int d = 0; d < num_docs; ++d)
+        if (cu[d + 1] < cu[d]) return fail(KP_ERR_INVALID_ARG, "cu_seqlens decreases at %d", d + 1);
+    if (cu[num_docs] != num_tokens)
+        return fail(KP_ERR_INVALID_ARG, "cu_seqlens[num_docs] = %d, expected %d", cu[num_docs], num_tokens);
+    if (q_pos && num_q > 0) {
+        e = hipMemcpy(qp.data(), q_pos, qp.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpy q_pos");
+        for (int i = 0; i < num_q; ++i)
+            if (qp[i] < 0 || qp[i] >= num_tokens)
+                return fail(KP_ERR_INVALID_ARG, "q_pos[%d] = %d outside [0, %d)", i, qp[i], num_tokens);
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Device helpers shared by the gfx950 kernels of libkpool: vector types, MFMA
+// wrappers, the FP8 convert, wave shuffles, and the per-query document lookup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kp {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define KP_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- MFMA ------
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// D[4*(l/16) + i][l%16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x128, e4m3) * B(128x16, e4m3), unit block scales.
+// Lane l holds 32 A bytes of row l%16 and 32 B bytes of column l%16 (the same
+// k positions for A and B), and D[4*(l/16) + i][l%16].
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+    // operand formats 0/0 = FP8 E4M3; E8M0 scale 127 = 2^0 for both operands
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ----------------------------------------------------------------- FP8 ------
+// Four fp32 values to four OCP E4M3FN codes (round to nearest even), packed
+// little-endian: byte 0 holds x0.
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float x0, float x1, float x2, float x3) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, v, true);
+    return (uint32_t)v;
+}
+
+// --------------------------------------------------------------- bf16 -------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------- shuffles -----
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ float shfl_idx(float v, int src) { return __shfl(v, src, 64); }
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+    return v;
+}
+
+// --------------------------------------------------------- doc lookup -------
+// Document d holding token t: the d with cu[d] <= t < cu[d+1] (empty
+// documents are skipped because cu[d] == cu[d+1]).
+__device__ __forceinline__ int find_doc(const int32_t* __restrict__ cu, int num_docs, int t) {
+    int lo = 0, hi = num_docs + 1;  // first index with cu[i] > t lies in [lo, hi)
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] > t) hi = mid; else lo = mid + 1;
+    }
+    return lo - 1;
+}
+
+struct QueryPools {
+    int doc;        // document of the query
+    int pool_lo;    // global number of the document's first pool
+    int n_vis;      // complete pools of the document ending at or before t
+    int tail_start; // first token of the query's incomplete pool
+};
+
+__device__ __forceinline__ QueryPools query_pools(const int32_t* __restrict__ cu, int num_docs,
+                                                  const int32_t* __restrict__ cu_pools, int kpool,
+                                                  int t) {
+    QueryPools r;
+    r.doc = find_doc(cu, num_docs, t);
+    int start = cu[r.doc];
+    r.pool_lo = cu_pools[r.doc];
+    r.n_vis = (t - start + 1) / kpool;
+    r.tail_start = start + kpool * r.n_vis;
+    return r;
+}
+
+}  // namespace kp

@@ -1,0 +1,44 @@
+// Host-side launchers of the gfx950 kernels (internal to libkpool; the C ABI
+// in api.cpp validates arguments before calling any of these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kp {
+
+// Pool layout (cu_pools, pool_start) and rotated FP8 pooled keys.
+hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, const uint16_t* k_idx,
+                              const uint16_t* gate, const float* ape, int d_idx, int kpool,
+                              float norm, int32_t* cu_pools, int32_t* pool_start, uint8_t* k8,
+                              float* ks, float* kf32, hipStream_t stream);
+
+// Rotated FP8 indexer queries: rows = num_q * h_idx vectors of d_idx channels.
+hipError_t launch_rotate_quant(const uint16_t* q_idx, long long rows, int d_idx, float norm,
+                               uint8_t* codes, float* scales, hipStream_t stream);
+
+// Fill a float buffer with a constant.
+hipError_t launch_fill_f32(float* dst, size_t n, float value, hipStream_t stream);
+
+// FP8 indexer scores of the visible (query, pool) pairs; other entries untouched.
+hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                        const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
+                        const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
+                        int max_pools, float* scores, hipStream_t stream);
+
+// Top-k index rows from a score tensor (visible entries only are read).
+hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                       const int32_t* q_pos, int num_q, const float* scores, int max_pools,
+                       int topk, int row_width, int32_t* indices, int32_t* num_valid,
+                       hipStream_t stream);
+
+// Sparse latent attention over the index rows.
+hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int num_q,
+                             int num_kv, int heads, int d_latent, int row_width, float scale_log2,
+                             uint16_t* out, float* lse, hipStream_t stream);
+
+// Largest index row sparse_mla_fwd accepts.
+int sparse_mla_max_row_width();
+
+}  // namespace kp

@@ -1,0 +1,246 @@
+// Pool layout, k-pool compression, and the Hadamard + FP8 encoding of pooled
+// keys and indexer queries.
+//
+// prime-rl PR "GLM-5.3-Flash text model", Summary, third bullet: keys pooled
+// per document in groups of 4 from the document's first token, as a
+// per-channel softmax(gate + ape)-weighted mean; queries and pooled keys are
+// rotated by an fp32 butterfly Hadamard transform before FP8 scoring.
+//
+// One pooled key (or one query head vector) of n channels is handled by n/4
+// lanes, four consecutive channels per lane. The butterfly stages of stride 1
+// and 2 run inside a lane, the rest across lanes with xor shuffles; every
+// output of a stage is the single fp32 sum or difference of the same two
+// inputs as in the sequential Sylvester-order transform, so the rotated values
+// do not depend on how the vector is spread over lanes.
+#include "kp_device.h"
+#include "kp_launch.h"
+
+namespace kp {
+
+// ------------------------------------------------------------- layout -------
+// cu_pools[d+1] = cu_pools[d] + floor((cu[d+1] - cu[d]) / kpool); one block
+// scans the documents in chunks of its size.
+__global__ __launch_bounds__(1024) void layout_scan_kernel(const int32_t* __restrict__ cu,
+                                                           int num_docs, int kpool,
+                                                           int32_t* __restrict__ cu_pools) {
+    __shared__ int wave_tot[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) { carry_s = 0; cu_pools[0] = 0; }
+    __syncthreads();
+    for (int base = 0; base < num_docs; base += 1024) {
+        int d = base + tid;
+        int v = d < num_docs ? (cu[d + 1] - cu[d]) / kpool : 0;
+        // inclusive scan inside the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int u = __shfl_up(v, o, 64);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) wave_tot[wave] = v;
+        __syncthreads();
+        int add = carry_s;
+        for (int w = 0; w < wave; ++w) add += wave_tot[w];
+        if (d < num_docs) cu_pools[d + 1] = v + add;
+        __syncthreads();
+        if (tid == blockDim.x - 1) carry_s = v + add;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------- rotate + quantise -----------
+// x holds channels 4*j .. 4*j+3 of a vector of n = 4*L channels spread over L
+// consecutive lanes (j = lane % L). Orthonormal Walsh-Hadamard transform in
+// Sylvester order: stride 1, 2 in-lane, 4 .. n/2 across lanes; then one
+// multiply by `norm` = fp32(1/sqrt(n)).
+template <int L>
+__device__ __forceinline__ void fwht4(float (&x)[4], int lane, float norm) {
+    float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
+    x[0] = a0 + a2; x[2] = a0 - a2; x[1] = a1 + a3; x[3] = a1 - a3;
+#pragma unroll
+    for (int b = 1; b < L; b <<= 1) {
+        const bool upper = (lane & b) != 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float y = shfl_xor(x[e], b);
+            x[e] = upper ? (y - x[e]) : (x[e] + y);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = x[e] * norm;
+}
+
+// Per-vector scale s = amax/448 (1 when the vector is zero) and E4M3 codes of
+// x/s. Returns the four codes of this lane packed little-endian.
+template <int L>
+__device__ __forceinline__ uint32_t quant4(const float (&x)[4], float* scale_out) {
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    amax = group_max<L>(amax);
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    *scale_out = s;
+    return cvt_e4m3x4(x[0] / s, x[1] / s, x[2] / s, x[3] / s);
+}
+
+// ------------------------------------------------------------ keys ----------
+// One pool per L lanes. Capacity rows (num_tokens / kpool) past the last pool
+// get pool_start -1, zero codes and a zero scale.
+template <int L, int KP>
+__global__ __launch_bounds__(256) void pool_keys_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools,
+    const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ gate,
+    const float* __restrict__ ape, int kpool, int pool_cap, float norm,
+    int32_t* __restrict__ pool_start, uint8_t* __restrict__ k8, float* __restrict__ ks,
+    float* __restrict__ kf32) {
+    constexpr int N = 4 * L;
+    const int lane = threadIdx.x & 63;
+    const int j = lane % L;
+    const int p = (blockIdx.x * blockDim.x + threadIdx.x) / L;
+    if (p >= pool_cap) return;
+    const int total = cu_pools[num_docs];
+    if (p >= total) {
+        if (j == 0) { pool_start[p] = -1; ks[p] = 0.0f; }
+        reinterpret_cast<uint32_t*>(k8 + (size_t)p * N)[j] = 0u;
+        if (kf32) reinterpret_cast<float4*>(kf32 + (size_t)p * N)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    // document of pool p: the d with cu_pools[d] <= p < cu_pools[d+1]
+    int d = find_doc(cu_pools, num_docs, p);
+    const int s = cu[d] + kpool * (p - cu_pools[d]);
+
+    // per-channel softmax over the kpool tokens of the pool, then the weighted sum
+    float x[4];
+    if (KP > 0) {
+        // max-subtracted softmax over a fixed pool size, values held in registers
+        float a[KP > 0 ? KP : 1][4], kv[KP > 0 ? KP : 1][4];
+        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            uint2 g = reinterpret_cast<const uint2*>(gate + (size_t)(s + i) * N)[j];
+            uint2 k = reinterpret_cast<const uint2*>(k_idx + (size_t)(s + i) * N)[j];
+            float4 e = reinterpret_cast<const float4*>(ape + (size_t)i * N)[j];
+            a[i][0] = bf16_lo(g.x) + e.x; a[i][1] = bf16_hi(g.x) + e.y;
+            a[i][2] = bf16_lo(g.y) + e.z; a[i][3] = bf16_hi(g.y) + e.w;
+            kv[i][0] = bf16_lo(k.x); kv[i][1] = bf16_hi(k.x);
+            kv[i][2] = bf16_lo(k.y); kv[i][3] = bf16_hi(k.y);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m[c] = fmaxf(m[c], a[i][c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float den = 0.0f, num = 0.0f;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) {
+                float e = expf(a[i][c] - m[c]);
+                den += e;
+                num += e * kv[i][c];
+            }
+            x[c] = num / den;
+        }
+    } else {
+        // any pool size: running max with rescaled partial sums
+        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        float den[4] = {0.f, 0.f, 0.f, 0.f}, num[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kpool; ++i) {
+            uint2 g = reinterpret_cast<const uint2*>(gate + (size_t)(s + i) * N)[j];
+            uint2 k = reinterpret_cast<const uint2*>(k_idx + (size_t)(s + i) * N)[j];
+            float4 e = reinterpret_cast<const float4*>(ape + (size_t)i * N)[j];
+            float av[4] = {bf16_lo(g.x) + e.x, bf16_hi(g.x) + e.y, bf16_lo(g.y) + e.z, bf16_hi(g.y) + e.w};
+            float kk[4] = {bf16_lo(k.x), bf16_hi(k.x), bf16_lo(k.y), bf16_hi(k.y)};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float mn = fmaxf(m[c], av[c]);
+                float r = expf(m[c] - mn);   // 0 on the first token
+                float w = expf(av[c] - mn);
+                den[c] = den[c] * r + w;
+                num[c] = num[c] * r + w * kk[c];
+                m[c] = mn;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = num[c] / den[c];
+    }
+    if (kf32) reinterpret_cast<float4*>(kf32 + (size_t)p * N)[j] = make_float4(x[0], x[1], x[2], x[3]);
+    fwht4<L>(x, lane, norm);
+    float sc;
+    uint32_t codes = quant4<L>(x, &sc);
+    reinterpret_cast<uint32_t*>(k8 + (size_t)p * N)[j] = codes;
+    if (j == 0) { ks[p] = sc; pool_start[p] = s; }
+}
+
+// ---------------------------------------------------------- queries ---------
+// One (query, head) vector per L lanes: bf16 -> fp32 (exact), rotate, quantise.
+template <int L>
+__global__ __launch_bounds__(256) void rotate_quant_kernel(const uint16_t* __restrict__ q_idx,
+                                                           long long rows, float norm,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+    constexpr int N = 4 * L;
+    const int lane = threadIdx.x & 63;
+    const int j = lane % L;
+    const long long r = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / L;
+    if (r >= rows) return;
+    uint2 q = reinterpret_cast<const uint2*>(q_idx + (size_t)r * N)[j];
+    float x[4] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y)};
+    fwht4<L>(x, lane, norm);
+    float sc;
+    uint32_t c = quant4<L>(x, &sc);
+    reinterpret_cast<uint32_t*>(codes + (size_t)r * N)[j] = c;
+    if (j == 0) scales[r] = sc;
+}
+
+// ------------------------------------------------------------ launchers -----
+template <int KP>
+static void launch_pool_keys(int blocks, hipStream_t stream, int d_idx, const int32_t* cu, int num_docs,
+                             const int32_t* cu_pools, const uint16_t* k_idx, const uint16_t* gate,
+                             const float* ape, int kpool, int pool_cap, float norm, int32_t* pool_start,
+                             uint8_t* k8, float* ks, float* kf32) {
+    switch (d_idx) {
+        case 32:
+            pool_keys_kernel<8, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
+                                                            pool_cap, norm, pool_start, k8, ks, kf32);
+            break;
+        case 64:
+            pool_keys_kernel<16, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
+                                                             pool_cap, norm, pool_start, k8, ks, kf32);
+            break;
+        default:
+            pool_keys_kernel<32, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
+                                                             pool_cap, norm, pool_start, k8, ks, kf32);
+            break;
+    }
+}
+
+hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, const uint16_t* k_idx,
+                              const uint16_t* gate, const float* ape, int d_idx, int kpool,
+                              float norm, int32_t* cu_pools, int32_t* pool_start, uint8_t* k8,
+                              float* ks, float* kf32, hipStream_t stream) {
+    layout_scan_kernel<<<1, 1024, 0, stream>>>(cu, num_docs, kpool, cu_pools);
+    const int pool_cap = num_tokens / kpool;
+    if (pool_cap == 0) return hipGetLastError();
+    const int L = d_idx / 4;
+    const long long threads = (long long)pool_cap * L;
+    const int blocks = (int)((threads + 255) / 256);
+    if (kpool == 4)
+        launch_pool_keys<4>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
+                            norm, pool_start, k8, ks, kf32);
+    else
+        launch_pool_keys<0>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
+                            norm, pool_start, k8, ks, kf32);
+    return hipGetLastError();
+}
+
+hipError_t launch_rotate_quant(const uint16_t* q_idx, long long rows, int d_idx, float norm,
+                               uint8_t* codes, float* scales, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    const int L = d_idx / 4;
+    const long long threads = rows * L;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    switch (d_idx) {
+        case 32: rotate_quant_kernel<8><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
+        case 64: rotate_quant_kernel<16><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
+        default: rotate_quant_kernel<32><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kp

@@ -1,0 +1,87 @@
+"""The C ABI loads on a host without a GPU, exports every entry point its
+header declares, and rejects bad arguments before touching the device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kpool.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_attention_kpool_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_kpool_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(k\w+|indexer_\w+|sparse_\w+)\s*\(", src, re.M)))
+
+
+def test_header_symbols_exported(L):
+    from sparse_attention_kpool_amd import _lib
+    names = _declared()
+    assert set(names) == {n for n, _, _ in _lib.SIGNATURES}
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_row_width(L):
+    assert L.kp_row_width(4, 512) == 2176          # 2051 raw slots -> 2176
+    assert L.kp_row_width(4, 4) == 128
+    assert L.kp_row_width(4, 0) == 128
+    assert L.kp_row_width(1, 128) == 128
+    assert L.kp_row_width(1, 129) == 256
+    assert L.kp_row_width(0, 4) == -1 and L.kp_row_width(4, -1) == -1
+    assert L.kp_version() >= 100
+
+
+def test_workspace_size(L):
+    ws = L.kp_indexer_workspace_bytes(32768, 8192, 32, 128)
+    assert ws >= 32768 * 32 * 128 + 32768 * 32 * 4 + 32768 * 8192 * 4
+    assert ws % 256 == 0
+    assert L.kp_indexer_workspace_bytes(0, 8192, 32, 128) == 0
+
+
+def test_invalid_args_rejected_on_host(L):
+    """Each of these fails its host-side check and returns before any HIP call."""
+    P = C.c_void_p
+    fake = P(0x1000)
+    # kpool_build: bad kpool / d_idx / missing pointers
+    assert L.kpool_build(fake, 1, 64, fake, fake, fake, 128, 0, fake, fake, fake, fake, None, None) == 2
+    assert L.kpool_build(fake, 1, 64, fake, fake, fake, 100, 4, fake, fake, fake, fake, None, None) == 2
+    assert L.kpool_build(None, 1, 64, fake, fake, fake, 128, 4, fake, fake, fake, fake, None, None) == 1
+    assert b"required" in L.kp_last_error()
+    assert L.kpool_build(fake, -1, 64, fake, fake, fake, 128, 4, fake, fake, fake, fake, None, None) == 1
+    # empty row: a no-op
+    assert L.kpool_build(fake, 0, 0, None, None, None, 128, 4, fake, None, None, None, None, None) == 0
+    # indexer: row width not a multiple of 128 / too narrow / max_pools mismatch
+    args = lambda W, mp=16, nq=64, qpos=None: (fake, 1, 64, fake, mp, fake, fake, qpos, nq, fake, fake, 2, 32, 4,
+                                               4, W, fake, None, None, fake, 1 << 30, None)
+    assert L.indexer_score_topk(*args(100)) == 1
+    assert L.indexer_score_topk(*args(0)) == 1
+    assert L.indexer_score_topk(*args(128, mp=15)) == 1
+    assert L.indexer_score_topk(*args(128, nq=10)) == 1          # q_pos NULL needs num_q == num_tokens
+    assert L.indexer_score_topk(*args(128, nq=0)) == 0           # empty shard: no-op
+    # workspace too small
+    a = list(args(128))
+    a[20] = 16
+    assert L.indexer_score_topk(*a) == 1
+    assert b"workspace" in L.kp_last_error()
+    # unsupported head count / latent width
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 65, 512, 128, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 1
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
+    assert L.indexer_rotate_quant(fake, 4, 2, 48, fake, fake, None) == 2
+    assert L.indexer_topk_from_scores(fake, 1, 64, fake, 16, None, 64, None, 4, 4, 128, fake, None, None) == 1

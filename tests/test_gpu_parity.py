@@ -1,0 +1,299 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the
+C ABI, on the same seeded inputs. Each GPU stage is fed the oracle's upstream
+outputs so that errors do not compound; the end-to-end tests then run the
+GPU pipeline alone and compare what is unique (layout, selection where it
+covers every pool, attention on the oracle's rows).
+
+Bars: layout and index rows bit-exact; query FP8 codes bit-exact (same fp32
+butterfly order and IEEE division on both sides); pooled keys within fp32
+rounding with at most rare one-step FP8 code flips; scores, attention and lse
+within the tolerances of tests/_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests._util import (check_lse, check_out, check_scores, dev, dev_bf16, host, host_bf16_f32)
+from workloads import Workload, custom, spec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_kpool_amd as K
+    K.lib()
+    return K
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- layout -----
+LAYOUT_ROWS = [
+    [0, 64], [0, 2048], [0, 3, 11, 11, 20, 24, 25], [0, 1, 2, 3, 4, 5, 6, 7],
+    [0, 0, 0, 9], [0, 5, 5, 5, 100, 101, 333, 1000],
+]
+
+
+@pytest.mark.parametrize("cu", LAYOUT_ROWS + ["rand%d" % s for s in range(5)])
+def test_layout_bitexact(K, oracle_mod, cu):
+    if isinstance(cu, str):
+        rng = np.random.default_rng(int(cu[4:]))
+        lens = rng.integers(0, 40, size=int(rng.integers(1, 30)))
+        lens[rng.random(len(lens)) < 0.15] = 0
+        lens[0] += 1
+        cu = [0, *np.cumsum(lens).tolist()]
+    cu = np.array(cu, np.int32)
+    T = int(cu[-1])
+    _log("layout", cu.tolist()[:12])
+    s = custom("lay", T, cu, D_I=32)
+    wl = Workload(s)
+    cp, ps, k8, ks, _ = K.kpool_build(dev(cu), dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")),
+                                      dev(wl.ape()), 4)
+    want_cp, want_ps = oracle_mod.layout(cu, T, 4)
+    assert host(cp).tolist() == want_cp.tolist()
+    got_ps = host(ps)
+    assert got_ps[:len(want_ps)].tolist() == want_ps.tolist()
+    assert np.all(got_ps[len(want_ps):] == -1)
+
+
+# ------------------------------------------------------------ pooled keys ----
+@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k"])
+def test_pooled_keys(K, oracle_mod, name):
+    s = spec(name)
+    wl = Workload(s)
+    _log("keys", name)
+    cp, ps, k8, ks, kf = K.kpool_build(dev(s.cu), dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")),
+                                       dev(wl.ape()), s.kpool, with_f32=True)
+    _, want_ps = oracle_mod.layout(s.cu, s.T, s.kpool)
+    kc, kscale, pooled = oracle_mod.keys(wl.full("k_idx"), wl.full("gate"), wl.ape(), want_ps, s.kpool)
+    P = len(want_ps)
+    g_pooled = host(kf)[:P]
+    assert np.all(np.abs(g_pooled - pooled) <= 1e-5 * np.abs(pooled) + 1e-6)
+    g_codes = host(k8)[:P]
+    diff = g_codes != kc
+    assert diff.mean() <= 1e-3, f"{diff.mean():.2e} of key codes differ"
+    if diff.any():   # a flip is one step of the code (same sign, adjacent magnitude)
+        a = g_codes[diff].astype(int)
+        b = kc[diff].astype(int)
+        assert np.all((a ^ b) & 0x80 == 0) and np.all(np.abs((a & 0x7F) - (b & 0x7F)) == 1)
+    assert np.allclose(host(ks)[:P], kscale, rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k"])
+def test_query_codes_bitexact(K, oracle_mod, name):
+    s = spec(name)
+    wl = Workload(s)
+    q_idx = wl.full("q_idx")
+    _log("query codes", name, q_idx.shape)
+    codes, scales = K.indexer_rotate_quant(dev_bf16(q_idx))
+    qc, qs = oracle_mod.queries(q_idx)
+    assert np.array_equal(host(codes), qc)
+    assert np.array_equal(host(scales), qs)
+
+
+# ---------------------------------------------------------------- scoring ----
+def _oracle_keys(oracle_mod, s, wl):
+    cp, ps = oracle_mod.layout(s.cu, s.T, s.kpool)
+    kc, kscale, _ = oracle_mod.keys(wl.full("k_idx"), wl.full("gate"), wl.ape(), ps, s.kpool)
+    # capacity rows past the last pool: zero codes and scale, as the library writes them
+    cap = s.max_pools
+    k8 = np.zeros((cap, s.D_I), np.uint8)
+    k8[:len(ps)] = kc
+    sk = np.zeros(cap, np.float32)
+    sk[:len(ps)] = kscale
+    return cp, ps, k8, sk
+
+
+def _gpu_scores(K, s, wl, cp, k8, sk, rows=None):
+    qpos = s.query_positions()
+    q_idx = wl.full("q_idx")
+    w = wl.full("w")
+    if rows is not None:
+        qpos, q_idx, w = qpos[rows], q_idx[rows], w[rows]
+    idx, nv, sc = K.indexer_score_topk(dev(s.cu), dev(cp), dev(k8), dev(sk), dev_bf16(q_idx), dev(w), s.T,
+                                       s.kpool, s.topk, q_pos=dev(qpos.astype(np.int32)), return_scores=True)
+    return host(idx), host(nv), host(sc)
+
+
+@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k", "32k_rows", "decode1m_rows"])
+def test_scores_fed_oracle_keys(K, oracle_mod, name):
+    base = name.replace("_rows", "")
+    s = spec(base)
+    wl = Workload(s)
+    rng = np.random.default_rng(0)
+    rows = None
+    if name.endswith("_rows"):
+        nr = 4 if base == "decode1m" else 12
+        rows = np.unique(np.concatenate([rng.choice(s.Tq, nr, replace=False), [0, s.Tq - 1]]))
+    _log("scores", name, "rows", None if rows is None else rows.tolist())
+    cp, ps, k8, sk = _oracle_keys(oracle_mod, s, wl)
+    _, _, g_sc = _gpu_scores(K, s, wl, cp, k8, sk, rows)
+    qpos = s.query_positions() if rows is None else s.query_positions()[rows]
+    q_idx = wl.full("q_idx") if rows is None else wl.full("q_idx")[rows]
+    w = wl.full("w") if rows is None else wl.full("w")[rows]
+    qc, qs = oracle_mod.queries(q_idx)
+    ref = oracle_mod.scores(s.cu, cp, s.kpool, qpos, s.max_pools, w, qc, qs, k8[:len(ps)], sk[:len(ps)])
+    info = check_scores(g_sc, ref, name)
+    _log("  worst rel", info)
+
+
+# ------------------------------------------------------------------ top-k -----
+@pytest.mark.parametrize("case", ["tiny", "2k", "packed4k", "ties", "zeros", "negzero", "nan", "topk0",
+                                  "decode1m_rows"])
+def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
+    rng = np.random.default_rng(7)
+    if case in ("tiny", "2k", "packed4k"):
+        s = spec(case)
+        wl = Workload(s)
+        cp, ps, k8, sk = _oracle_keys(oracle_mod, s, wl)
+        qc, qs = oracle_mod.queries(wl.full("q_idx"))
+        qpos = s.query_positions()
+        sc = oracle_mod.scores(s.cu, cp, s.kpool, qpos, s.max_pools, wl.full("w"), qc, qs, k8[:len(ps)],
+                               sk[:len(ps)])
+        T, topk, cu = s.T, s.topk, s.cu
+    elif case == "decode1m_rows":
+        s = spec("decode1m")
+        wl = Workload(s)
+        cp, ps, k8, sk = _oracle_keys(oracle_mod, s, wl)
+        rows = np.array([0, 31, 63])
+        qpos = s.query_positions()[rows]
+        qc, qs = oracle_mod.queries(wl.full("q_idx")[rows])
+        sc = oracle_mod.scores(s.cu, cp, s.kpool, qpos, s.max_pools, wl.full("w")[rows], qc, qs, k8[:len(ps)],
+                               sk[:len(ps)])
+        T, topk, cu = s.T, s.topk, s.cu
+    else:
+        T = 5000
+        cu = np.array([0, 700, 700, 2900, 2903, 5000], np.int32)
+        cp, _ = oracle_mod.layout(cu, T, 4)
+        qpos = np.arange(T, dtype=np.int32)
+        sc = np.round(rng.standard_normal((T, T // 4)) * 2).astype(np.float32)     # heavy ties
+        if case == "zeros":
+            sc = np.maximum(sc, 0).astype(np.float32)
+        if case == "negzero":
+            sc[rng.random(sc.shape) < 0.3] = -0.0
+            sc[rng.random(sc.shape) < 0.3] = 0.0
+        if case == "nan":
+            sc[rng.random(sc.shape) < 0.01] = np.nan
+            sc[rng.random(sc.shape) < 0.01] = -np.inf
+        topk = 0 if case == "topk0" else 37
+    W = -(-(4 * topk + 3) // 128) * 128
+    _log("topk", case, sc.shape, topk)
+    ref_idx, ref_nv = oracle_mod.topk(cu, cp, 4, qpos, sc, topk, W)
+    g_idx, g_nv = K.indexer_topk_from_scores(dev(cu), dev(cp), dev(sc), T, 4, topk, W, q_pos=dev(qpos))
+    g_idx, g_nv = host(g_idx), host(g_nv)
+    assert np.array_equal(g_nv, ref_nv)
+    bad = np.nonzero(np.any(g_idx != ref_idx, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5]}"
+
+
+# ------------------------------------------------------------ sparse MLA -----
+def _oracle_rows(oracle_mod, s, wl, rows):
+    res = oracle_mod.dsa_forward(wl, q_rows=rows, with_mla=False)
+    return res["indices"], res["num_valid"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k", "32k_rows", "decode1m_rows"])
+def test_mla_fed_oracle_rows(K, oracle_mod, name):
+    base = name.replace("_rows", "")
+    s = spec(base)
+    wl = Workload(s)
+    rows = np.arange(s.Tq)
+    if name.endswith("_rows"):
+        rng = np.random.default_rng(1)
+        nr = 3 if base == "decode1m" else 10
+        rows = np.unique(np.concatenate([rng.choice(s.Tq, nr, replace=False), [0, 1, 2, 3, s.Tq - 1]]))
+    elif s.Tq > 512:
+        rows = np.unique(np.concatenate([np.arange(0, s.Tq, 97), [s.Tq - 1]]))
+    _log("mla", name, len(rows))
+    idx, nv = _oracle_rows(oracle_mod, s, wl, rows)
+    q = wl.full("q")[rows] if s.Tq * s.H * s.D <= (1 << 28) else \
+        np.concatenate([wl.rows("q", int(r), int(r) + 1) for r in rows])
+    kv = wl.full("kv")
+    g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), s.scale)
+    ref_out, ref_lse, ref_abs = oracle_mod.sparse_mla(q, kv, idx, s.scale, with_abs=True)
+    info = check_out(host_bf16_f32(g_out), ref_out, name, ref_abs)
+    check_lse(host(g_lse), ref_lse, name)
+    _log("  ", info)
+
+
+@pytest.mark.parametrize("case", ["scattered_mask", "empty_rows", "single", "duplicates", "heads40"])
+def test_mla_edge_rows(K, oracle_mod, case):
+    rng = np.random.default_rng(3)
+    H, D, N, W, Tq = 64, 512, 3000, 256, 9
+    if case == "heads40":
+        H = 40
+    q = (rng.standard_normal((Tq, H, D))).astype(np.float32)
+    kv = (rng.standard_normal((N, D))).astype(np.float32)
+    from workloads import f32_to_bf16_bits
+    q, kv = f32_to_bf16_bits(q), f32_to_bf16_bits(kv)
+    idx = rng.integers(0, N, size=(Tq, W)).astype(np.int32)
+    if case == "scattered_mask":
+        m = rng.random(idx.shape) < 0.4
+        idx[m] = rng.choice([-1, -5, N, N + 7, 2 ** 31 - 1], size=m.sum())
+    if case == "empty_rows":
+        idx[::2] = -1
+    if case == "single":
+        idx[:] = -1
+        idx[np.arange(Tq), rng.integers(0, W, Tq)] = rng.integers(0, N, Tq)
+    if case == "duplicates":
+        idx[:, 100:] = idx[:, :W - 100][:, :W - 100]
+    _log("mla edge", case)
+    g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), 1 / np.sqrt(D))
+    ref_out, ref_lse = oracle_mod.sparse_mla(q, kv, idx, 1 / np.sqrt(D))
+    check_out(host_bf16_f32(g_out), ref_out, case)
+    check_lse(host(g_lse), ref_lse, case)
+
+
+# ------------------------------------------------------------ end to end -----
+@pytest.mark.parametrize("name", ["tiny_dense", "2k"])
+def test_end_to_end_dense_cover(K, oracle_mod, name):
+    """Top-k covers every visible pool: the GPU pipeline's index rows must equal
+    the oracle's bit for bit whatever the scores, and attention must match."""
+    s = spec(name)
+    wl = Workload(s)
+    _log("e2e", name)
+    out, lse, idx, nv = K.dsa_forward(dev(s.cu), dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")),
+                                      dev(wl.ape()), dev_bf16(wl.full("q_idx")), dev(wl.full("w")),
+                                      dev_bf16(wl.full("q")), dev_bf16(wl.full("kv")), kpool=s.kpool,
+                                      topk_pools=s.topk, softmax_scale=s.scale)
+    rows = np.arange(s.Tq) if s.Tq <= 64 else np.unique(np.concatenate([np.arange(0, s.Tq, 61), [s.Tq - 1]]))
+    res = oracle_mod.dsa_forward(wl, q_rows=rows)
+    assert np.array_equal(host(idx)[rows], res["indices"])
+    assert np.array_equal(host(nv)[rows], res["num_valid"])
+    check_out(host_bf16_f32(out)[rows], res["out"], name)
+    check_lse(host(lse)[rows], res["lse"], name)
+
+
+@pytest.mark.parametrize("name", ["packed4k", "32k"])
+def test_end_to_end_selection_agreement(K, oracle_mod, name):
+    """GPU pipeline on its own: index rows stay in the query's document and at
+    or before it, and agree with the oracle's selection (the two differ only
+    where FP8 rounding of pooled keys flips a near-tie)."""
+    s = spec(name)
+    wl = Workload(s)
+    _log("e2e selection", name)
+    cu_d = dev(s.cu)
+    cp, ps, k8, ks, _ = K.kpool_build(cu_d, dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")),
+                                      dev(wl.ape()), s.kpool)
+    idx, nv, _ = K.indexer_score_topk(cu_d, cp, k8, ks, dev_bf16(wl.full("q_idx")), dev(wl.full("w")), s.T,
+                                      s.kpool, s.topk)
+    idx, nv = host(idx), host(nv)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(s.Tq, 24, replace=False), [s.Tq - 1]]))
+    res = oracle_mod.dsa_forward(wl, q_rows=rows, with_mla=False)
+    doc = np.searchsorted(s.cu, np.arange(s.T), side="right") - 1
+    jac = []
+    for i, t in enumerate(rows):
+        g = idx[t, :nv[t]]
+        assert nv[t] == res["num_valid"][i]
+        assert np.all(doc[g] == doc[t]) and np.all(g <= t) and np.all(np.diff(g) > 0)
+        assert np.all(idx[t, nv[t]:] == -1)
+        a, b = set(g.tolist()), set(res["indices"][i, :nv[t]].tolist())
+        jac.append(len(a & b) / len(a | b))
+    _log("  jaccard mean", np.mean(jac), "min", np.min(jac), "identical", np.mean(np.array(jac) == 1.0))
+    assert np.mean(jac) >= 0.97

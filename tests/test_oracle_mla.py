@@ -138,3 +138,19 @@ def test_end_to_end_packed_isolation(oracle_mod):
         r = res["indices"][i, :res["num_valid"][i]]
         assert np.all(doc[r] == doc[t]) and np.all(r <= t) and r[-1] <= t
         assert np.all(res["indices"][i, res["num_valid"][i]:] == -1)
+
+
+def test_mla_abs_magnitude(oracle_mod):
+    """The error scale sum_j p_j |v_j| bounds |o| and equals o when every value
+    is non-negative."""
+    rng = np.random.default_rng(4)
+    H, D, N = 4, 64, 40
+    q = f32_to_bf16_bits(rng.standard_normal((3, H, D)))
+    kv = f32_to_bf16_bits(rng.standard_normal((N, D)))
+    idx = np.full((3, 128), -1, np.int32)
+    idx[:, :25] = rng.choice(N, (3, 25))
+    out, lse, oabs = oracle_mod.sparse_mla(q, kv, idx, 0.125, with_abs=True)
+    assert np.all(oabs >= np.abs(out) - 1e-6)
+    kv_pos = kv & np.uint16(0x7FFF)              # clear the sign bit: |v|
+    out_p, _, oabs_p = oracle_mod.sparse_mla(q, kv_pos, idx, 0.125, with_abs=True)
+    assert np.allclose(out_p, oabs_p, rtol=1e-6, atol=0)
