@@ -214,7 +214,7 @@ def main():
         "sparse_mla_pct_bf16_peak": 100 * mla_tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": mla_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": mla_tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "sparse_mla_kernel<512,4>",
+                     "kernel": "sparse_mla_kernel<512>",
                      "algorithmic": f"4*H*D = {4 * s.H * s.D} flop per valid slot x {wc['sum_n_valid']} slots"},
     }
     if not args.no_cpu_baseline:

@@ -7,19 +7,24 @@
 // attends to the rows its index row names (up to 2051 of them, "cuDNN sparse
 // MLA parity and performance").
 //
-// One workgroup of 4 waves per query token (64 heads). The index row is
-// compacted in LDS (masked entries dropped, order kept); its latent rows are
-// gathered 32 at a time into a ring of 3 LDS tiles with the gfx950
-// direct-to-LDS load (global_load_lds_dwordx4), two tiles ahead of the one
-// being consumed. Per tile, wave w owns latent columns [w*D/4, (w+1)*D/4):
-//   1. partial S^T = K[:, cols_w] . Q[:, cols_w]^T for all 32 rows and all 64
-//      heads (bf16 MFMA 16x16x32; Q's columns stay in registers; every K
-//      fragment read from LDS feeds four MFMAs, and K is read once per CU);
-//   2. the four partial sums meet in LDS; wave w adds them for the 16 heads
-//      16w.. and runs their online softmax, writing P (bf16) to LDS;
-//   3. O[:, cols_w] += P . V[:, cols_w] for all 64 heads: one V fragment, read
-//      with the transposing ds_read_b64_tr_b16 (the slow LDS read, so V is
-//      read exactly once per CU), feeds four MFMAs.
+// One workgroup of 8 waves (two per SIMD) per query token (64 heads). The
+// index row is compacted in LDS (masked entries dropped, order kept); its
+// latent rows are gathered 32 at a time: each wave loads 4 whole rows (16-byte
+// loads, 1 KB per wave-wide load) into registers one tile ahead and writes them
+// into a 2-tile LDS ring after the current tile is done (plain vector loads
+// keep the gather near the memory system's random-row bandwidth at this
+// occupancy; the direct-to-LDS loads of gfx950 reach well under half of it).
+// Per tile:
+//   1. wave w computes a partial S^T = K[rows_h, cols_c] . Q[:, cols_c]^T for
+//      the row half h = w/4 and column quarter c = w%4, all 64 heads (bf16
+//      MFMA 16x16x32; Q's columns stay in registers; every K fragment read
+//      from LDS feeds four MFMAs, and K is read once per CU);
+//   2. the four column partials meet in LDS; wave w adds them for heads
+//      8w .. 8w+7 and runs their online softmax, writing P (bf16) to LDS;
+//   3. wave w accumulates O[:, cols] += P . V[:, cols] over its eighth of the
+//      latent columns for all 64 heads: one V fragment, read with the
+//      transposing ds_read_b64_tr_b16 (the slow LDS read, so V is read exactly
+//      once per CU), feeds four MFMAs.
 // The softmax reference max of a head is re-based (and O rescaled) only when a
 // tile's max exceeds it by more than 8 (log2 units), so weights stay below 2^8
 // and O is untouched outside the MFMAs on most tiles. LDS rows keep their
@@ -32,9 +37,8 @@
 namespace kp {
 
 constexpr int MLA_TK = 32;    // latent rows per tile
-constexpr int MLA_NW = 4;     // waves per workgroup
-constexpr int MLA_NBUF = 3;   // LDS tiles in the gather ring
-constexpr int MLA_AHEAD = MLA_NBUF - 1;
+constexpr int MLA_NW = 8;     // waves per workgroup (two per SIMD)
+constexpr int MLA_NBUF = 2;   // LDS tiles in the gather ring
 constexpr int MLA_MAX_ROW = 4096;  // index-row entries the LDS list holds
 
 // chunk permutation of LDS row r (16-byte chunks, within aligned groups of 8)
@@ -44,39 +48,8 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((KP_LDS bf16x4*)(p));
 }
 
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (loads retire in order, so the oldest tiles are complete).
-__device__ __forceinline__ void wait_vm(int n) {
-    // s_waitcnt immediate: vmcnt in bits [3:0] and [15:14]; expcnt 7 and
-    // lgkmcnt 15 mean "do not wait" on those counters
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
-
 // compiler-only barrier: keeps LDS accesses on their side of the explicit waits
 __device__ __forceinline__ void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
-
-// Direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane l copies the 16
-// bytes at its own global address `src` to LDS byte address lds_base + 16*l;
-// lds_base is wave-uniform and travels in M0. Issued as inline assembly so the
-// compiler does not treat later LDS reads of other ring tiles as dependent on
-// it (it would wait for every outstanding gather); completion is tracked by
-// the explicit vmcnt waits of the ring. M0 is not otherwise used by these
-// kernels (gfx9 LDS instructions do not read it).
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-    __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                         :: "s"(lds_base), "v"(src) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)((KP_LDS const uint8_t*)p);
-}
 
 constexpr int P_STRIDE = 80;   // bytes per head row of the P tile (32 bf16 + 16 pad: conflict-free reads)
 constexpr int SP_STRIDE = 36;  // floats per head row of a partial-S block (32 + 4 pad)
@@ -86,8 +59,8 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
 }
 
-// Barrier that orders LDS traffic between waves but leaves the gathers of the
-// ring in flight (a __syncthreads would also wait for them).
+// Barrier that orders LDS traffic between waves but does not wait for the
+// gathers in flight (a __syncthreads would also wait for them).
 __device__ __forceinline__ void lds_barrier() {
     compiler_fence();
     wait_lgkm0();
@@ -96,7 +69,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
+__global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ indices,
     int num_kv, int heads, int row_width, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
@@ -105,18 +78,21 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
     constexpr int DP = D < 128 ? 128 : D;   // latent width in LDS (zero-padded)
     constexpr int RB = DP * 2;              // LDS bytes per latent row
     constexpr int CH = D / 8;               // 16-byte chunks a gathered row brings
-    constexpr int KSW = DP / 128;           // QK k-steps (32 columns) per wave
-    constexpr int DTW = DP / 64;            // 16-wide O column tiles per wave
+    constexpr int KSW = DP / 128;           // QK k-steps (32 columns) per wave: a quarter of the columns
+    constexpr int DTW = DP / 128;           // 16-wide O column tiles per wave: an eighth of the columns
     constexpr int TILE_B = MLA_TK * RB;     // bytes per LDS tile
-    constexpr int IPW = MLA_TK / NW;        // gathered rows per wave per tile (one load each)
-    static_assert(NW == 4 && CH >= 8 && CH <= 64 && IPW == 8, "tile staging split");
+    constexpr int IPW = MLA_TK / NW;        // gathered rows per wave per tile
+    constexpr int RPL = (64 / CH) < IPW ? (64 / CH) : IPW;  // rows one wave-wide load covers
+    constexpr int NL = IPW / RPL;           // such loads per wave per tile
+    static_assert(NW == 8 && CH >= 8 && CH <= 64 && 64 % CH == 0 && IPW % RPL == 0, "tile staging split");
     static_assert(DP * 2 * 64 <= MLA_NBUF * TILE_B, "output staging fits the ring");
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
     __shared__ int32_t list[MLA_MAX_ROW];
-    __shared__ __align__(16) float spart[NW * 64 * SP_STRIDE];  // partial S, [wave][head][row]
+    __shared__ __align__(16) float spart[4 * 64 * SP_STRIDE];   // partial S, [column quarter][head][row]
     __shared__ __align__(16) uint8_t ptile[64 * P_STRIDE];      // P, bf16 [head][row]
     __shared__ __align__(16) float alpha_s[64];                 // per-head rescale of this tile
+    __shared__ int rebase_tile;                                 // last tile (+1) that moved a reference max
     __shared__ float lsum[64 * 2];                              // per-head (rounded, exact) sums
     __shared__ float mref_s[64];                                // per-head final reference max
     __shared__ int wave_buf[NW];
@@ -124,6 +100,8 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int i = blockIdx.x;
+    const int cq = wave & 3;    // QK: column quarter
+    const int rh = wave >> 2;   // QK: row half of the tile
 
     // ---- compact the index row (valid entries, original order) ----------------
     const int32_t* irow = indices + (size_t)i * row_width;
@@ -141,7 +119,7 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
         if (lane >= o) x += u;
     }
     if (lane == 63) wave_buf[wave] = x;
-    if (DP != D) {   // zero the padding columns of the ring once; the gathers never touch them
+    if (DP != D) {   // zero the padding columns of the ring once; the staging never writes them
         for (int e = tid; e < MLA_NBUF * TILE_B / 16; e += NT)
             reinterpret_cast<uint4*>(ring)[e] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -165,50 +143,60 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
         return;
     }
     const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
+    if (tid == 0) rebase_tile = 0;   // visible after the barrier that follows the first staging
 
-    // ---- gather ring: wave w moves tile rows 8w .. 8w+7, one load per row ------
-    // Lane l (< CH) writes LDS chunk l of the row and reads the logical chunk
-    // that the row's xor permutation places there.
-    // Row numbers of a tile: lane c (< IPW) of wave w reads list entry
-    // kt*32 + 8w + c; the loads then take them with readlane, so the IPW
-    // gathers issue back to back.
-    auto tile_rows = [&](int kt) {
-        const int li = kt * MLA_TK + wave * IPW + (lane & (IPW - 1));
-        return list[li < n_valid ? li : 0];
-    };
-    auto issue_rows = [&](int kt, int rows_v) {
-        const uint32_t tb = lds_addr(ring) + (uint32_t)((kt % MLA_NBUF) * TILE_B);
-#pragma unroll
-        for (int c = 0; c < IPW; ++c) {
-            const int r = wave * IPW + c;
-            const int row = __builtin_amdgcn_readlane(rows_v, c);
-            if (lane < CH) {
-                const uint16_t* src = kv + (size_t)row * D + 8 * (lane ^ row_swz(r));
-                lds_dma16(src, __builtin_amdgcn_readfirstlane(tb + (uint32_t)(r * RB)));
-            }
-        }
-    };
-    auto issue_tile = [&](int kt) { issue_rows(kt, tile_rows(kt)); };
+    // ---- gather: wave w stages tile rows IPW*w .. IPW*w + IPW-1 --------------------
+    // Load j of a tile: lane l (< RPL*CH) covers tile row r = IPW*w + j*RPL + l/CH
+    // and its 16-byte chunk l%CH, which lands in LDS at chunk (l%CH) ^ row_swz(r).
+    const int lrow = lane / CH, lchunk = lane % CH;
+    const bool lact = lane < RPL * CH;
+    const int srow0 = wave * IPW + lrow;     // tile row of this lane's first load
+    u32x4 stg[NL];                           // the next tile, in flight
+    int rows_next[NL];                       // latent rows of the tile after it
+#define KP_ROWS_OF(kt_)                                                              \
+    _Pragma("unroll") for (int j = 0; j < NL; ++j) {                                 \
+        const int li_ = (kt_) * MLA_TK + srow0 + j * RPL;                            \
+        rows_next[j] = list[li_ < n_valid ? li_ : 0];                                \
+    }
+#define KP_LOAD_TILE()                                                               \
+    if (lact) {                                                                      \
+        _Pragma("unroll") for (int j = 0; j < NL; ++j)                               \
+            stg[j] = *reinterpret_cast<const u32x4*>(                                \
+                reinterpret_cast<const uint8_t*>(kv) +                               \
+                ((uint32_t)rows_next[j] * (uint32_t)(D * 2) + 16u * (uint32_t)lchunk)); \
+    }
+#define KP_STORE_TILE(kt_)                                                           \
+    if (lact) {                                                                      \
+        _Pragma("unroll") for (int j = 0; j < NL; ++j) {                             \
+            const int r_ = srow0 + j * RPL;                                          \
+            *reinterpret_cast<u32x4*>(ring + ((kt_) % MLA_NBUF) * TILE_B + r_ * RB + \
+                                      ((lchunk ^ row_swz(r_)) << 4)) = stg[j];       \
+        }                                                                            \
+    }
 
-    // ---- Q columns of this wave for all 64 heads, B-operand layout -------------
+    // ---- Q of this wave's column quarter for all 64 heads, B-operand layout ---------
     bf16x8 qf[4][KSW];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
         const int head = 16 * ht + n;
 #pragma unroll
         for (int s = 0; s < KSW; ++s) {
-            const int col = wave * (DP / 4) + 32 * s + 8 * g;
+            const int col = cq * (DP / 4) + 32 * s + 8 * g;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (head < heads && col < D) v = *reinterpret_cast<const uint4*>(q + ((size_t)i * heads + head) * D + col);
             qf[ht][s] = __builtin_bit_cast(bf16x8, v);
         }
     }
-    // Complete the Q loads now: the compiler cannot see the gathers (inline
-    // assembly), and if Q were still pending on entry to the tile loop it
-    // would wait for every outstanding gather before each tile's first MFMA.
-    wait_vm(0);
-    compiler_fence();
-    for (int kt = 0; kt < MLA_AHEAD && kt < ntiles; ++kt) issue_tile(kt);
+
+    // tile 0 into LDS, tile 1 into registers
+    KP_ROWS_OF(0)
+    KP_LOAD_TILE()
+    KP_STORE_TILE(0)
+    if (ntiles > 1) {
+        KP_ROWS_OF(1)
+        KP_LOAD_TILE()
+    }
+    __syncthreads();
 
     // PV state: O for heads 16*ht + 4*g + e, columns 16*(wave*DTW + dtl) + n
     f32x4 o[4][DTW];
@@ -216,17 +204,18 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
         for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // softmax state of the owned heads 16*wave + n (rows 8g .. 8g+7 of each tile)
+    // softmax state of the owned heads 8*wave + (lane & 7), rows 4*(lane >> 3) .. +3
+    const int hown = 8 * wave + (lane & 7);
+    const int srow = 4 * (lane >> 3);
     float m_ref = -INFINITY, l_run = 0.f, l_lse = 0.f;
 
     // fixed per-lane LDS offsets
-    int kb[2][2];                                    // K rows 16*rt + n, chunk parity
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = 16 * rt + n;
-        const int base_c = wave * (DP / 4) / 8;      // first chunk of this wave's columns
-        kb[rt][0] = r * RB + (((base_c + g) ^ row_swz(r)) << 4);
-        kb[rt][1] = r * RB + (((base_c + 4 + g) ^ row_swz(r)) << 4);
+    const int rq = 16 * rh + n;                      // K row this lane feeds
+    int kb[2];                                       // K chunk for even / odd k-steps
+    {
+        const int base_c = cq * (DP / 4) / 8;        // first chunk of this wave's columns
+        kb[0] = rq * RB + (((base_c + g) ^ row_swz(rq)) << 4);
+        kb[1] = rq * RB + (((base_c + 4 + g) ^ row_swz(rq)) << 4);
     }
     const int e4 = (lane >> 2) & 3, q4 = lane & 3;
     const int vr0 = 8 * g + e4, vr1 = 8 * g + 4 + e4;  // V rows of the two transposing reads
@@ -237,136 +226,142 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
         vb0[j] = vr0 * RB + ((c ^ row_swz(vr0)) << 4) + 8 * (q4 & 1);
         vb1[j] = vr1 * RB + ((c ^ row_swz(vr1)) << 4) + 8 * (q4 & 1);
     }
-    float* my_sp = spart + wave * 64 * SP_STRIDE;
+    float* my_sp = spart + cq * 64 * SP_STRIDE;
 
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int next_rows = tile_rows(kt + MLA_AHEAD);   // LDS read overlaps the waits below
-        // tile kt complete for this wave, then for all waves
-        const int newer = min(MLA_AHEAD - 1, ntiles - 1 - kt);   // tiles issued after kt
-        compiler_fence();
-        wait_vm(newer * IPW);
-        wait_lgkm0();   // this wave's reads of tile kt-1 have landed
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-        // every wave is done with tile kt-1, so its buffer can take tile kt+2
-        if (kt + MLA_AHEAD < ntiles) issue_rows(kt + MLA_AHEAD, next_rows);
-        compiler_fence();
-        const uint8_t* tb = ring + (kt % MLA_NBUF) * TILE_B;
+    // PV for tile kt and the staging of the next tile (shared by both paths)
+#define KP_TILE_TAIL()                                                                            \
+    {                                                                                             \
+        const uint8_t* tbv = ring + (kt % MLA_NBUF) * TILE_B;                                     \
+        bf16x4 va[DTW][2];                                                                        \
+        _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) {                                   \
+            const int dt_ = wave * DTW + dtl;                                                     \
+            va[dtl][0] = lds_read_tr16(tbv + vb0[dt_ & 3] + 128 * (dt_ >> 2));                    \
+            va[dtl][1] = lds_read_tr16(tbv + vb1[dt_ & 3] + 128 * (dt_ >> 2));                    \
+        }                                                                                         \
+        _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) {                                   \
+            const bf16x8 vb = __builtin_shufflevector(va[dtl][0], va[dtl][1], 0, 1, 2, 3, 4, 5, 6, 7); \
+            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
+                o[ht][dtl] = mfma_bf16_16x16x32(pa[ht], vb, o[ht][dtl]);                         \
+        }                                                                                         \
+        /* tile kt+1 from registers into LDS (its buffer held tile kt-1, which */                 \
+        /* every wave finished before the previous closing barrier); then the  */                 \
+        /* loads of tile kt+2 start                                            */                 \
+        if (kt + 1 < ntiles) {                                                                    \
+            KP_STORE_TILE(kt + 1)                                                                 \
+            if (kt + 2 < ntiles) {                                                                \
+                KP_LOAD_TILE()                                                                    \
+            }                                                                                     \
+        }                                                                                         \
+        lds_barrier();                                                                            \
+    }
 
-        // ---- 1. partial S^T over this wave's columns: 2 row tiles x 4 head tiles ----
-        f32x4 sp[2][4];
+    // The tile loop runs in two levels: the inner loop is the common path and
+    // never rescales O; when a tile moves the reference max of any head (every
+    // wave reads the same alphas, so all agree), it leaves the inner loop, O is
+    // rescaled, and that tile finishes outside. Keeping the rescale out of the
+    // hot loop keeps O in the accumulation registers there.
+    bf16x8 pa[4];
+    f32x4 al[4];
+    int kt = 0;
+    for (;;) {
+        bool rebase = false;
+        for (; kt < ntiles; ++kt) {
+            // row numbers of tile kt+2 (the LDS read overlaps this tile's work)
+            if (kt + 2 < ntiles) {
+                KP_ROWS_OF(kt + 2)
+            }
+            const uint8_t* tb = ring + (kt % MLA_NBUF) * TILE_B;
+
+            // ---- 1. partial S^T: rows 16*rh + (0..15), columns of quarter cq, all heads ----
+            u32x4 ka[KSW];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            for (int s = 0; s < KSW; ++s) ka[s] = *reinterpret_cast<const u32x4*>(tb + kb[s & 1] + 128 * (s >> 1));
+            f32x4 sp[4];
 #pragma unroll
-            for (int ht = 0; ht < 4; ++ht) sp[rt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-        uint4 ka[2][KSW];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int s = 0; s < KSW; ++s)
-                ka[rt][s] = *reinterpret_cast<const uint4*>(tb + kb[rt][s & 1] + 128 * (s >> 1));
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            for (int ht = 0; ht < 4; ++ht) sp[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KSW; ++s) {
-                const bf16x8 af = __builtin_bit_cast(bf16x8, ka[rt][s]);
+                const bf16x8 af = __builtin_bit_cast(bf16x8, ka[s]);
 #pragma unroll
-                for (int ht = 0; ht < 4; ++ht) sp[rt][ht] = mfma_bf16_16x16x32(af, qf[ht][s], sp[rt][ht]);
+                for (int ht = 0; ht < 4; ++ht) sp[ht] = mfma_bf16_16x16x32(af, qf[ht][s], sp[ht]);
             }
-        // lane holds S^T[rows 16*rt + 4*g + e][head 16*ht + n]; store as [head][row]
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            // lane holds S^T[rows 16*rh + 4*g + e][head 16*ht + n]; store as [head][row]
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
-                *reinterpret_cast<f32x4*>(my_sp + (16 * ht + n) * SP_STRIDE + 16 * rt + 4 * g) = sp[rt][ht];
-        lds_barrier();
+                *reinterpret_cast<f32x4*>(my_sp + (16 * ht + n) * SP_STRIDE + 16 * rh + 4 * g) = sp[ht];
+            lds_barrier();
 
-        // ---- 2. full S of the owned heads, rows 8g .. 8g+7; online softmax ----
-        const int hown = 16 * wave + n;
-        float sv[8];
+            // ---- 2. full S of the owned heads (4 rows per lane); online softmax ----
+            f32x4 sv = *reinterpret_cast<const f32x4*>(spart + (0 * 64 + hown) * SP_STRIDE + srow);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] = 0.f;
+            for (int w = 1; w < 4; ++w) sv += *reinterpret_cast<const f32x4*>(spart + (w * 64 + hown) * SP_STRIDE + srow);
+            if ((kt + 1) * MLA_TK > n_valid) {   // ragged last tile: mask the rows past the end
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float* src = spart + (w * 64 + hown) * SP_STRIDE + 8 * g;
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+                for (int e = 0; e < 4; ++e)
+                    if (kt * MLA_TK + srow + e >= n_valid) sv[e] = -INFINITY;
+            }
+            float mt = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { sv[e] += lo[e]; sv[4 + e] += hi[e]; }
-        }
-        float mt = -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+                sv[e] *= scale_log2;
+                mt = fmaxf(mt, sv[e]);
+            }
+            mt = fmaxf(mt, shfl_xor(mt, 8));
+            mt = fmaxf(mt, shfl_xor(mt, 16));
+            mt = fmaxf(mt, shfl_xor(mt, 32));
+            float alpha = 1.0f;
+            if (mt > m_ref + 8.0f) {
+                alpha = __builtin_amdgcn_exp2f(m_ref - mt);
+                m_ref = mt;
+                rebase_tile = kt + 1;   // any writer stores the same value
+            }
+            bf16x4 pw;
+            float ps = 0.f, pe = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int li = kt * MLA_TK + 8 * g + e;
-            sv[e] = li < n_valid ? sv[e] * scale_log2 : -INFINITY;
-            mt = fmaxf(mt, sv[e]);
-        }
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        float alpha = 1.0f;
-        if (mt > m_ref + 8.0f) {
-            alpha = __builtin_amdgcn_exp2f(m_ref - mt);
-            m_ref = mt;
-        }
-        bf16x8 pw;
-        float ps = 0.f, pe = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float w = __builtin_amdgcn_exp2f(sv[e] - m_ref);
-            pw[e] = (__bf16)w;
-            ps += (float)pw[e];
-            pe += w;
-        }
-        l_run = l_run * alpha + ps;
-        l_lse = l_lse * alpha + pe;
-        *reinterpret_cast<bf16x8*>(ptile + hown * P_STRIDE + 16 * g) = pw;
-        if (g == 0) alpha_s[hown] = alpha;
-        lds_barrier();
+            for (int e = 0; e < 4; ++e) {
+                const float w = __builtin_amdgcn_exp2f(sv[e] - m_ref);
+                pw[e] = (__bf16)w;
+                ps += (float)pw[e];
+                pe += w;
+            }
+            l_run = l_run * alpha + ps;
+            l_lse = l_lse * alpha + pe;
+            *reinterpret_cast<bf16x4*>(ptile + hown * P_STRIDE + 2 * srow) = pw;
+            if (lane < 8) alpha_s[hown] = alpha;
+            lds_barrier();
 
-        // ---- 3. O[:, cols_w] += P . V[:, cols_w] for all heads ----
-        bf16x8 pa[4];
-        f32x4 al[4];
-        bool moved = false;
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-            pa[ht] = *reinterpret_cast<const bf16x8*>(ptile + (16 * ht + n) * P_STRIDE + 16 * g);
-            al[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);
-            moved |= (al[ht][0] != 1.0f) | (al[ht][1] != 1.0f) | (al[ht][2] != 1.0f) | (al[ht][3] != 1.0f);
-        }
-        if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-            // rare: keep it a real branch (not a multiply by 1 on every tile)
-            __asm__ __volatile__("");
+            // ---- 3. O[:, cols_w] += P . V[:, cols_w] for all heads ----
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
+                pa[ht] = *reinterpret_cast<const bf16x8*>(ptile + (16 * ht + n) * P_STRIDE + 16 * g);
 #pragma unroll
-                for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
+            for (int ht = 0; ht < 4; ++ht) al[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);
+            if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
+                rebase = true;
+                break;
+            }
+            KP_TILE_TAIL()
         }
-        bf16x4 va[2][2];
-        auto vread = [&](int dtl, bf16x4 (&dst)[2]) {
-            const int dt = wave * DTW + dtl;
-            const int off = 128 * (dt >> 2);
-            dst[0] = lds_read_tr16(tb + vb0[dt & 3] + off);
-            dst[1] = lds_read_tr16(tb + vb1[dt & 3] + off);
-        };
-        vread(0, va[0]);
-        if (DTW > 1) vread(1, va[1]);
+        if (!rebase) break;
+        // rare path: re-base O for this tile, then finish the tile
 #pragma unroll
-        for (int dtl = 0; dtl < DTW; ++dtl) {
-            const bf16x8 vb = __builtin_shufflevector(va[dtl & 1][0], va[dtl & 1][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            if (dtl + 2 < DTW) vread(dtl + 2, va[dtl & 1]);
+        for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-            for (int ht = 0; ht < 4; ++ht) o[ht][dtl] = mfma_bf16_16x16x32(pa[ht], vb, o[ht][dtl]);
-        }
+            for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
+        KP_TILE_TAIL()
+        ++kt;
     }
+#undef KP_TILE_TAIL
 
     // ---- normalise and write ----------------------------------------------------
     {
-        float lr = l_run + shfl_xor(l_run, 16);
+        float lr = l_run + shfl_xor(l_run, 8);
+        lr += shfl_xor(lr, 16);
         lr += shfl_xor(lr, 32);
-        float le = l_lse + shfl_xor(l_lse, 16);
+        float le = l_lse + shfl_xor(l_lse, 8);
+        le += shfl_xor(le, 16);
         le += shfl_xor(le, 32);
-        const int hown = 16 * wave + n;
-        if (g == 0) {
+        if (lane < 8) {
             lsum[hown * 2] = lr;
             lsum[hown * 2 + 1] = le;
             mref_s[hown] = m_ref;
@@ -398,6 +393,9 @@ __global__ __launch_bounds__(64 * MLA_NW) void sparse_mla_kernel(
     uint4* dst = reinterpret_cast<uint4*>(orow);
     const int nvec = heads * D / 8;
     for (int e = tid; e < nvec; e += NT) dst[e] = src[e];
+#undef KP_ROWS_OF
+#undef KP_LOAD_TILE
+#undef KP_STORE_TILE
 }
 
 template <int D>
