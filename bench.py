@@ -27,6 +27,26 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 
+# HBM bytes per sparse_mla_fwd launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# passes scaled by the same counters' reading of a plain 1 GiB device copy (the
+# commands and raw counts are in profiles/dsa_forward_32k_hbm_traffic.md). Keyed
+# by the attention kernel's source hash: a changed kernel reports null until its
+# counters are taken again.
+MEASURED_TRAFFIC = {
+    "aa0362960cd4ce30": {"workload": "32k", "read": 44557047853, "write": 2155872256},
+}
+MLA_SOURCE = os.path.join(ROOT, "sparse_attention_kpool_amd", "csrc", "sparse_mla.hip")
+
+
+def measured_traffic(workload: str):
+    import hashlib
+    with open(MLA_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    m = MEASURED_TRAFFIC.get(sha)
+    if m is None or m["workload"] != workload:
+        return None, sha
+    return m["read"] + m["write"], sha
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -97,6 +117,9 @@ def main():
     ap.add_argument("--workload", default="32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the reference "
+                         "reading for rocprofv3's FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -104,6 +127,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
     import sparse_attention_kpool_amd as K
     from workloads import Workload, spec
 
@@ -185,6 +217,7 @@ def main():
     wc = work_counts(s)
     assert int(nv.sum().item()) == wc["sum_n_valid"], "index rows disagree with the closed-form slot count"
     mla_s = ms_stage[2] / 1e3
+    traffic, mla_sha = measured_traffic(s.name)
     mla_tflops = wc["mla_flop"] / mla_s / 1e12
     log(f"stages (ms, mean of {args.steps}): kpool_build {ms_stage[0]:.3f}  indexer_score_topk {ms_stage[1]:.3f}"
         f"  sparse_mla_fwd {ms_stage[2]:.3f}  | step wall {ms_step:.3f}")
@@ -213,8 +246,9 @@ def main():
         "sparse_mla_tflops": mla_tflops,
         "sparse_mla_pct_bf16_peak": 100 * mla_tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": mla_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": mla_tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "sparse_mla_kernel<512>",
+                     "frac": mla_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
+                     "traffic_unit": "bytes per launch (HBM read + write)",
+                     "kernel": "sparse_mla_kernel<512>", "kernel_source_sha256": mla_sha,
                      "algorithmic": f"4*H*D = {4 * s.H * s.D} flop per valid slot x {wc['sum_n_valid']} slots"},
     }
     if not args.no_cpu_baseline:
