@@ -56,6 +56,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ float shfl_idx(float v, int src) { return __shfl(v, src, 64); }
 
+// Data-parallel moves inside a row of 16 lanes (no LDS traffic). CTRL is the
+// DPP control: 0xB1 = quad_perm(1,0,3,2) (lane ^ 1), 0x4E = quad_perm(2,3,0,1)
+// (lane ^ 2), 0x141 = row_half_mirror (lane i of each 8 reads lane 7 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// max / sum over each aligned group of 8 lanes, result in all 8
+__device__ __forceinline__ float max_in_8(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    return fmaxf(v, dpp_mov<0x141>(v));
+}
+__device__ __forceinline__ float sum_in_8(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    return v + dpp_mov<0x141>(v);
+}
+
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll

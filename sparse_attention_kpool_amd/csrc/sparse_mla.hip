@@ -10,21 +10,24 @@
 // One workgroup of 8 waves (two per SIMD) per query token (64 heads). The
 // index row is compacted in LDS (masked entries dropped, order kept); its
 // latent rows are gathered 32 at a time: each wave loads 4 whole rows (16-byte
-// loads, 1 KB per wave-wide load) into registers one tile ahead and writes them
-// into a 2-tile LDS ring after the current tile is done (plain vector loads
-// keep the gather near the memory system's random-row bandwidth at this
-// occupancy; the direct-to-LDS loads of gfx950 reach well under half of it).
-// Per tile:
-//   1. wave w computes a partial S^T = K[rows_h, cols_c] . Q[:, cols_c]^T for
-//      the row half h = w/4 and column quarter c = w%4, all 64 heads (bf16
-//      MFMA 16x16x32; Q's columns stay in registers; every K fragment read
-//      from LDS feeds four MFMAs, and K is read once per CU);
-//   2. the four column partials meet in LDS; wave w adds them for heads
-//      8w .. 8w+7 and runs their online softmax, writing P (bf16) to LDS;
-//   3. wave w accumulates O[:, cols] += P . V[:, cols] over its eighth of the
-//      latent columns for all 64 heads: one V fragment, read with the
-//      transposing ds_read_b64_tr_b16 (the slow LDS read, so V is read exactly
-//      once per CU), feeds four MFMAs.
+// loads, 1 KB per wave-wide load) into registers and writes them into a 3-tile
+// LDS ring one tile later (plain vector loads keep the gather near the memory
+// system's random-row bandwidth at this occupancy; the direct-to-LDS loads of
+// gfx950 reach well under half of it). The work on a tile t:
+//   QK: wave w computes a partial S^T = K[rows_h, cols_c] . Q[:, cols_c]^T for
+//       the row half h = w/4 and column quarter c = w%4, all 64 heads (bf16
+//       MFMA 16x16x32; Q's columns stay in registers; every K fragment read
+//       from LDS feeds four MFMAs, and K is read once per CU);
+//   SM: the four column partials meet in LDS; wave w adds them for heads
+//       w, w+8, .., w+56 and runs their online softmax, writing P (bf16);
+//   PV: wave w accumulates O[:, cols] += P . V[:, cols] over its eighth of the
+//       latent columns for all 64 heads: one V fragment, read with the
+//       transposing ds_read_b64_tr_b16 (V is read exactly once per CU), feeds
+//       four MFMAs.
+// The loop is software-pipelined with two barriers per tile: phase 1 runs
+// QK(t+1) together with the first half of PV(t) and the staging of tile t+2;
+// phase 2 runs SM(t+1) together with the second half of PV(t), so the MFMA
+// pipe has work while the softmax waits on LDS.
 // The softmax reference max of a head is re-based (and O rescaled) only when a
 // tile's max exceeds it by more than 8 (log2 units), so weights stay below 2^8
 // and O is untouched outside the MFMAs on most tiles. LDS rows keep their
@@ -38,11 +41,18 @@ namespace kp {
 
 constexpr int MLA_TK = 32;    // latent rows per tile
 constexpr int MLA_NW = 8;     // waves per workgroup (two per SIMD)
-constexpr int MLA_NBUF = 2;   // LDS tiles in the gather ring
+constexpr int MLA_NBUF = 3;   // LDS tiles in the gather ring
 constexpr int MLA_MAX_ROW = 4096;  // index-row entries the LDS list holds
 
-// chunk permutation of LDS row r (16-byte chunks, within aligned groups of 8)
-__device__ __forceinline__ int row_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk permutation of LDS row r: 16-byte chunk c is stored at c ^ row_swz(r)
+// (within aligned groups of 16 chunks, i.e. one pass over the 64 banks).
+// row_swz is a permutation of 0..15 over any 16 consecutive rows (row-wise
+// 16-byte reads of 16 rows hit distinct banks), and its upper three bits differ
+// across rows {0..3, 8..11} and across {4..7, 12..15} (the 8 rows one
+// transposing read touches in 32 lanes hit distinct 32-byte bank groups).
+__device__ __forceinline__ int row_swz(int r) {
+    return ((r & 3) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
+}
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((KP_LDS bf16x4*)(p));
@@ -80,6 +90,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     constexpr int CH = D / 8;               // 16-byte chunks a gathered row brings
     constexpr int KSW = DP / 128;           // QK k-steps (32 columns) per wave: a quarter of the columns
     constexpr int DTW = DP / 128;           // 16-wide O column tiles per wave: an eighth of the columns
+    constexpr int DTA = DTW - DTW / 2;      // of which PV runs in phase 1 (the rest in phase 2)
     constexpr int TILE_B = MLA_TK * RB;     // bytes per LDS tile
     constexpr int IPW = MLA_TK / NW;        // gathered rows per wave per tile
     constexpr int RPL = (64 / CH) < IPW ? (64 / CH) : IPW;  // rows one wave-wide load covers
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     __shared__ int32_t list[MLA_MAX_ROW];
     __shared__ __align__(16) float spart[4 * 64 * SP_STRIDE];   // partial S, [column quarter][head][row]
     __shared__ __align__(16) uint8_t ptile[64 * P_STRIDE];      // P, bf16 [head][row]
-    __shared__ __align__(16) float alpha_s[64];                 // per-head rescale of this tile
+    __shared__ __align__(16) float alpha_s[64];                 // per-head rescale of the last softmax tile
     __shared__ int rebase_tile;                                 // last tile (+1) that moved a reference max
     __shared__ float lsum[64 * 2];                              // per-head (rounded, exact) sums
     __shared__ float mref_s[64];                                // per-head final reference max
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         return;
     }
     const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
-    if (tid == 0) rebase_tile = 0;   // visible after the barrier that follows the first staging
+    if (tid == 0) rebase_tile = 0;   // visible after the first barrier below
 
     // ---- gather: wave w stages tile rows IPW*w .. IPW*w + IPW-1 --------------------
     // Load j of a tile: lane l (< RPL*CH) covers tile row r = IPW*w + j*RPL + l/CH
@@ -151,8 +162,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int lrow = lane / CH, lchunk = lane % CH;
     const bool lact = lane < RPL * CH;
     const int srow0 = wave * IPW + lrow;     // tile row of this lane's first load
-    u32x4 stg[NL];                           // the next tile, in flight
-    int rows_next[NL];                       // latent rows of the tile after it
+    u32x4 stg[NL];                           // a tile in flight
+    int rows_next[NL];                       // latent rows of the next tile to load
 #define KP_ROWS_OF(kt_)                                                              \
     _Pragma("unroll") for (int j = 0; j < NL; ++j) {                                 \
         const int li_ = (kt_) * MLA_TK + srow0 + j * RPL;                            \
@@ -188,180 +199,195 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         }
     }
 
-    // tile 0 into LDS, tile 1 into registers
-    KP_ROWS_OF(0)
-    KP_LOAD_TILE()
-    KP_STORE_TILE(0)
-    if (ntiles > 1) {
-        KP_ROWS_OF(1)
-        KP_LOAD_TILE()
-    }
-    __syncthreads();
-
     // PV state: O for heads 16*ht + 4*g + e, columns 16*(wave*DTW + dtl) + n
     f32x4 o[4][DTW];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
         for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // softmax state of the owned heads 8*wave + (lane & 7), rows 4*(lane >> 3) .. +3
-    const int hown = 8 * wave + (lane & 7);
-    const int srow = 4 * (lane >> 3);
+    // softmax state: wave w owns heads w, w+8, .., w+56 (lanes 8j..8j+7 hold head
+    // w+8j, rows 4*(lane&7) .. +3; a row-group reduction stays inside 8 lanes)
+    const int hown = wave + 8 * (lane >> 3);
+    const int srow = 4 * (lane & 7);
     float m_ref = -INFINITY, l_run = 0.f, l_lse = 0.f;
 
     // fixed per-lane LDS offsets
     const int rq = 16 * rh + n;                      // K row this lane feeds
-    int kb[2];                                       // K chunk for even / odd k-steps
-    {
-        const int base_c = cq * (DP / 4) / 8;        // first chunk of this wave's columns
-        kb[0] = rq * RB + (((base_c + g) ^ row_swz(rq)) << 4);
-        kb[1] = rq * RB + (((base_c + 4 + g) ^ row_swz(rq)) << 4);
-    }
+    int kb[KSW];                                     // K chunk of each k-step
+#pragma unroll
+    for (int s = 0; s < KSW; ++s)
+        kb[s] = rq * RB + (((cq * (DP / 32) + 4 * s + g) ^ row_swz(rq)) << 4);
     const int e4 = (lane >> 2) & 3, q4 = lane & 3;
     const int vr0 = 8 * g + e4, vr1 = 8 * g + 4 + e4;  // V rows of the two transposing reads
-    int vb0[4], vb1[4];
+    int vb0[DTW], vb1[DTW];                          // V chunk of each column tile
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = 2 * j + (q4 >> 1);
-        vb0[j] = vr0 * RB + ((c ^ row_swz(vr0)) << 4) + 8 * (q4 & 1);
-        vb1[j] = vr1 * RB + ((c ^ row_swz(vr1)) << 4) + 8 * (q4 & 1);
+    for (int dtl = 0; dtl < DTW; ++dtl) {
+        const int c = 2 * (wave * DTW + dtl) + (q4 >> 1);
+        vb0[dtl] = vr0 * RB + ((c ^ row_swz(vr0)) << 4) + 8 * (q4 & 1);
+        vb1[dtl] = vr1 * RB + ((c ^ row_swz(vr1)) << 4) + 8 * (q4 & 1);
     }
     float* my_sp = spart + cq * 64 * SP_STRIDE;
 
-    // PV for tile kt and the staging of the next tile (shared by both paths)
-#define KP_TILE_TAIL()                                                                            \
+    // QK of tile kt_ into partial S (LDS)
+#define KP_QK(kt_)                                                                                \
     {                                                                                             \
-        const uint8_t* tbv = ring + (kt % MLA_NBUF) * TILE_B;                                     \
-        bf16x4 va[DTW][2];                                                                        \
-        _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) {                                   \
-            const int dt_ = wave * DTW + dtl;                                                     \
-            va[dtl][0] = lds_read_tr16(tbv + vb0[dt_ & 3] + 128 * (dt_ >> 2));                    \
-            va[dtl][1] = lds_read_tr16(tbv + vb1[dt_ & 3] + 128 * (dt_ >> 2));                    \
+        const uint8_t* tb_ = ring + ((kt_) % MLA_NBUF) * TILE_B;                                  \
+        u32x4 ka_[KSW];                                                                           \
+        _Pragma("unroll") for (int s = 0; s < KSW; ++s) ka_[s] = *reinterpret_cast<const u32x4*>(tb_ + kb[s]); \
+        _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) sp[ht] = f32x4{0.f, 0.f, 0.f, 0.f};     \
+        _Pragma("unroll") for (int s = 0; s < KSW; ++s) {                                         \
+            const bf16x8 af_ = __builtin_bit_cast(bf16x8, ka_[s]);                                \
+            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) sp[ht] = mfma_bf16_16x16x32(af_, qf[ht][s], sp[ht]); \
         }                                                                                         \
-        _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) {                                   \
-            const bf16x8 vb = __builtin_shufflevector(va[dtl][0], va[dtl][1], 0, 1, 2, 3, 4, 5, 6, 7); \
+    }
+    /* lane holds S^T[rows 16*rh + 4*g + e][head 16*ht + n]; stored as [head][row] */
+#define KP_QK_STORE()                                                                             \
+    _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                              \
+        *reinterpret_cast<f32x4*>(my_sp + (16 * ht + n) * SP_STRIDE + 16 * rh + 4 * g) = sp[ht];
+    // full S of the owned heads (4 rows per lane) for tile kt_: read and sum the partials
+#define KP_SM_READ()                                                                              \
+    sv = *reinterpret_cast<const f32x4*>(spart + (0 * 64 + hown) * SP_STRIDE + srow);             \
+    _Pragma("unroll") for (int w = 1; w < 4; ++w)                                                 \
+        sv += *reinterpret_cast<const f32x4*>(spart + (w * 64 + hown) * SP_STRIDE + srow);
+    // online softmax of tile kt_; P (bf16) and the per-head rescale to LDS
+#define KP_SM_FINISH(kt_)                                                                         \
+    {                                                                                             \
+        if (((kt_) + 1) * MLA_TK > n_valid) {   /* ragged last tile: mask the rows past the end */ \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e)                                         \
+                if ((kt_) * MLA_TK + srow + e >= n_valid) sv[e] = -INFINITY;                      \
+        }                                                                                         \
+        float mt_ = -INFINITY;                                                                    \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                           \
+            sv[e] *= scale_log2;                                                                  \
+            mt_ = fmaxf(mt_, sv[e]);                                                              \
+        }                                                                                         \
+        mt_ = max_in_8(mt_);                                                                      \
+        float alpha_ = 1.0f;                                                                      \
+        if (mt_ > m_ref + 8.0f) {                                                                 \
+            alpha_ = __builtin_amdgcn_exp2f(m_ref - mt_);                                         \
+            m_ref = mt_;                                                                          \
+            rebase_tile = (kt_) + 1;   /* any writer stores the same value */                     \
+        }                                                                                         \
+        bf16x4 pw_;                                                                               \
+        float ps_ = 0.f, pe_ = 0.f;                                                               \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                           \
+            const float w_ = __builtin_amdgcn_exp2f(sv[e] - m_ref);                               \
+            pw_[e] = (__bf16)w_;                                                                  \
+            ps_ += (float)pw_[e];                                                                 \
+            pe_ += w_;                                                                            \
+        }                                                                                         \
+        l_run = l_run * alpha_ + ps_;                                                             \
+        l_lse = l_lse * alpha_ + pe_;                                                             \
+        *reinterpret_cast<bf16x4*>(ptile + hown * P_STRIDE + 2 * srow) = pw_;                     \
+        if ((lane & 7) == 0) alpha_s[hown] = alpha_;                                              \
+    }
+    // O[:, cols] += P . V[:, cols] over the column tiles [d0_, d1_) of tile kt_
+#define KP_PV(kt_, d0_, d1_)                                                                      \
+    {                                                                                             \
+        const uint8_t* tbv_ = ring + ((kt_) % MLA_NBUF) * TILE_B;                                 \
+        _Pragma("unroll") for (int dtl = (d0_); dtl < (d1_); ++dtl) {                             \
+            const bf16x4 v0_ = lds_read_tr16(tbv_ + vb0[dtl]);                                    \
+            const bf16x4 v1_ = lds_read_tr16(tbv_ + vb1[dtl]);                                    \
+            const bf16x8 vb_ = __builtin_shufflevector(v0_, v1_, 0, 1, 2, 3, 4, 5, 6, 7);         \
             _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
-                o[ht][dtl] = mfma_bf16_16x16x32(pa[ht], vb, o[ht][dtl]);                         \
+                o[ht][dtl] = mfma_bf16_16x16x32(pa[ht], vb_, o[ht][dtl]);                         \
         }                                                                                         \
-        /* tile kt+1 from registers into LDS (its buffer held tile kt-1, which */                 \
-        /* every wave finished before the previous closing barrier); then the  */                 \
-        /* loads of tile kt+2 start                                            */                 \
-        if (kt + 1 < ntiles) {                                                                    \
-            KP_STORE_TILE(kt + 1)                                                                 \
-            if (kt + 2 < ntiles) {                                                                \
+    }
+#define KP_READ_P()                                                                               \
+    _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                              \
+        pa[ht] = *reinterpret_cast<const bf16x8*>(ptile + (16 * ht + n) * P_STRIDE + 16 * g);
+    // One pipelined step, for a tile kt with a successor (kt + 1 < ntiles):
+    //   phase 1: QK(kt+1), PV(kt) on the first DTA column tiles, tile kt+2 from
+    //            registers into the ring (its buffer last held tile kt-1, which
+    //            every wave finished before the previous barrier), loads of kt+3;
+    //   phase 2: SM(kt+1) and PV(kt) on the remaining column tiles.
+#define KP_STEP()                                                                                 \
+    {                                                                                             \
+        if (kt + 3 < ntiles) {                                                                    \
+            KP_ROWS_OF(kt + 3)                                                                    \
+        }                                                                                         \
+        KP_QK(kt + 1)                                                                             \
+        KP_QK_STORE()                                                                             \
+        KP_READ_P()                                                                               \
+        KP_PV(kt, 0, DTA)                                                                         \
+        if (kt + 2 < ntiles) {                                                                    \
+            KP_STORE_TILE(kt + 2)                                                                 \
+            if (kt + 3 < ntiles) {                                                                \
                 KP_LOAD_TILE()                                                                    \
             }                                                                                     \
         }                                                                                         \
         lds_barrier();                                                                            \
+        KP_SM_READ()                                                                              \
+        KP_PV(kt, DTA, DTW)                                                                       \
+        KP_SM_FINISH(kt + 1)                                                                      \
+        lds_barrier();                                                                            \
     }
 
-    // The tile loop runs in two levels: the inner loop is the common path and
-    // never rescales O; when a tile moves the reference max of any head (every
-    // wave reads the same alphas, so all agree), it leaves the inner loop, O is
-    // rescaled, and that tile finishes outside. Keeping the rescale out of the
-    // hot loop keeps O in the accumulation registers there.
+    f32x4 sp[4];
+    f32x4 sv;
     bf16x8 pa[4];
-    f32x4 al[4];
+
+    // ---- prologue: tiles 0 and 1 into the ring, tile 2 into registers; SM(0) -------
+    KP_ROWS_OF(0)
+    KP_LOAD_TILE()
+    KP_STORE_TILE(0)
+    if (ntiles > 1) {
+        KP_ROWS_OF(1)
+        KP_LOAD_TILE()
+        KP_STORE_TILE(1)
+        if (ntiles > 2) {
+            KP_ROWS_OF(2)
+            KP_LOAD_TILE()
+        }
+    }
+    lds_barrier();
+    KP_QK(0)
+    KP_QK_STORE()
+    lds_barrier();
+    KP_SM_READ()
+    KP_SM_FINISH(0)
+    lds_barrier();
+
+    // When the last softmax moved the reference max of any head (every wave
+    // reads the same flag, so all agree), O is rescaled before PV of that tile.
     int kt = 0;
-    for (;;) {
-        bool rebase = false;
-        for (; kt < ntiles; ++kt) {
-            // row numbers of tile kt+2 (the LDS read overlaps this tile's work)
-            if (kt + 2 < ntiles) {
-                KP_ROWS_OF(kt + 2)
-            }
-            const uint8_t* tb = ring + (kt % MLA_NBUF) * TILE_B;
-
-            // ---- 1. partial S^T: rows 16*rh + (0..15), columns of quarter cq, all heads ----
-            u32x4 ka[KSW];
-#pragma unroll
-            for (int s = 0; s < KSW; ++s) ka[s] = *reinterpret_cast<const u32x4*>(tb + kb[s & 1] + 128 * (s >> 1));
-            f32x4 sp[4];
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht) sp[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KSW; ++s) {
-                const bf16x8 af = __builtin_bit_cast(bf16x8, ka[s]);
-#pragma unroll
-                for (int ht = 0; ht < 4; ++ht) sp[ht] = mfma_bf16_16x16x32(af, qf[ht][s], sp[ht]);
-            }
-            // lane holds S^T[rows 16*rh + 4*g + e][head 16*ht + n]; store as [head][row]
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
-                *reinterpret_cast<f32x4*>(my_sp + (16 * ht + n) * SP_STRIDE + 16 * rh + 4 * g) = sp[ht];
-            lds_barrier();
-
-            // ---- 2. full S of the owned heads (4 rows per lane); online softmax ----
-            f32x4 sv = *reinterpret_cast<const f32x4*>(spart + (0 * 64 + hown) * SP_STRIDE + srow);
-#pragma unroll
-            for (int w = 1; w < 4; ++w) sv += *reinterpret_cast<const f32x4*>(spart + (w * 64 + hown) * SP_STRIDE + srow);
-            if ((kt + 1) * MLA_TK > n_valid) {   // ragged last tile: mask the rows past the end
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (kt * MLA_TK + srow + e >= n_valid) sv[e] = -INFINITY;
-            }
-            float mt = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sv[e] *= scale_log2;
-                mt = fmaxf(mt, sv[e]);
-            }
-            mt = fmaxf(mt, shfl_xor(mt, 8));
-            mt = fmaxf(mt, shfl_xor(mt, 16));
-            mt = fmaxf(mt, shfl_xor(mt, 32));
-            float alpha = 1.0f;
-            if (mt > m_ref + 8.0f) {
-                alpha = __builtin_amdgcn_exp2f(m_ref - mt);
-                m_ref = mt;
-                rebase_tile = kt + 1;   // any writer stores the same value
-            }
-            bf16x4 pw;
-            float ps = 0.f, pe = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float w = __builtin_amdgcn_exp2f(sv[e] - m_ref);
-                pw[e] = (__bf16)w;
-                ps += (float)pw[e];
-                pe += w;
-            }
-            l_run = l_run * alpha + ps;
-            l_lse = l_lse * alpha + pe;
-            *reinterpret_cast<bf16x4*>(ptile + hown * P_STRIDE + 2 * srow) = pw;
-            if (lane < 8) alpha_s[hown] = alpha;
-            lds_barrier();
-
-            // ---- 3. O[:, cols_w] += P . V[:, cols_w] for all heads ----
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
-                pa[ht] = *reinterpret_cast<const bf16x8*>(ptile + (16 * ht + n) * P_STRIDE + 16 * g);
+    for (; kt + 1 < ntiles; ++kt) {
+        if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
+            f32x4 al[4];
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) al[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);
-            if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
-                rebase = true;
-                break;
-            }
-            KP_TILE_TAIL()
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
         }
-        if (!rebase) break;
-        // rare path: re-base O for this tile, then finish the tile
+        KP_STEP()
+    }
+    // last tile: PV only
+    if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
+        f32x4 al[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) al[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
             for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
-        KP_TILE_TAIL()
-        ++kt;
     }
-#undef KP_TILE_TAIL
+    KP_READ_P()
+    KP_PV(kt, 0, DTW)
+#undef KP_STEP
+#undef KP_READ_P
+#undef KP_PV
+#undef KP_SM_FINISH
+#undef KP_SM_READ
+#undef KP_QK_STORE
+#undef KP_QK
 
     // ---- normalise and write ----------------------------------------------------
     {
-        float lr = l_run + shfl_xor(l_run, 8);
-        lr += shfl_xor(lr, 16);
-        lr += shfl_xor(lr, 32);
-        float le = l_lse + shfl_xor(l_lse, 8);
-        le += shfl_xor(le, 16);
-        le += shfl_xor(le, 32);
-        if (lane < 8) {
+        const float lr = sum_in_8(l_run);
+        const float le = sum_in_8(l_lse);
+        if ((lane & 7) == 0) {
             lsum[hown * 2] = lr;
             lsum[hown * 2 + 1] = le;
             mref_s[hown] = m_ref;
