@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define KP_LDS __attribute__((address_space(3)))
 
@@ -61,7 +62,9 @@ __device__ __forceinline__ float shfl_idx(float v, int src) { return __shfl(v, s
 // (lane ^ 2), 0x141 = row_half_mirror (lane i of each 8 reads lane 7 - i).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    // every source lane exists for these controls, so bound_ctrl (zero for a
+    // missing source) never applies; setting it lets the move fold into the ALU op
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // max / sum over each aligned group of 8 lanes, result in all 8
@@ -74,6 +77,26 @@ __device__ __forceinline__ float sum_in_8(float v) {
     v += dpp_mov<0xB1>(v);
     v += dpp_mov<0x4E>(v);
     return v + dpp_mov<0x141>(v);
+}
+
+// max(a, b, c, d) over each aligned group of 8 lanes, result in all 8. The
+// inputs are finite or -inf. Written out so the three cross-lane steps are
+// single v_max_f32 DPP instructions (the compiler's IEEE-mode max would quiet
+// each DPP result first). A VALU write followed by a DPP read of the same VGPR
+// needs two wait states, hence the s_nop 1 before each DPP step.
+__device__ __forceinline__ float max4_in_8(float a, float b, float c, float d) {
+    float r;
+    __asm__("v_max3_f32 %0, %1, %2, %3\n\t"
+            "v_max_f32 %0, %0, %4\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "=&v"(r)
+            : "v"(a), "v"(b), "v"(c), "v"(d));
+    return r;
 }
 
 template <int W>

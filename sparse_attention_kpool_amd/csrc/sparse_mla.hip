@@ -146,6 +146,13 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         if (v >= 0 && v < num_kv) list[before++] = v;
     }
     __syncthreads();
+    // pad the list to whole tiles with a valid row (its scores are masked), so
+    // the gather needs no bounds test
+    {
+        const int pad_end = (n_valid + MLA_TK - 1) / MLA_TK * MLA_TK;
+        if (n_valid > 0 && tid < pad_end - n_valid) list[n_valid + tid] = list[0];
+    }
+    __syncthreads();
 
     uint16_t* orow = out + (size_t)i * heads * D;
     if (n_valid == 0) {
@@ -162,12 +169,17 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int lrow = lane / CH, lchunk = lane % CH;
     const bool lact = lane < RPL * CH;
     const int srow0 = wave * IPW + lrow;     // tile row of this lane's first load
+    int sto[NL];                             // LDS offsets of this lane's staged chunks
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int r = srow0 + j * RPL;
+        sto[j] = r * RB + ((lchunk ^ row_swz(r)) << 4);
+    }
     u32x4 stg[NL];                           // a tile in flight
     int rows_next[NL];                       // latent rows of the next tile to load
 #define KP_ROWS_OF(kt_)                                                              \
     _Pragma("unroll") for (int j = 0; j < NL; ++j) {                                 \
-        const int li_ = (kt_) * MLA_TK + srow0 + j * RPL;                            \
-        rows_next[j] = list[li_ < n_valid ? li_ : 0];                                \
+        rows_next[j] = list[(kt_) * MLA_TK + srow0 + j * RPL];                       \
     }
 #define KP_LOAD_TILE()                                                               \
     if (lact) {                                                                      \
@@ -176,13 +188,10 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
                 reinterpret_cast<const uint8_t*>(kv) +                               \
                 ((uint32_t)rows_next[j] * (uint32_t)(D * 2) + 16u * (uint32_t)lchunk)); \
     }
-#define KP_STORE_TILE(kt_)                                                           \
+#define KP_STORE_TILE(buf_)                                                          \
     if (lact) {                                                                      \
-        _Pragma("unroll") for (int j = 0; j < NL; ++j) {                             \
-            const int r_ = srow0 + j * RPL;                                          \
-            *reinterpret_cast<u32x4*>(ring + ((kt_) % MLA_NBUF) * TILE_B + r_ * RB + \
-                                      ((lchunk ^ row_swz(r_)) << 4)) = stg[j];       \
-        }                                                                            \
+        _Pragma("unroll") for (int j = 0; j < NL; ++j)                               \
+            *reinterpret_cast<u32x4*>(ring + (buf_) * TILE_B + sto[j]) = stg[j];     \
     }
 
     // ---- Q of this wave's column quarter for all 64 heads, B-operand layout ---------
@@ -229,9 +238,9 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     float* my_sp = spart + cq * 64 * SP_STRIDE;
 
     // QK of tile kt_ into partial S (LDS)
-#define KP_QK(kt_)                                                                                \
+#define KP_QK(buf_)                                                                               \
     {                                                                                             \
-        const uint8_t* tb_ = ring + ((kt_) % MLA_NBUF) * TILE_B;                                  \
+        const uint8_t* tb_ = ring + (buf_) * TILE_B;                                              \
         u32x4 ka_[KSW];                                                                           \
         _Pragma("unroll") for (int s = 0; s < KSW; ++s) ka_[s] = *reinterpret_cast<const u32x4*>(tb_ + kb[s]); \
         _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) sp[ht] = f32x4{0.f, 0.f, 0.f, 0.f};     \
@@ -256,35 +265,32 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             _Pragma("unroll") for (int e = 0; e < 4; ++e)                                         \
                 if ((kt_) * MLA_TK + srow + e >= n_valid) sv[e] = -INFINITY;                      \
         }                                                                                         \
-        float mt_ = -INFINITY;                                                                    \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                           \
-            sv[e] *= scale_log2;                                                                  \
-            mt_ = fmaxf(mt_, sv[e]);                                                              \
-        }                                                                                         \
-        mt_ = max_in_8(mt_);                                                                      \
+        /* the scale is positive: the max of the raw scores, scaled, is the tile max */           \
+        const float mt_ = max4_in_8(sv[0], sv[1], sv[2], sv[3]) * scale_log2;                     \
         float alpha_ = 1.0f;                                                                      \
         if (mt_ > m_ref + 8.0f) {                                                                 \
             alpha_ = __builtin_amdgcn_exp2f(m_ref - mt_);                                         \
             m_ref = mt_;                                                                          \
             rebase_tile = (kt_) + 1;   /* any writer stores the same value */                     \
         }                                                                                         \
+        float w_[4];                                                                              \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e)                                             \
+            w_[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, -m_ref));            \
         bf16x4 pw_;                                                                               \
-        float ps_ = 0.f, pe_ = 0.f;                                                               \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                           \
-            const float w_ = __builtin_amdgcn_exp2f(sv[e] - m_ref);                               \
-            pw_[e] = (__bf16)w_;                                                                  \
-            ps_ += (float)pw_[e];                                                                 \
-            pe_ += w_;                                                                            \
-        }                                                                                         \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) pw_[e] = (__bf16)w_[e];                     \
+        /* the sum of the rounded weights, from the packed bf16 words */                          \
+        const u32x2 pk_ = __builtin_bit_cast(u32x2, pw_);                                         \
+        const float ps_ = (bf16_lo(pk_[0]) + bf16_hi(pk_[0])) + (bf16_lo(pk_[1]) + bf16_hi(pk_[1])); \
+        const float pe_ = (w_[0] + w_[1]) + (w_[2] + w_[3]);                                      \
         l_run = l_run * alpha_ + ps_;                                                             \
         l_lse = l_lse * alpha_ + pe_;                                                             \
         *reinterpret_cast<bf16x4*>(ptile + hown * P_STRIDE + 2 * srow) = pw_;                     \
         if ((lane & 7) == 0) alpha_s[hown] = alpha_;                                              \
     }
     // O[:, cols] += P . V[:, cols] over the column tiles [d0_, d1_) of tile kt_
-#define KP_PV(kt_, d0_, d1_)                                                                      \
+#define KP_PV(buf_, d0_, d1_)                                                                     \
     {                                                                                             \
-        const uint8_t* tbv_ = ring + ((kt_) % MLA_NBUF) * TILE_B;                                 \
+        const uint8_t* tbv_ = ring + (buf_) * TILE_B;                                             \
         _Pragma("unroll") for (int dtl = (d0_); dtl < (d1_); ++dtl) {                             \
             const bf16x4 v0_ = lds_read_tr16(tbv_ + vb0[dtl]);                                    \
             const bf16x4 v1_ = lds_read_tr16(tbv_ + vb1[dtl]);                                    \
@@ -296,31 +302,42 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #define KP_READ_P()                                                                               \
     _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                              \
         pa[ht] = *reinterpret_cast<const bf16x8*>(ptile + (16 * ht + n) * P_STRIDE + 16 * g);
-    // One pipelined step, for a tile kt with a successor (kt + 1 < ntiles):
+    // One pipelined step, for a tile kt with a successor (kt + 1 < ntiles); the
+    // ring buffers of tiles kt, kt+1 and kt+2 are BV, BK and BS (compile-time,
+    // so LDS addresses are immediates):
     //   phase 1: QK(kt+1), PV(kt) on the first DTA column tiles, tile kt+2 from
     //            registers into the ring (its buffer last held tile kt-1, which
     //            every wave finished before the previous barrier), loads of kt+3;
     //   phase 2: SM(kt+1) and PV(kt) on the remaining column tiles.
-#define KP_STEP()                                                                                 \
+    // O is rescaled first when the softmax of tile kt moved a reference max.
+#define KP_STEP(BV, BK, BS)                                                                       \
     {                                                                                             \
+        if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {                              \
+            f32x4 al_[4];                                                                         \
+            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
+                al_[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);             \
+            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
+                _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al_[ht];      \
+        }                                                                                         \
         if (kt + 3 < ntiles) {                                                                    \
             KP_ROWS_OF(kt + 3)                                                                    \
         }                                                                                         \
-        KP_QK(kt + 1)                                                                             \
+        KP_QK(BK)                                                                                 \
         KP_QK_STORE()                                                                             \
         KP_READ_P()                                                                               \
-        KP_PV(kt, 0, DTA)                                                                         \
+        KP_PV(BV, 0, DTA)                                                                         \
         if (kt + 2 < ntiles) {                                                                    \
-            KP_STORE_TILE(kt + 2)                                                                 \
+            KP_STORE_TILE(BS)                                                                     \
             if (kt + 3 < ntiles) {                                                                \
                 KP_LOAD_TILE()                                                                    \
             }                                                                                     \
         }                                                                                         \
         lds_barrier();                                                                            \
         KP_SM_READ()                                                                              \
-        KP_PV(kt, DTA, DTW)                                                                       \
+        KP_PV(BV, DTA, DTW)                                                                       \
         KP_SM_FINISH(kt + 1)                                                                      \
         lds_barrier();                                                                            \
+        ++kt;                                                                                     \
     }
 
     f32x4 sp[4];
@@ -348,20 +365,16 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     KP_SM_FINISH(0)
     lds_barrier();
 
-    // When the last softmax moved the reference max of any head (every wave
-    // reads the same flag, so all agree), O is rescaled before PV of that tile.
+    // the loop runs three steps per pass so that every ring buffer index is a
+    // compile-time constant
     int kt = 0;
-    for (; kt + 1 < ntiles; ++kt) {
-        if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
-            f32x4 al[4];
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht) al[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-                for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
-        }
-        KP_STEP()
+    for (;;) {
+        if (kt + 1 >= ntiles) break;
+        KP_STEP(0, 1, 2)
+        if (kt + 1 >= ntiles) break;
+        KP_STEP(1, 2, 0)
+        if (kt + 1 >= ntiles) break;
+        KP_STEP(2, 0, 1)
     }
     // last tile: PV only
     if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
@@ -374,7 +387,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
     }
     KP_READ_P()
-    KP_PV(kt, 0, DTW)
+    KP_PV(kt % MLA_NBUF, 0, DTW)
 #undef KP_STEP
 #undef KP_READ_P
 #undef KP_PV

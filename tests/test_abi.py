@@ -83,5 +83,7 @@ def test_invalid_args_rejected_on_host(L):
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, None, None) == 2
     assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 1
     assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
+    for bad in (0.0, -0.1, float("inf"), float("nan")):          # the softmax scale must be positive
+        assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 128, C.c_float(bad), fake, None, None) == 1
     assert L.indexer_rotate_quant(fake, 4, 2, 48, fake, fake, None) == 2
     assert L.indexer_topk_from_scores(fake, 1, 64, fake, 16, None, 64, None, 4, 4, 128, fake, None, None) == 1
