@@ -9,22 +9,26 @@
 // positive.
 //
 // Work decomposition: a workgroup takes 16 queries and a chunk of 512 pools;
-// each of its 4 waves holds the E4M3 codes of 128 pools (8 tiles of 16) in
-// registers as the B operand and streams the query tile from LDS as the A
-// operand: one v_mfma_f32_16x16x128_f8f6f4 covers a full 128-wide dot for 16
-// heads x 16 pools. The ReLU and head weighting run on the fp32 accumulator
-// lanes; the sum over the 16 heads of a tile is finished with two cross-lane
-// adds. Workgroups whose pool chunk lies outside every query's visible range
-// exit at once; query tiles are dispatched last-first so the longest causal
-// rows start early.
+// each of its 8 waves holds the E4M3 codes of 64 pools (4 tiles of 16) in
+// registers as the B operand (few enough registers for four waves per SIMD,
+// so one wave's ReLU/weighting overlaps another's MFMAs). The query tile sits in LDS head-major; for each
+// indexer head h, one v_mfma_f32_16x16x128_f8f6f4 per pool tile computes the
+// full 128-wide dots of 16 queries x 16 pools, and each lane folds its 4
+// (query, pool) results into running sums with w*sq of that query and head
+// after the ReLU. The head sum thus stays inside the lane: no cross-lane
+// reduction. Workgroups whose pool chunk lies outside every query's visible
+// range exit at once; query tiles are dispatched last-first so the longest
+// causal rows start early.
 #include "kp_device.h"
 #include "kp_launch.h"
 
 namespace kp {
 
 constexpr int SC_QT = 16;     // queries per workgroup
-constexpr int SC_PW = 128;    // pools per wave
-constexpr int SC_WAVES = 4;
+constexpr int SC_NJ = 4;      // 16-pool tiles per wave
+constexpr int SC_PW = 16 * SC_NJ;  // pools per wave
+constexpr int SC_WAVES = 8;
+constexpr int SC_THREADS = 64 * SC_WAVES;
 constexpr int SC_PC = SC_PW * SC_WAVES;  // pools per workgroup
 
 __global__ void fill_f32_kernel(float* __restrict__ dst, size_t n, float v) {
@@ -41,20 +45,59 @@ hipError_t launch_fill_f32(float* dst, size_t n, float value, hipStream_t stream
     return hipGetLastError();
 }
 
-// LDS layout of the query tile: row (q, h) of 128 bytes = 8 chunks of 16 B;
-// chunk c of row with head h is stored at chunk c ^ (h & 7) so that the 16
-// rows an A-operand read touches fall in distinct banks.
-template <int NHT>
-__global__ __launch_bounds__(256) void score_kernel(
+// LDS layout of the query tile: [head][query][128 bytes]; the 16-byte chunk c
+// of query row q is stored at chunk c ^ ((q >> 1) & 7), so the 16 rows one
+// A-operand read touches fall in distinct banks.
+// max(x, 0) on the bit pattern: a set sign bit reads as a negative integer
+// (-0 included), so one integer max clears every negative value; positive
+// values pass unchanged. One instruction, and no quieting of the MFMA result.
+__device__ __forceinline__ float relu_f32(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+template <bool FULL>
+__device__ __forceinline__ void score_heads(const uint8_t* __restrict__ q_lds, const float* __restrict__ wq_lds,
+                                            int h_idx, const i32x8 (&b)[SC_NJ], int jlo, int jhi,
+                                            f32x4 (&acc)[SC_NJ]) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int sw = (n >> 1) & 7;
+    const uint8_t* rowp = q_lds + n * 128;
+    const int off0 = ((2 * g) ^ sw) << 4, off1 = ((2 * g + 1) ^ sw) << 4;
+    // operands of head h are read one head ahead
+    uint4 a0 = *reinterpret_cast<const uint4*>(rowp + off0);
+    uint4 a1 = *reinterpret_cast<const uint4*>(rowp + off1);
+    f32x4 wv = *reinterpret_cast<const f32x4*>(wq_lds + 4 * g);
+#pragma unroll 2
+    for (int h = 0; h < h_idx; ++h) {
+        const i32x8 a = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                              (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const f32x4 wh = wv;
+        if (h + 1 < h_idx) {
+            const uint8_t* r = rowp + (h + 1) * (16 * 128);
+            a0 = *reinterpret_cast<const uint4*>(r + off0);
+            a1 = *reinterpret_cast<const uint4*>(r + off1);
+            wv = *reinterpret_cast<const f32x4*>(wq_lds + (h + 1) * 16 + 4 * g);
+        }
+        f32x4 c[SC_NJ];
+#pragma unroll
+        for (int j = 0; j < SC_NJ; ++j)
+            if (FULL || (j >= jlo && j < jhi)) c[j] = mfma_fp8_16x16x128(a, b[j], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j < SC_NJ; ++j)
+            if (FULL || (j >= jlo && j < jhi)) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(wh[e], relu_f32(c[j][e]), acc[j][e]);
+            }
+    }
+}
+
+__global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, int num_q, const uint8_t* __restrict__ q8,
     const float* __restrict__ sq, const float* __restrict__ w, int h_idx, int d_idx,
     const uint8_t* __restrict__ k8, const float* __restrict__ sk, int max_pools,
     float* __restrict__ scores) {
-    constexpr int NH = NHT * 16;
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* q_lds = smem;                                           // [QT][NH][128]
-    float* wq_lds = reinterpret_cast<float*>(smem + SC_QT * NH * 128);  // [QT][NH]
+    uint8_t* q_lds = smem;                                                 // [h_idx][QT][128]
+    float* wq_lds = reinterpret_cast<float*>(smem + (size_t)h_idx * SC_QT * 128);  // [h_idx][QT]
     __shared__ int lo_s[SC_QT], hi_s[SC_QT];
     __shared__ int any_s;
 
@@ -84,20 +127,37 @@ __global__ __launch_bounds__(256) void score_kernel(
     __syncthreads();
     if (!any_s) return;
 
-    // stage the query tile: codes (zero-padded to NH heads x 128 bytes) and w*sq
+    // stage the query tile, head-major: codes (zero-padded to 128 bytes) and w*sq
     const int dchunks = d_idx >> 4;
-    for (int c = tid; c < SC_QT * NH * 8; c += 256) {
-        int ch = c & 7, row = c >> 3, h = row % NH, q = row / NH;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (q0 + q < num_q && h < h_idx && ch < dchunks)
-            v = *reinterpret_cast<const uint4*>(q8 + (((size_t)(q0 + q) * h_idx + h) * d_idx) + ch * 16);
-        *reinterpret_cast<uint4*>(q_lds + (size_t)row * 128 + ((ch ^ (h & 7)) << 4)) = v;
+    {
+        // 16-byte chunk c = tid + SC_THREADS * k: head c >> 7, query (c >> 3) & 15,
+        // chunk c & 7; eight loads are put in flight before their LDS stores
+        constexpr int SB = 8;
+        const int nch = h_idx * SC_QT * 8;
+        const int ch = tid & 7, q = (tid >> 3) & (SC_QT - 1);
+        const bool qok = q0 + q < num_q && ch < dchunks;
+        const uint8_t* src = q8 + (size_t)(qok ? q0 + q : 0) * h_idx * d_idx + ch * 16;
+        uint8_t* dst = q_lds + (size_t)q * 128 + ((ch ^ ((q >> 1) & 7)) << 4);
+        for (int c0 = 0; c0 < nch; c0 += SC_THREADS * SB) {
+            uint4 v[SB];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int h = (c0 + tid + SC_THREADS * k) >> 7;
+                v[k] = make_uint4(0u, 0u, 0u, 0u);
+                if (qok && c0 + SC_THREADS * k + tid < nch) v[k] = *reinterpret_cast<const uint4*>(src + (size_t)h * d_idx);
+            }
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int h = (c0 + tid + SC_THREADS * k) >> 7;
+                if (c0 + SC_THREADS * k + tid < nch) *reinterpret_cast<uint4*>(dst + (size_t)h * SC_QT * 128) = v[k];
+            }
+        }
     }
-    for (int c = tid; c < SC_QT * NH; c += 256) {
-        int h = c % NH, q = c / NH;
+    for (int c = tid; c < h_idx * SC_QT; c += SC_THREADS) {
+        const int q = c & (SC_QT - 1), h = c >> 4;
         float v = 0.0f;
-        if (q0 + q < num_q && h < h_idx) {
-            size_t o = (size_t)(q0 + q) * h_idx + h;
+        if (q0 + q < num_q) {
+            const size_t o = (size_t)(q0 + q) * h_idx + h;
             v = w[o] * sq[o];
         }
         wq_lds[c] = v;
@@ -105,10 +165,10 @@ __global__ __launch_bounds__(256) void score_kernel(
 
     // this wave's pools: B operands (32 code bytes of column n per lane) and key scales
     const int Pw = P0 + wave * SC_PW;
-    i32x8 b[8];
-    float skj[8];
+    i32x8 b[SC_NJ];
+    float skj[SC_NJ];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < SC_NJ; ++j) {
         int p = Pw + 16 * j + n;
         uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
         float s = 0.0f;
@@ -124,36 +184,36 @@ __global__ __launch_bounds__(256) void score_kernel(
     }
     __syncthreads();
 
+    // pool tiles [jlo, jhi) of this wave that some query of the tile sees
+    int jlo = SC_NJ, jhi = 0;
     for (int q = 0; q < SC_QT; ++q) {
-        const int lo = lo_s[q], hi = hi_s[q];
-        if (hi <= Pw || lo >= Pw + SC_PW || lo >= hi) continue;
-        float acc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-            const int head = ht * 16 + n;
-            const uint8_t* row = q_lds + (size_t)(q * NH + head) * 128;
-            uint4 a0 = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ (head & 7)) << 4));
-            uint4 a1 = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ (head & 7)) << 4));
-            i32x8 a = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            float4 wv = *reinterpret_cast<const float4*>(wq_lds + q * NH + ht * 16 + 4 * g);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                f32x4 c = mfma_fp8_16x16x128(a, b[j], f32x4{0.f, 0.f, 0.f, 0.f});
-                acc[j] += wv.x * fmaxf(c[0], 0.0f) + wv.y * fmaxf(c[1], 0.0f) +
-                          wv.z * fmaxf(c[2], 0.0f) + wv.w * fmaxf(c[3], 0.0f);
-            }
+        const int lo = max(lo_s[q], Pw), hi = min(hi_s[q], Pw + SC_PW);
+        if (lo < hi) {
+            jlo = min(jlo, (lo - Pw) >> 4);
+            jhi = max(jhi, (hi - Pw + 15) >> 4);
         }
-        const size_t orow = (size_t)(q0 + q) * max_pools;
+    }
+    if (jlo >= jhi) return;
+
+    f32x4 acc[SC_NJ];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float v = acc[j];
-            v += shfl_xor(v, 16);
-            v += shfl_xor(v, 32);
+    for (int j = 0; j < SC_NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (jlo == 0 && jhi == SC_NJ)
+        score_heads<true>(q_lds, wq_lds, h_idx, b, 0, SC_NJ, acc);
+    else
+        score_heads<false>(q_lds, wq_lds, h_idx, b, jlo, jhi, acc);
+
+    // lane holds queries 4g + e of the tile for pool Pw + 16j + n
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int q = 4 * g + e;
+        if (q0 + q >= num_q) continue;
+        const int lo = lo_s[q], hi = hi_s[q];
+        float* orow = scores + (size_t)(q0 + q) * max_pools;
+#pragma unroll
+        for (int j = 0; j < SC_NJ; ++j) {
             const int p = Pw + 16 * j + n;
-            if ((j & 3) == g && p >= lo && p < hi) scores[orow + p] = v * skj[j];
+            if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
         }
     }
 }
@@ -163,33 +223,14 @@ hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools
                         const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
                         int max_pools, float* scores, hipStream_t stream) {
     if (num_q == 0 || max_pools == 0) return hipSuccess;
-    const int nht = (h_idx + 15) / 16;
     const long long nblk = (long long)((max_pools + SC_PC - 1) / SC_PC) * ((num_q + SC_QT - 1) / SC_QT);
     if (nblk > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nblk);
-    const size_t lds = (size_t)SC_QT * nht * 16 * (128 + 4);
-    const void* fns[4] = {(const void*)score_kernel<1>, (const void*)score_kernel<2>, (const void*)score_kernel<3>,
-                          (const void*)score_kernel<4>};
-    hipError_t e = hipFuncSetAttribute(fns[nht - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const size_t lds = (size_t)h_idx * SC_QT * (128 + 4);
+    hipError_t e = hipFuncSetAttribute((const void*)score_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    switch (nht) {
-        case 1:
-            score_kernel<1><<<grid, 256, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w,
-                                                        h_idx, d_idx, k8, sk, max_pools, scores);
-            break;
-        case 2:
-            score_kernel<2><<<grid, 256, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w,
-                                                        h_idx, d_idx, k8, sk, max_pools, scores);
-            break;
-        case 3:
-            score_kernel<3><<<grid, 256, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w,
-                                                        h_idx, d_idx, k8, sk, max_pools, scores);
-            break;
-        default:
-            score_kernel<4><<<grid, 256, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w,
-                                                        h_idx, d_idx, k8, sk, max_pools, scores);
-            break;
-    }
+    score_kernel<<<grid, SC_THREADS, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx,
+                                             k8, sk, max_pools, scores);
     return hipGetLastError();
 }
 

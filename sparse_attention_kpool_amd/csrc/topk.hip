@@ -8,8 +8,9 @@
 //
 // One workgroup per query row. Scores map to order-preserving 32-bit keys
 // (-0 folded onto +0; NaN below -inf). A most-significant-digit-first radix
-// select (four 8-bit digits, histograms in LDS) finds the key K of the k-th
-// largest score and how many of the kept pools score exactly K. A final pass
+// select (digits of 11, 11 and 10 bits, histograms in LDS) finds the key K of
+// the k-th largest score and how many of the kept pools score exactly K; it
+// stops early when the bin holding the k-th key is kept whole. A final pass
 // over contiguous per-thread chunks, in pool order, keeps every pool above K
 // and the first pools equal to K, and writes each kept pool's tokens at its
 // rank: the kept pools come out ascending with no sort. The keys of a row
@@ -20,7 +21,8 @@
 namespace kp {
 
 constexpr int TK_THREADS = 256;
-constexpr int TK_LDS_KEYS = 12288;   // keys cached in LDS (48 KB)
+constexpr int TK_LDS_KEYS = 8192;    // keys cached in LDS (32 KB)
+constexpr int TK_BINS = 2048;        // histogram bins of the widest digit
 
 __device__ __forceinline__ uint32_t score_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -58,9 +60,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
     int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid) {
     __shared__ uint32_t keys_lds[TK_LDS_KEYS];
-    __shared__ int hist[256];
+    __shared__ int hist[TK_BINS];
     __shared__ int wave_buf[TK_THREADS / 64];
-    __shared__ int sel_digit, sel_above;
+    __shared__ int sel_digit, sel_above, sel_cnt;
 
     const int tid = threadIdx.x;
     const int i = blockIdx.x;
@@ -77,50 +79,70 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     uint32_t thresh = 0xFFFFFFFFu;  // key of the k-th largest score (k == 0: above every key)
     int take_eq = 0;                // how many pools equal to thresh are kept (lowest first)
     if (!all && k > 0) {
-        if (cached)
-            for (int j = tid; j < n; j += TK_THREADS) keys_lds[j] = score_key(srow[j]);
+        if (cached) {
+            // sixteen loads in flight per thread before their LDS stores
+            constexpr int SB = 16;
+            for (int j0 = 0; j0 < n; j0 += TK_THREADS * SB) {
+                float v[SB];
+#pragma unroll
+                for (int q = 0; q < SB; ++q) {
+                    const int j = j0 + tid + TK_THREADS * q;
+                    v[q] = j < n ? srow[j] : 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < SB; ++q) {
+                    const int j = j0 + tid + TK_THREADS * q;
+                    if (j < n) keys_lds[j] = score_key(v[q]);
+                }
+            }
+        }
         int remaining = k;  // still to choose among keys matching the prefix
         uint32_t prefix = 0u, pmask = 0u;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            hist[tid] = 0;
+        take_eq = -1;
+#pragma unroll 1
+        for (int pass = 0; pass < 3; ++pass) {
+            const int width = pass < 2 ? 11 : 10;
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int nb = 1 << width;
+            for (int b = tid; b < nb; b += TK_THREADS) hist[b] = 0;
             __syncthreads();
             for (int j = tid; j < n; j += TK_THREADS) {
                 uint32_t key = cached ? keys_lds[j] : score_key(srow[j]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1);
             }
             __syncthreads();
-            if (tid < 64) {
-                // wave 0: bins 255..0 as 64 lanes x 4, counting from the top
-                int c0 = hist[255 - 4 * tid], c1 = hist[254 - 4 * tid], c2 = hist[253 - 4 * tid],
-                    c3 = hist[252 - 4 * tid];
-                int s = c0 + c1 + c2 + c3, incl = s;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    int u = __shfl_up(incl, o, 64);
-                    if (tid >= o) incl += u;
-                }
-                int before = incl - s;  // count in bins above this lane's four
-                if (before < remaining && incl >= remaining) {
-                    int cs[4] = {c0, c1, c2, c3};
-                    int acc = before;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (acc < remaining && acc + cs[e] >= remaining) {
-                            sel_digit = 255 - 4 * tid - e;
-                            sel_above = acc;
-                        }
-                        acc += cs[e];
+            // thread t owns the nb/256 bins just below the top 'nb/256 * t' bins;
+            // a scan over threads counts the keys in bins above each thread's
+            const int per = nb / TK_THREADS;
+            const int top = nb - 1 - per * tid;
+            int cnt_own = 0;
+            for (int e = 0; e < per; ++e) cnt_own += hist[top - e];
+            int tot;
+            const int before = block_excl_scan(cnt_own, wave_buf, &tot);
+            if (before < remaining && before + cnt_own >= remaining) {
+                int acc = before;
+                for (int e = 0; e < per; ++e) {
+                    const int c = hist[top - e];
+                    if (acc < remaining && acc + c >= remaining) {
+                        sel_digit = top - e;
+                        sel_above = acc;
+                        sel_cnt = c;
                     }
+                    acc += c;
                 }
             }
             __syncthreads();
             remaining -= sel_above;
             prefix |= (uint32_t)sel_digit << shift;
-            pmask |= 255u << shift;
-            __syncthreads();
+            pmask |= (uint32_t)(nb - 1) << shift;
+            if (sel_cnt == remaining) {
+                // the whole bin is kept: every key >= prefix (low bits zero) is selected
+                take_eq = 0x7FFFFFFF;
+                break;
+            }
         }
         thresh = prefix;
-        take_eq = remaining;
+        if (take_eq < 0) take_eq = remaining;
     }
 
     // final pass: contiguous chunk per thread, in pool order
