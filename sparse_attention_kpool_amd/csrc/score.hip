@@ -8,7 +8,8 @@
 // which equals sum_h w * ReLU(sq * sk * <q8, k8>) because both scales are
 // positive.
 //
-// Work decomposition: a workgroup takes 16 queries and a chunk of 512 pools;
+// Work decomposition: a workgroup takes 16 queries, stages their codes in LDS
+// once, and walks the pools its queries see in chunks of 512; for each chunk,
 // each of its 8 waves holds the E4M3 codes of 64 pools (4 tiles of 16) in
 // registers as the B operand (few enough registers for four waves per SIMD,
 // so one wave's ReLU/weighting overlaps another's MFMAs). The query tile sits in LDS head-major; for each
@@ -16,9 +17,9 @@
 // full 128-wide dots of 16 queries x 16 pools, and each lane folds its 4
 // (query, pool) results into running sums with w*sq of that query and head
 // after the ReLU. The head sum thus stays inside the lane: no cross-lane
-// reduction. Workgroups whose pool chunk lies outside every query's visible
-// range exit at once; query tiles are dispatched last-first so the longest
-// causal rows start early.
+// reduction. Chunks and tiles outside every query's visible range are
+// skipped; query tiles are dispatched last-first so the longest causal rows
+// start early.
 #include "kp_device.h"
 #include "kp_launch.h"
 
@@ -99,15 +100,13 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     uint8_t* q_lds = smem;                                                 // [h_idx][QT][128]
     float* wq_lds = reinterpret_cast<float*>(smem + (size_t)h_idx * SC_QT * 128);  // [h_idx][QT]
     __shared__ int lo_s[SC_QT], hi_s[SC_QT];
-    __shared__ int any_s;
+    __shared__ int plo_s, phi_s;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int nchunks = (max_pools + SC_PC - 1) / SC_PC;
     const int nqt = (num_q + SC_QT - 1) / SC_QT;
-    const int qtile = nqt - 1 - (int)(blockIdx.x / nchunks);
+    const int qtile = nqt - 1 - (int)blockIdx.x;
     const int q0 = qtile * SC_QT;
-    const int P0 = (int)(blockIdx.x % nchunks) * SC_PC;
 
     if (tid < SC_QT) {
         int lo = 0, hi = 0;
@@ -121,11 +120,20 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
         lo_s[tid] = lo;
         hi_s[tid] = hi;
     }
-    if (tid == 0) any_s = 0;
     __syncthreads();
-    if (tid < SC_QT && lo_s[tid] < hi_s[tid] && hi_s[tid] > P0 && lo_s[tid] < P0 + SC_PC) any_s = 1;
+    if (tid == 0) {   // the pools any query of the tile sees lie in [plo, phi)
+        int plo = 0x7FFFFFFF, phi = 0;
+        for (int q = 0; q < SC_QT; ++q)
+            if (lo_s[q] < hi_s[q]) {
+                plo = min(plo, lo_s[q]);
+                phi = max(phi, hi_s[q]);
+            }
+        plo_s = plo;
+        phi_s = phi;
+    }
     __syncthreads();
-    if (!any_s) return;
+    const int plo = plo_s, phi = phi_s;
+    if (plo >= phi) return;
 
     // stage the query tile, head-major: codes (zero-padded to 128 bytes) and w*sq
     const int dchunks = d_idx >> 4;
@@ -163,57 +171,60 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
         wq_lds[c] = v;
     }
 
-    // this wave's pools: B operands (32 code bytes of column n per lane) and key scales
-    const int Pw = P0 + wave * SC_PW;
-    i32x8 b[SC_NJ];
-    float skj[SC_NJ];
-#pragma unroll
-    for (int j = 0; j < SC_NJ; ++j) {
-        int p = Pw + 16 * j + n;
-        uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
-        float s = 0.0f;
-        if (p < max_pools) {
-            const uint8_t* src = k8 + (size_t)p * d_idx;
-            if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src + 32 * g);
-            if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 32 * g + 16);
-            s = sk[p];
-        }
-        b[j] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                     (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-        skj[j] = s;
-    }
     __syncthreads();
 
-    // pool tiles [jlo, jhi) of this wave that some query of the tile sees
-    int jlo = SC_NJ, jhi = 0;
-    for (int q = 0; q < SC_QT; ++q) {
-        const int lo = max(lo_s[q], Pw), hi = min(hi_s[q], Pw + SC_PW);
-        if (lo < hi) {
-            jlo = min(jlo, (lo - Pw) >> 4);
-            jhi = max(jhi, (hi - Pw + 15) >> 4);
+    for (int P0 = plo / SC_PC * SC_PC; P0 < phi; P0 += SC_PC) {
+        const int Pw = P0 + wave * SC_PW;
+        // pool tiles [jlo, jhi) of this wave that some query of the tile sees
+        int jlo = SC_NJ, jhi = 0;
+        for (int q = 0; q < SC_QT; ++q) {
+            const int lo = max(lo_s[q], Pw), hi = min(hi_s[q], Pw + SC_PW);
+            if (lo < hi) {
+                jlo = min(jlo, (lo - Pw) >> 4);
+                jhi = max(jhi, (hi - Pw + 15) >> 4);
+            }
         }
-    }
-    if (jlo >= jhi) return;
+        if (jlo >= jhi) continue;
 
-    f32x4 acc[SC_NJ];
-#pragma unroll
-    for (int j = 0; j < SC_NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (jlo == 0 && jhi == SC_NJ)
-        score_heads<true>(q_lds, wq_lds, h_idx, b, 0, SC_NJ, acc);
-    else
-        score_heads<false>(q_lds, wq_lds, h_idx, b, jlo, jhi, acc);
-
-    // lane holds queries 4g + e of the tile for pool Pw + 16j + n
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int q = 4 * g + e;
-        if (q0 + q >= num_q) continue;
-        const int lo = lo_s[q], hi = hi_s[q];
-        float* orow = scores + (size_t)(q0 + q) * max_pools;
+        // this wave's pools: B operands (32 code bytes of column n per lane) and key scales
+        i32x8 b[SC_NJ];
+        float skj[SC_NJ];
 #pragma unroll
         for (int j = 0; j < SC_NJ; ++j) {
-            const int p = Pw + 16 * j + n;
-            if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
+            int p = Pw + 16 * j + n;
+            uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
+            float s = 0.0f;
+            if (p < max_pools) {
+                const uint8_t* src = k8 + (size_t)p * d_idx;
+                if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src + 32 * g);
+                if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 32 * g + 16);
+                s = sk[p];
+            }
+            b[j] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                         (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+            skj[j] = s;
+        }
+
+        f32x4 acc[SC_NJ];
+#pragma unroll
+        for (int j = 0; j < SC_NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (jlo == 0 && jhi == SC_NJ)
+            score_heads<true>(q_lds, wq_lds, h_idx, b, 0, SC_NJ, acc);
+        else
+            score_heads<false>(q_lds, wq_lds, h_idx, b, jlo, jhi, acc);
+
+        // lane holds queries 4g + e of the tile for pool Pw + 16j + n
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = 4 * g + e;
+            if (q0 + q >= num_q) continue;
+            const int lo = lo_s[q], hi = hi_s[q];
+            float* orow = scores + (size_t)(q0 + q) * max_pools;
+#pragma unroll
+            for (int j = 0; j < SC_NJ; ++j) {
+                const int p = Pw + 16 * j + n;
+                if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
+            }
         }
     }
 }
@@ -223,9 +234,7 @@ hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools
                         const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
                         int max_pools, float* scores, hipStream_t stream) {
     if (num_q == 0 || max_pools == 0) return hipSuccess;
-    const long long nblk = (long long)((max_pools + SC_PC - 1) / SC_PC) * ((num_q + SC_QT - 1) / SC_QT);
-    if (nblk > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)nblk);
+    const dim3 grid((unsigned)((num_q + SC_QT - 1) / SC_QT));
     const size_t lds = (size_t)h_idx * SC_QT * (128 + 4);
     hipError_t e = hipFuncSetAttribute((const void*)score_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -10,7 +10,8 @@
 // (-0 folded onto +0; NaN below -inf). A most-significant-digit-first radix
 // select (digits of 11, 11 and 10 bits, histograms in LDS) finds the key K of
 // the k-th largest score and how many of the kept pools score exactly K; it
-// stops early when the bin holding the k-th key is kept whole. A final pass
+// stops early when the bin holding the k-th key is kept whole (then no
+// ordering among equal keys is needed). A final pass
 // over contiguous per-thread chunks, in pool order, keeps every pool above K
 // and the first pools equal to K, and writes each kept pool's tokens at its
 // rank: the kept pools come out ascending with no sort. The keys of a row
@@ -31,16 +32,24 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast 15 and 31 carry the
+// row totals into the rows above.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Exclusive scan of one int per thread over the block; returns the prefix and
 // writes the total to *total.
 __device__ __forceinline__ int block_excl_scan(int v, int* wave_buf, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int u = __shfl_up(x, o, 64);
-        if (lane >= o) x += u;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) wave_buf[wave] = x;
     __syncthreads();
     int add = 0, tot = 0;
@@ -55,14 +64,161 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wave_buf, int* total)
     return add + x - v;
 }
 
+// Keys j .. j+3 of the row (j a multiple of 4); entries at or past n read as 0.
+// Cached rows read one 16-byte LDS vector; others read the scores.
+template <bool CACHED>
+__device__ __forceinline__ void fetch4(uint32_t (&kk)[4], const uint32_t* keys_lds, const float* srow,
+                                       int j, int n) {
+    if (CACHED) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys_lds + j);
+        kk[0] = v.x; kk[1] = v.y; kk[2] = v.z; kk[3] = v.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[e] = j + e < n ? score_key(srow[j + e]) : 0u;
+    }
+}
+
+template <bool CACHED>
+__device__ __forceinline__ void topk_row(const uint32_t* keys_lds, int (*hist)[TK_BINS], int* wave_buf,
+                                         int* sel, const float* srow, int n, int k, int kpool,
+                                         int doc_start, int32_t* row) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool all = k >= n;        // every visible pool is kept (no scores needed)
+    uint32_t thresh = 0xFFFFFFFFu;  // key of the k-th largest score (k == 0: above every key)
+    int take_eq = 0;                // how many pools equal to thresh are kept (lowest first)
+    constexpr int ALL_EQ = 0x7FFFFFFF;
+    if (!all && k > 0) {
+        for (int b = tid; b < TK_BINS; b += TK_THREADS) hist[0][b] = 0;
+        __syncthreads();            // cached keys and the first histogram are ready
+        int remaining = k;          // still to choose among keys matching the prefix
+        uint32_t prefix = 0u, pmask = 0u;
+        take_eq = -1;
+        // Two barriers per digit: the histogram is complete, then the bin is
+        // known. The histograms alternate between two buffers, so the one for
+        // the next digit is cleared while this one is counted.
+#pragma unroll 1
+        for (int pass = 0; pass < 3; ++pass) {
+            const int width = pass < 2 ? 11 : 10;
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int nb = 1 << width;
+            int* h = hist[pass & 1];
+#pragma unroll 2
+            for (int j = 4 * tid; j < n; j += 4 * TK_THREADS) {
+                uint32_t kk[4];
+                fetch4<CACHED>(kk, keys_lds, srow, j, n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < n && (kk[e] & pmask) == prefix)
+                        atomicAdd(&h[(kk[e] >> shift) & (uint32_t)(nb - 1)], 1);
+            }
+            for (int b = tid; b < TK_BINS; b += TK_THREADS) hist[(pass + 1) & 1][b] = 0;
+            __syncthreads();
+            if (wave == 0) {
+                // lane l owns bins [nb - per*(l+1), nb - per*l): a scan over lanes
+                // counts the keys in the bins above each lane's
+                const int per = nb >> 6;    // 32 or 16
+                const int base = nb - per * (lane + 1);
+                int4 r[8];
+                int own = 0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    r[q] = make_int4(0, 0, 0, 0);
+                    if (4 * q < per) r[q] = *reinterpret_cast<const int4*>(h + base + 4 * q);
+                    own += r[q].x + r[q].y + r[q].z + r[q].w;
+                }
+                const int incl = wave_incl_scan(own);
+                const int before = incl - own;
+                if (before < remaining && incl >= remaining) {
+                    int acc = before;
+#pragma unroll
+                    for (int m = 31; m >= 0; --m) {
+                        if (m < per) {
+                            const int4 v = r[m >> 2];
+                            const int c = (m & 3) == 0 ? v.x : (m & 3) == 1 ? v.y : (m & 3) == 2 ? v.z : v.w;
+                            if (acc < remaining && acc + c >= remaining) {
+                                sel[0] = base + m;
+                                sel[1] = acc;
+                                sel[2] = c;
+                            }
+                            acc += c;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const int sel_digit = sel[0], sel_above = sel[1], sel_cnt = sel[2];
+            remaining -= sel_above;
+            prefix |= (uint32_t)sel_digit << shift;
+            pmask |= (uint32_t)(nb - 1) << shift;
+            if (sel_cnt == remaining) {
+                // the whole bin is kept: every key >= prefix (low bits zero) is selected
+                take_eq = ALL_EQ;
+                break;
+            }
+        }
+        thresh = prefix;
+        if (take_eq < 0) take_eq = remaining;
+    }
+
+    // final pass: contiguous chunks (multiples of 4) per thread, in pool order
+    const int chunk = ((n + TK_THREADS - 1) / TK_THREADS + 3) & ~3;
+    const int j0 = min(n, tid * chunk), j1 = min(n, j0 + chunk);
+    int tot;
+    // rank among the keys equal to thresh, needed only when ties are split
+    int eq_before = 0;
+    if (!all && take_eq != ALL_EQ) {
+        int n_eq = 0;
+        for (int j = j0; j < j1; j += 4) {
+            uint32_t kk[4];
+            fetch4<CACHED>(kk, keys_lds, srow, j, n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n_eq += (j + e < j1 && kk[e] == thresh);
+        }
+        eq_before = block_excl_scan(n_eq, wave_buf, &tot);
+    }
+    int n_sel = 0;
+    if (!all) {
+        int e_rank = eq_before;
+        for (int j = j0; j < j1; j += 4) {
+            uint32_t kk[4];
+            fetch4<CACHED>(kk, keys_lds, srow, j, n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e < j1) n_sel += kk[e] > thresh || (kk[e] == thresh && e_rank++ < take_eq);
+        }
+    } else {
+        n_sel = j1 - j0;
+    }
+    const int sel_before = block_excl_scan(n_sel, wave_buf, &tot);
+    int e_rank = eq_before, pos = sel_before;
+    for (int j = j0; j < j1; j += 4) {
+        uint32_t kk[4] = {0u, 0u, 0u, 0u};
+        if (!all) fetch4<CACHED>(kk, keys_lds, srow, j, n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (j + e >= j1) break;
+            const bool keep = all || kk[e] > thresh || (kk[e] == thresh && e_rank++ < take_eq);
+            if (keep) {
+                const int tok = doc_start + kpool * (j + e);
+                if (kpool == 4) {   // the four tokens of the pool as one 16-byte store
+                    *reinterpret_cast<int4*>(row + 4 * pos) = make_int4(tok, tok + 1, tok + 2, tok + 3);
+                } else {
+                    for (int r = 0; r < kpool; ++r) row[pos * kpool + r] = tok + r;
+                }
+                ++pos;
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
     int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid) {
-    __shared__ uint32_t keys_lds[TK_LDS_KEYS];
-    __shared__ int hist[TK_BINS];
+    __shared__ __align__(16) uint32_t keys_lds[TK_LDS_KEYS];
+    __shared__ __align__(16) int hist[2][TK_BINS];
     __shared__ int wave_buf[TK_THREADS / 64];
-    __shared__ int sel_digit, sel_above, sel_cnt;
+    __shared__ int sel[3];   // selected digit, keys in bins above it, keys in it
 
     const int tid = threadIdx.x;
     const int i = blockIdx.x;
@@ -73,13 +229,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int doc_start = cu[qp.doc];
     int32_t* row = indices + (size_t)i * row_width;
     const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
-    const bool cached = n <= TK_LDS_KEYS;
 
-    const bool all = k >= n;  // every visible pool is kept (no scores needed)
-    uint32_t thresh = 0xFFFFFFFFu;  // key of the k-th largest score (k == 0: above every key)
-    int take_eq = 0;                // how many pools equal to thresh are kept (lowest first)
-    if (!all && k > 0) {
-        if (cached) {
+    if (n <= TK_LDS_KEYS) {
+        if (k < n && k > 0) {
             // sixteen loads in flight per thread before their LDS stores
             constexpr int SB = 16;
             for (int j0 = 0; j0 < n; j0 += TK_THREADS * SB) {
@@ -96,88 +248,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
                 }
             }
         }
-        int remaining = k;  // still to choose among keys matching the prefix
-        uint32_t prefix = 0u, pmask = 0u;
-        take_eq = -1;
-#pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            const int width = pass < 2 ? 11 : 10;
-            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-            const int nb = 1 << width;
-            for (int b = tid; b < nb; b += TK_THREADS) hist[b] = 0;
-            __syncthreads();
-            for (int j = tid; j < n; j += TK_THREADS) {
-                uint32_t key = cached ? keys_lds[j] : score_key(srow[j]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1);
-            }
-            __syncthreads();
-            // thread t owns the nb/256 bins just below the top 'nb/256 * t' bins;
-            // a scan over threads counts the keys in bins above each thread's
-            const int per = nb / TK_THREADS;
-            const int top = nb - 1 - per * tid;
-            int cnt_own = 0;
-            for (int e = 0; e < per; ++e) cnt_own += hist[top - e];
-            int tot;
-            const int before = block_excl_scan(cnt_own, wave_buf, &tot);
-            if (before < remaining && before + cnt_own >= remaining) {
-                int acc = before;
-                for (int e = 0; e < per; ++e) {
-                    const int c = hist[top - e];
-                    if (acc < remaining && acc + c >= remaining) {
-                        sel_digit = top - e;
-                        sel_above = acc;
-                        sel_cnt = c;
-                    }
-                    acc += c;
-                }
-            }
-            __syncthreads();
-            remaining -= sel_above;
-            prefix |= (uint32_t)sel_digit << shift;
-            pmask |= (uint32_t)(nb - 1) << shift;
-            if (sel_cnt == remaining) {
-                // the whole bin is kept: every key >= prefix (low bits zero) is selected
-                take_eq = 0x7FFFFFFF;
-                break;
-            }
-        }
-        thresh = prefix;
-        if (take_eq < 0) take_eq = remaining;
-    }
-
-    // final pass: contiguous chunk per thread, in pool order
-    const int chunk = (n + TK_THREADS - 1) / TK_THREADS;
-    const int j0 = min(n, tid * chunk), j1 = min(n, j0 + chunk);
-    int n_eq = 0;
-    if (!all)
-        for (int j = j0; j < j1; ++j) n_eq += ((cached ? keys_lds[j] : score_key(srow[j])) == thresh);
-    int tot;
-    int eq_before = block_excl_scan(n_eq, wave_buf, &tot);
-    int n_sel = 0;
-    if (!all) {
-        int e = eq_before;
-        for (int j = j0; j < j1; ++j) {
-            uint32_t key = cached ? keys_lds[j] : score_key(srow[j]);
-            n_sel += key > thresh || (key == thresh && e++ < take_eq);
-        }
+        topk_row<true>(keys_lds, hist, wave_buf, sel, srow, n, k, kpool, doc_start, row);
     } else {
-        n_sel = j1 - j0;
-    }
-    int sel_before = block_excl_scan(n_sel, wave_buf, &tot);
-    {
-        int e = eq_before, pos = sel_before;
-        for (int j = j0; j < j1; ++j) {
-            bool keep = true;
-            if (!all) {
-                uint32_t key = cached ? keys_lds[j] : score_key(srow[j]);
-                keep = key > thresh || (key == thresh && e++ < take_eq);
-            }
-            if (keep) {
-                const int tok = doc_start + kpool * j;
-                for (int r = 0; r < kpool; ++r) row[pos * kpool + r] = tok + r;
-                ++pos;
-            }
-        }
+        topk_row<false>(keys_lds, hist, wave_buf, sel, srow, n, k, kpool, doc_start, row);
     }
     // own incomplete pool, then padding
     const int base = k * kpool;
