@@ -25,9 +25,9 @@
 //       transposing ds_read_b64_tr_b16 (V is read exactly once per CU), feeds
 //       four MFMAs.
 // The loop is software-pipelined with two barriers per tile: phase 1 runs
-// QK(t+1) together with the first half of PV(t) and the staging of tile t+2;
-// phase 2 runs SM(t+1) together with the second half of PV(t), so the MFMA
-// pipe has work while the softmax waits on LDS.
+// QK(t+1) together with a quarter of PV(t); phase 2 runs SM(t+1) and the
+// staging of tile t+2 together with the rest of PV(t), so the MFMA pipe has
+// work while the softmax and the staging wait on LDS.
 // The softmax reference max of a head is re-based (and O rescaled) only when a
 // tile's max exceeds it by more than 8 (log2 units), so weights stay below 2^8
 // and O is untouched outside the MFMAs on most tiles. LDS rows keep their
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     constexpr int CH = D / 8;               // 16-byte chunks a gathered row brings
     constexpr int KSW = DP / 128;           // QK k-steps (32 columns) per wave: a quarter of the columns
     constexpr int DTW = DP / 128;           // 16-wide O column tiles per wave: an eighth of the columns
-    constexpr int DTA = DTW - DTW / 2;      // of which PV runs in phase 1 (the rest in phase 2)
+    constexpr int DTA = (DTW + 3) / 4;      // of which PV runs in phase 1 (the rest in phase 2)
     constexpr int TILE_B = MLA_TK * RB;     // bytes per LDS tile
     constexpr int IPW = MLA_TK / NW;        // gathered rows per wave per tile
     constexpr int RPL = (64 / CH) < IPW ? (64 / CH) : IPW;  // rows one wave-wide load covers
@@ -305,36 +305,41 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // One pipelined step, for a tile kt with a successor (kt + 1 < ntiles); the
     // ring buffers of tiles kt, kt+1 and kt+2 are BV, BK and BS (compile-time,
     // so LDS addresses are immediates):
-    //   phase 1: QK(kt+1), PV(kt) on the first DTA column tiles, tile kt+2 from
-    //            registers into the ring (its buffer last held tile kt-1, which
-    //            every wave finished before the previous barrier), loads of kt+3;
-    //   phase 2: SM(kt+1) and PV(kt) on the remaining column tiles.
+    //   phase 1: QK(kt+1) and PV(kt) on the first DTA column tiles (the partial
+    //            S of QK is stored after PV is issued, so PV hides the QK
+    //            latency);
+    //   phase 2: SM(kt+1), PV(kt) on the remaining column tiles, tile kt+2
+    //            from registers into the ring (its buffer last held tile kt-1,
+    //            which every wave finished before the previous barrier) and
+    //            the loads of tile kt+3; the MFMAs of PV run under the LDS
+    //            traffic and the softmax arithmetic.
     // O is rescaled first when the softmax of tile kt moved a reference max.
 #define KP_STEP(BV, BK, BS)                                                                       \
     {                                                                                             \
-        if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {                              \
+        const int rb_ = rebase_tile;                                                              \
+        if (kt + 3 < ntiles) {                                                                    \
+            KP_ROWS_OF(kt + 3)                                                                    \
+        }                                                                                         \
+        KP_QK(BK)                                                                                 \
+        KP_READ_P()                                                                               \
+        if (__builtin_amdgcn_readfirstlane(rb_) == kt + 1) {                                      \
             f32x4 al_[4];                                                                         \
             _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
                 al_[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);             \
             _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
                 _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al_[ht];      \
         }                                                                                         \
-        if (kt + 3 < ntiles) {                                                                    \
-            KP_ROWS_OF(kt + 3)                                                                    \
-        }                                                                                         \
-        KP_QK(BK)                                                                                 \
-        KP_QK_STORE()                                                                             \
-        KP_READ_P()                                                                               \
         KP_PV(BV, 0, DTA)                                                                         \
+        KP_QK_STORE()                                                                             \
+        lds_barrier();                                                                            \
+        KP_SM_READ()                                                                              \
+        KP_PV(BV, DTA, DTW)                                                                       \
         if (kt + 2 < ntiles) {                                                                    \
             KP_STORE_TILE(BS)                                                                     \
             if (kt + 3 < ntiles) {                                                                \
                 KP_LOAD_TILE()                                                                    \
             }                                                                                     \
         }                                                                                         \
-        lds_barrier();                                                                            \
-        KP_SM_READ()                                                                              \
-        KP_PV(BV, DTA, DTW)                                                                       \
         KP_SM_FINISH(kt + 1)                                                                      \
         lds_barrier();                                                                            \
         ++kt;                                                                                     \
