@@ -45,14 +45,16 @@ constexpr int MLA_NBUF = 3;   // LDS tiles in the gather ring
 constexpr int MLA_MAX_ROW = 4096;  // index-row entries the LDS list holds
 
 // Chunk permutation of LDS row r: 16-byte chunk c is stored at c ^ row_swz(r)
-// (within aligned groups of 16 chunks, i.e. one pass over the 64 banks).
-// row_swz is a permutation of 0..15 over any 16 consecutive rows (row-wise
-// 16-byte reads of 16 rows hit distinct banks), and its upper three bits differ
-// across rows {0..3, 8..11} and across {4..7, 12..15} (the 8 rows one
-// transposing read touches in 32 lanes hit distinct 32-byte bank groups).
-__device__ __forceinline__ int row_swz(int r) {
-    return ((r & 3) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
-}
+// (within aligned groups of 16 chunks, one pass over the 64 banks).
+// gfx950 services a 16-byte LDS read in four passes of 16 lanes (lanes
+// {0-3, 12-15, 20-27}, {4-11, 16-19, 28-31} and the same in the upper half),
+// 8-byte and transposing reads in two passes of 32 consecutive lanes, and
+// 16-byte writes in passes of 8 consecutive lanes. This linear map of the row
+// bits (row bits 0, 1, 2, 3 -> chunk masks 2, 4, 8, 9) is conflict-free, under
+// those passes, for the row-wise K reads (16 rows, one chunk column per lane
+// group), the column-wise transposing V reads (8 rows per pass) and the
+// row-contiguous staging writes.
+__device__ __forceinline__ int row_swz(int r) { return ((r & 7) << 1) ^ (((r >> 3) & 1) * 9); }
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((KP_LDS bf16x4*)(p));
@@ -61,7 +63,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
 // compiler-only barrier: keeps LDS accesses on their side of the explicit waits
 __device__ __forceinline__ void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
 
-constexpr int P_STRIDE = 80;   // bytes per head row of the P tile (32 bf16 + 16 pad: conflict-free reads)
+constexpr int P_STRIDE = 96;   // bytes per head row of the P tile (32 bf16 + 32 pad: conflict-free 16-byte reads)
 constexpr int SP_STRIDE = 36;  // floats per head row of a partial-S block (32 + 4 pad)
 
 __device__ __forceinline__ void wait_lgkm0() {
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     constexpr int RPL = (64 / CH) < IPW ? (64 / CH) : IPW;  // rows one wave-wide load covers
     constexpr int NL = IPW / RPL;           // such loads per wave per tile
     static_assert(NW == 8 && CH >= 8 && CH <= 64 && 64 % CH == 0 && IPW % RPL == 0, "tile staging split");
-    static_assert(DP * 2 * 64 <= MLA_NBUF * TILE_B, "output staging fits the ring");
+    static_assert((D * 2 + 16) * 64 <= MLA_NBUF * TILE_B, "output staging fits the ring");
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
     __shared__ int32_t list[MLA_MAX_ROW];
@@ -415,7 +417,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     __syncthreads();   // all waves done with the ring; sums visible
     if (lse && tid < heads)
         lse[(size_t)i * heads + tid] = (mref_s[tid] + log2f(lsum[tid * 2 + 1])) * 0.69314718055994530942f;
-    // stage O (bf16, [head][D]) in the ring, then copy the real heads out
+    // stage O (bf16, [head][D], rows padded by 16 bytes against bank conflicts)
+    // in the ring, then copy the real heads out
     uint16_t* stage = reinterpret_cast<uint16_t*>(ring);
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -428,15 +431,17 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             if (col < D) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    stage[(16 * ht + 4 * g + e) * D + col] = f32_to_bf16_rne(o[ht][dtl][e] * inv[e]);
+                    stage[(16 * ht + 4 * g + e) * (D + 8) + col] = f32_to_bf16_rne(o[ht][dtl][e] * inv[e]);
             }
         }
     }
     __syncthreads();
-    const uint4* src = reinterpret_cast<const uint4*>(stage);
     uint4* dst = reinterpret_cast<uint4*>(orow);
     const int nvec = heads * D / 8;
-    for (int e = tid; e < nvec; e += NT) dst[e] = src[e];
+    for (int e = tid; e < nvec; e += NT) {
+        const int h = e / (D / 8), c = e % (D / 8);
+        dst[e] = *reinterpret_cast<const uint4*>(ring + h * (D * 2 + 16) + c * 16);
+    }
 #undef KP_ROWS_OF
 #undef KP_LOAD_TILE
 #undef KP_STORE_TILE
