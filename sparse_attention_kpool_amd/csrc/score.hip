@@ -9,7 +9,8 @@
 // positive.
 //
 // Work decomposition: a workgroup takes 16 queries, stages their codes in LDS
-// once, and walks the pools its queries see in chunks of 512; for each chunk,
+// once, and walks the pools its queries see in chunks of 512 (all of them, or
+// every n-th when there are too few query tiles to fill the GPU); for each chunk,
 // each of its 8 waves holds the E4M3 codes of 64 pools (4 tiles of 16) in
 // registers as the B operand (few enough registers for four waves per SIMD,
 // so one wave's ReLU/weighting overlaps another's MFMAs). The query tile sits in LDS head-major; for each
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int32_t* __restrict__ q_pos, int num_q, const uint8_t* __restrict__ q8,
     const float* __restrict__ sq, const float* __restrict__ w, int h_idx, int d_idx,
     const uint8_t* __restrict__ k8, const float* __restrict__ sk, int max_pools,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, int nsplit) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* q_lds = smem;                                                 // [h_idx][QT][128]
     float* wq_lds = reinterpret_cast<float*>(smem + (size_t)h_idx * SC_QT * 128);  // [h_idx][QT]
@@ -105,7 +106,10 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int nqt = (num_q + SC_QT - 1) / SC_QT;
-    const int qtile = nqt - 1 - (int)blockIdx.x;
+    // query tile, and which of the tile's 512-pool chunks this workgroup takes
+    // (every nsplit-th: few query tiles, as in decode, still fill the GPU)
+    const int qtile = nqt - 1 - (int)(blockIdx.x / nsplit);
+    const int split = (int)(blockIdx.x % nsplit);
     const int q0 = qtile * SC_QT;
 
     if (tid < SC_QT) {
@@ -133,7 +137,8 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     }
     __syncthreads();
     const int plo = plo_s, phi = phi_s;
-    if (plo >= phi) return;
+    const int P_first = (plo / SC_PC + split) * SC_PC;
+    if (plo >= phi || P_first >= phi) return;
 
     // stage the query tile, head-major: codes (zero-padded to 128 bytes) and w*sq
     const int dchunks = d_idx >> 4;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
     __syncthreads();
 
-    for (int P0 = plo / SC_PC * SC_PC; P0 < phi; P0 += SC_PC) {
+    for (int P0 = P_first; P0 < phi; P0 += SC_PC * nsplit) {
         const int Pw = P0 + wave * SC_PW;
         // pool tiles [jlo, jhi) of this wave that some query of the tile sees
         int jlo = SC_NJ, jhi = 0;
@@ -234,12 +239,21 @@ hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools
                         const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
                         int max_pools, float* scores, hipStream_t stream) {
     if (num_q == 0 || max_pools == 0) return hipSuccess;
-    const dim3 grid((unsigned)((num_q + SC_QT - 1) / SC_QT));
+    // split the pools of a query tile over several workgroups when the tiles
+    // alone give fewer than ~2048 workgroups
+    const int nqt = (num_q + SC_QT - 1) / SC_QT;
+    const int nchunks = (max_pools + SC_PC - 1) / SC_PC;
+    int nsplit = (2048 + nqt - 1) / nqt;
+    if (nsplit > nchunks) nsplit = nchunks;
+    if (nsplit < 1) nsplit = 1;
+    const long long nblk = (long long)nqt * nsplit;
+    if (nblk > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)nblk);
     const size_t lds = (size_t)h_idx * SC_QT * (128 + 4);
     hipError_t e = hipFuncSetAttribute((const void*)score_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     score_kernel<<<grid, SC_THREADS, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx,
-                                             k8, sk, max_pools, scores);
+                                             k8, sk, max_pools, scores, nsplit);
     return hipGetLastError();
 }
 

@@ -45,8 +45,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-// Exclusive scan of one int per thread over the block; returns the prefix and
-// writes the total to *total.
+// Exclusive scan of one int per thread over a block of NTH threads; returns
+// the prefix and writes the total to *total.
+template <int NTH = TK_THREADS>
 __device__ __forceinline__ int block_excl_scan(int v, int* wave_buf, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int x = wave_incl_scan(v);
@@ -54,7 +55,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wave_buf, int* total)
     __syncthreads();
     int add = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < TK_THREADS / 64; ++w) {
+    for (int w = 0; w < NTH / 64; ++w) {
         int t = wave_buf[w];
         if (w < wave) add += t;
         tot += t;
@@ -214,7 +215,7 @@ __device__ __forceinline__ void topk_row(const uint32_t* keys_lds, int (*hist)[T
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
-    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid) {
+    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid, int skip_long) {
     __shared__ __align__(16) uint32_t keys_lds[TK_LDS_KEYS];
     __shared__ __align__(16) int hist[2][TK_BINS];
     __shared__ int wave_buf[TK_THREADS / 64];
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int doc_start = cu[qp.doc];
     int32_t* row = indices + (size_t)i * row_width;
     const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
+    if (skip_long && n > TK_LDS_KEYS) return;   // a row for topk_long_kernel
 
     if (n <= TK_LDS_KEYS) {
         if (k < n && k > 0) {
@@ -260,13 +262,216 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     if (tid == 0 && num_valid) num_valid[i] = base + n_tail;
 }
 
+// ------------------------------------------------------------- long rows ----
+// Rows with more visible pools than the LDS key cache (decode over a long
+// context) get a workgroup of 1024 threads: the same radix select with the
+// scores streamed from memory in 16-byte loads, several in flight per thread;
+// when the boundary bin is kept whole (no tie is split) the kept pools are
+// collected in LDS in any order, sorted (bitonic) and written out with
+// contiguous 16-byte stores. A row whose selection splits ties takes the
+// ordered chunk scan of the short-row kernel instead.
+constexpr int TL_THREADS = 1024;
+constexpr int TL_LIST = 4096;    // kept pools collected in LDS
+
+__device__ __forceinline__ void fetch4_g(uint32_t (&kk)[4], const float* srow, int j, int n, bool aligned) {
+    if (aligned && j + 3 < n) {
+        const float4 v = *reinterpret_cast<const float4*>(srow + j);
+        kk[0] = score_key(v.x); kk[1] = score_key(v.y); kk[2] = score_key(v.z); kk[3] = score_key(v.w);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[e] = j + e < n ? score_key(srow[j + e]) : 0u;
+    }
+}
+
+__global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid) {
+    __shared__ __align__(16) int hist[2][TK_BINS];
+    __shared__ int wave_buf[TL_THREADS / 64];
+    __shared__ int sel[3];
+    __shared__ int list[TL_LIST];
+    __shared__ int list_n;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = blockIdx.x;
+    const int t = q_pos ? q_pos[i] : i;
+    const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
+    const int n = qp.n_vis;
+    if (n <= TK_LDS_KEYS) return;   // a row for topk_kernel
+    const int k = n < topk ? n : topk;
+    const int doc_start = cu[qp.doc];
+    int32_t* row = indices + (size_t)i * row_width;
+    const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
+    const bool aligned = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+    constexpr int ALL_EQ = 0x7FFFFFFF;
+
+    auto put_pool = [&](int pos, int j) {
+        const int tok = doc_start + kpool * j;
+        if (kpool == 4) {
+            *reinterpret_cast<int4*>(row + 4 * pos) = make_int4(tok, tok + 1, tok + 2, tok + 3);
+        } else {
+            for (int r = 0; r < kpool; ++r) row[pos * kpool + r] = tok + r;
+        }
+    };
+
+    if (k >= n) {   // every visible pool is kept, in order
+        for (int j = tid; j < n; j += TL_THREADS) put_pool(j, j);
+    } else if (k > 0) {
+        for (int b = tid; b < TK_BINS; b += TL_THREADS) hist[0][b] = 0;
+        __syncthreads();
+        int remaining = k;
+        uint32_t prefix = 0u, pmask = 0u;
+        int take_eq = -1;
+#pragma unroll 1
+        for (int pass = 0; pass < 3; ++pass) {
+            const int width = pass < 2 ? 11 : 10;
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int nb = 1 << width;
+            int* h = hist[pass & 1];
+#pragma unroll 4
+            for (int j = 4 * tid; j < n; j += 4 * TL_THREADS) {
+                uint32_t kk[4];
+                fetch4_g(kk, srow, j, n, aligned);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < n && (kk[e] & pmask) == prefix)
+                        atomicAdd(&h[(kk[e] >> shift) & (uint32_t)(nb - 1)], 1);
+            }
+            for (int b = tid; b < TK_BINS; b += TL_THREADS) hist[(pass + 1) & 1][b] = 0;
+            __syncthreads();
+            if (wave == 0) {
+                const int per = nb >> 6;
+                const int base = nb - per * (lane + 1);
+                int4 r[8];
+                int own = 0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    r[q] = make_int4(0, 0, 0, 0);
+                    if (4 * q < per) r[q] = *reinterpret_cast<const int4*>(h + base + 4 * q);
+                    own += r[q].x + r[q].y + r[q].z + r[q].w;
+                }
+                const int incl = wave_incl_scan(own);
+                const int before = incl - own;
+                if (before < remaining && incl >= remaining) {
+                    int acc = before;
+#pragma unroll
+                    for (int m = 31; m >= 0; --m) {
+                        if (m < per) {
+                            const int4 v = r[m >> 2];
+                            const int c = (m & 3) == 0 ? v.x : (m & 3) == 1 ? v.y : (m & 3) == 2 ? v.z : v.w;
+                            if (acc < remaining && acc + c >= remaining) {
+                                sel[0] = base + m;
+                                sel[1] = acc;
+                                sel[2] = c;
+                            }
+                            acc += c;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const int sel_digit = sel[0], sel_above = sel[1], sel_cnt = sel[2];
+            remaining -= sel_above;
+            prefix |= (uint32_t)sel_digit << shift;
+            pmask |= (uint32_t)(nb - 1) << shift;
+            if (sel_cnt == remaining) {
+                take_eq = ALL_EQ;
+                break;
+            }
+        }
+        const uint32_t thresh = prefix;
+        if (take_eq < 0) take_eq = remaining;
+
+        if (take_eq == ALL_EQ && k <= TL_LIST) {
+            // exactly the k keys >= thresh are kept: collect, sort, write
+            if (tid == 0) list_n = 0;
+            __syncthreads();
+#pragma unroll 4
+            for (int j = 4 * tid; j < n; j += 4 * TL_THREADS) {
+                uint32_t kk[4];
+                fetch4_g(kk, srow, j, n, aligned);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < n && kk[e] >= thresh) {
+                        const int pos = atomicAdd(&list_n, 1);   // ends at exactly k
+                        if (pos < TL_LIST) list[pos] = j + e;
+                    }
+            }
+            __syncthreads();
+            int P = 1;
+            while (P < k) P <<= 1;
+            for (int p = k + tid; p < P; p += TL_THREADS) list[p] = 0x7FFFFFFF;
+            __syncthreads();
+            for (int size = 2; size <= P; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    for (int p = tid; p < P / 2; p += TL_THREADS) {
+                        const int lo = 2 * stride * (p / stride) + (p % stride), hi = lo + stride;
+                        const bool up = (lo & size) == 0;
+                        const int a = list[lo], b = list[hi];
+                        if ((a > b) == up) {
+                            list[lo] = b;
+                            list[hi] = a;
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            for (int pos = tid; pos < k; pos += TL_THREADS) put_pool(pos, list[pos]);
+        } else {
+            // ties split (or too many kept for LDS): ordered contiguous chunks per thread
+            const int chunk = ((n + TL_THREADS - 1) / TL_THREADS + 3) & ~3;
+            const int j0 = min(n, tid * chunk), j1 = min(n, j0 + chunk);
+            int tot, n_eq = 0, n_sel = 0;
+            for (int j = j0; j < j1; j += 4) {
+                uint32_t kk[4];
+                fetch4_g(kk, srow, j, n, aligned);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) n_eq += (j + e < j1 && kk[e] == thresh);
+            }
+            const int eq_before = block_excl_scan<TL_THREADS>(n_eq, wave_buf, &tot);
+            int e_rank = eq_before;
+            for (int j = j0; j < j1; j += 4) {
+                uint32_t kk[4];
+                fetch4_g(kk, srow, j, n, aligned);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < j1) n_sel += kk[e] > thresh || (kk[e] == thresh && e_rank++ < take_eq);
+            }
+            int pos = block_excl_scan<TL_THREADS>(n_sel, wave_buf, &tot);
+            e_rank = eq_before;
+            for (int j = j0; j < j1; j += 4) {
+                uint32_t kk[4];
+                fetch4_g(kk, srow, j, n, aligned);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (j + e >= j1) break;
+                    if (kk[e] > thresh || (kk[e] == thresh && e_rank++ < take_eq)) put_pool(pos++, j + e);
+                }
+            }
+        }
+    }
+    // own incomplete pool, then padding
+    const int base = k * kpool;
+    const int n_tail = t - qp.tail_start + 1;
+    for (int r = tid; r < row_width - base; r += TL_THREADS)
+        row[base + r] = r < n_tail ? qp.tail_start + r : -1;
+    if (tid == 0 && num_valid) num_valid[i] = base + n_tail;
+}
+
 hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
                        const int32_t* q_pos, int num_q, const float* scores, int max_pools,
                        int topk, int row_width, int32_t* indices, int32_t* num_valid,
                        hipStream_t stream) {
     if (num_q == 0) return hipSuccess;
+    // rows with more visible pools than the key cache holds go to the long-row kernel
+    const int has_long = max_pools > TK_LDS_KEYS;
     topk_kernel<<<num_q, TK_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools,
-                                                  topk, row_width, indices, num_valid);
+                                                  topk, row_width, indices, num_valid, has_long);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !has_long) return e;
+    topk_long_kernel<<<num_q, TL_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools,
+                                                       topk, row_width, indices, num_valid);
     return hipGetLastError();
 }
 

@@ -144,7 +144,8 @@ def test_scores_fed_oracle_keys(K, oracle_mod, name):
 
 # ------------------------------------------------------------------ top-k -----
 @pytest.mark.parametrize("case", ["tiny", "2k", "packed4k", "ties", "zeros", "negzero", "nan", "topk0",
-                                  "decode1m_rows"])
+                                  "decode1m_rows", "long_rand", "long_ties", "long_zeros", "long_nan",
+                                  "long_bigk"])
 def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
     rng = np.random.default_rng(7)
     if case in ("tiny", "2k", "packed4k"):
@@ -166,6 +167,24 @@ def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
         sc = oracle_mod.scores(s.cu, cp, s.kpool, qpos, s.max_pools, wl.full("w")[rows], qc, qs, k8[:len(ps)],
                                sk[:len(ps)])
         T, topk, cu = s.T, s.topk, s.cu
+    elif case.startswith("long_"):
+        # rows with more visible pools than the short-row kernel caches (decode-like),
+        # mixed with short rows in the same launch
+        T = 65536
+        cu = np.array([0, T], np.int32)
+        cp, _ = oracle_mod.layout(cu, T, 4)
+        qpos = np.array([100, 32770, 32771, 33000, 35000, 40000, 45000, 50001, 60000, 65533, 65534, 65535],
+                        np.int32)
+        sc = rng.standard_normal((len(qpos), T // 4)).astype(np.float32)
+        if case == "long_ties":
+            sc = np.round(sc * 2).astype(np.float32)          # heavy ties: the k-th score is shared
+        if case == "long_zeros":
+            sc = np.maximum(np.round(sc * 2), 0).astype(np.float32)
+        if case == "long_nan":
+            sc[rng.random(sc.shape) < 0.01] = np.nan
+            sc[rng.random(sc.shape) < 0.01] = -np.inf
+            sc[rng.random(sc.shape) < 0.2] = -0.0
+        topk = 5000 if case == "long_bigk" else 512
     else:
         T = 5000
         cu = np.array([0, 700, 700, 2900, 2903, 5000], np.int32)
