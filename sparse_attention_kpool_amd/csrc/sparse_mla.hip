@@ -80,6 +80,22 @@ __device__ __forceinline__ void lds_barrier() {
     compiler_fence();
 }
 
+// Workgroups are handed to the eight XCDs round-robin by their index, and each
+// XCD has its own L2. Queries of one document that are close in position pick
+// mostly the same pools, so the workgroup -> query map gives each XCD runs of
+// MLA_XCD_RUN consecutive queries: the latent rows they gather are then shared
+// through one L2. Runs go to the XCDs in turn, which keeps the long and the
+// short rows of a causal batch spread over all of them. A bijection on
+// [0, n): the last n % (8 * MLA_XCD_RUN) workgroups keep their own index.
+#define MLA_XCD_RUN 32
+__device__ __forceinline__ int xcd_query(int b, int n) {
+    constexpr int R = MLA_XCD_RUN;
+    const int full = n / (8 * R) * (8 * R);
+    if (b >= full) return b;
+    const int slot = b >> 3, xcd = b & 7;   // slot-th workgroup that lands on this XCD
+    return (slot / R) * (8 * R) + xcd * R + slot % R;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ indices,
@@ -112,7 +128,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int i = blockIdx.x;
+    const int i = xcd_query(blockIdx.x, gridDim.x);
     const int cq = wave & 3;    // QK: column quarter
     const int rh = wave >> 2;   // QK: row half of the tile
 
