@@ -26,8 +26,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-munsafe-fp-at
 
 # Per-file additions. The scoring kernel consumes each MFMA result in VALU
 # code right away: asking for MFMA results in ordinary VGPRs (instead of the
-# accumulation registers) lets the compiler keep eight MFMAs in flight.
-EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# accumulation registers) lets the compiler keep eight MFMAs in flight. The
+# attention kernel's QK scores are read by the softmax the same way (its O
+# accumulators are pinned to AGPRs by inline assembly and unaffected).
+EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

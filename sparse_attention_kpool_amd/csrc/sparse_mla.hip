@@ -7,27 +7,25 @@
 // attends to the rows its index row names (up to 2051 of them, "cuDNN sparse
 // MLA parity and performance").
 //
-// One workgroup of 8 waves (two per SIMD) per query token (64 heads). The
-// index row is compacted in LDS (masked entries dropped, order kept); its
-// latent rows are gathered 32 at a time: each wave loads 4 whole rows (16-byte
-// loads, 1 KB per wave-wide load) into registers and writes them into a 3-tile
-// LDS ring one tile later (plain vector loads keep the gather near the memory
-// system's random-row bandwidth at this occupancy; the direct-to-LDS loads of
-// gfx950 reach well under half of it). The work on a tile t:
-//   QK: wave w computes a partial S^T = K[rows_h, cols_c] . Q[:, cols_c]^T for
-//       the row half h = w/4 and column quarter c = w%4, all 64 heads (bf16
-//       MFMA 16x16x32; Q's columns stay in registers; every K fragment read
-//       from LDS feeds four MFMAs, and K is read once per CU);
-//   SM: the four column partials meet in LDS; wave w adds them for heads
-//       w, w+8, .., w+56 and runs their online softmax, writing P (bf16);
-//   PV: wave w accumulates O[:, cols] += P . V[:, cols] over its eighth of the
-//       latent columns for all 64 heads: one V fragment, read with the
-//       transposing ds_read_b64_tr_b16 (V is read exactly once per CU), feeds
-//       four MFMAs.
-// The loop is software-pipelined with two barriers per tile: phase 1 runs
-// QK(t+1) together with a quarter of PV(t); phase 2 runs SM(t+1) and the
-// staging of tile t+2 together with the rest of PV(t), so the MFMA pipe has
-// work while the softmax and the staging wait on LDS.
+// One workgroup of 4 waves (one per SIMD, so each wave has the whole 512-entry
+// register file) per query token (64 heads). The index row is compacted in LDS
+// (masked entries dropped, order kept); its latent rows are gathered 64 at a
+// time into a 2-tile LDS ring with the direct-to-LDS loads of gfx950 (each
+// wave brings 16 whole rows per tile, issued one tile ahead). Wave w owns the
+// row half rh = w/2 of every tile and the head half hh = w%2, and runs the
+// whole attention of its (rows, heads) block with no exchange between waves:
+//   QK: S^T = K[rows] . Q[heads]^T over all 512 columns (bf16 MFMA 16x16x32;
+//       Q of its 32 heads stays in registers; every K fragment feeds two MFMAs);
+//   SM: online softmax of each head over its 32 rows, in registers: the MFMA
+//       row order is permuted so that each lane's eight S values are exactly the
+//       eight P values it feeds to PV as the B operand;
+//   PV: O^T[cols, heads] += V^T[cols, rows] . P^T[rows, heads] for all 512
+//       columns (V read with the transposing ds_read_b64_tr_b16; one V fragment
+//       feeds two MFMAs); O stays in the accumulation registers.
+// The two row halves of a head keep separate softmax states and partial O and
+// are merged once at the end through LDS. The LDS traffic per 32 gathered rows
+// is the 32 KB gather plus 128 KB of K and V reads (each row is read by the
+// two head halves), with one barrier per 64 rows.
 // The softmax reference max of a head is re-based (and O rescaled) only when a
 // tile's max exceeds it by more than 8 (log2 units), so weights stay below 2^8
 // and O is untouched outside the MFMAs on most tiles. LDS rows keep their
@@ -39,10 +37,17 @@
 
 namespace kp {
 
-constexpr int MLA_TK = 32;    // latent rows per tile
-constexpr int MLA_NW = 8;     // waves per workgroup (two per SIMD)
-constexpr int MLA_NBUF = 3;   // LDS tiles in the gather ring
+constexpr int MLA_TK = 64;    // latent rows per tile
+constexpr int MLA_NW = 4;     // waves per workgroup (one per SIMD)
+constexpr int MLA_NBUF = 2;   // LDS tiles in the gather ring
 constexpr int MLA_MAX_ROW = 4096;  // index-row entries the LDS list holds
+// A pass with a first-tile reference sets the reference MLA_REF_LIFT above the
+// max of the head's first tile with a valid row and accepts later tiles up to
+// MLA_HEADROOM above the reference: weights stay below 2^64, so the fp32 sums
+// (and O, for latent values up to 2^50) are far from overflow, and those of the
+// first tile are at least 2^-32, far from underflow.
+#define MLA_REF_LIFT 32.0f
+#define MLA_HEADROOM 64.0f
 
 // Chunk permutation of LDS row r: 16-byte chunk c is stored at c ^ row_swz(r)
 // (within aligned groups of 16 chunks, one pass over the 64 banks).
@@ -63,12 +68,53 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
 // compiler-only barrier: keeps LDS accesses on their side of the explicit waits
 __device__ __forceinline__ void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
 
-constexpr int P_STRIDE = 96;   // bytes per head row of the P tile (32 bf16 + 32 pad: conflict-free 16-byte reads)
-constexpr int SP_STRIDE = 36;  // floats per head row of a partial-S block (32 + 4 pad)
-
 __device__ __forceinline__ void wait_lgkm0() {
     // s_waitcnt lgkmcnt(0) only (vmcnt 63, expcnt 7: no wait)
     __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// Direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane l copies the 16
+// bytes at global address base + voff (base wave-uniform, in SGPRs; voff the
+// lane's 32-bit byte offset) to LDS byte address lds_base + 16*l; lds_base is
+// wave-uniform and travels in M0. Issued as inline assembly so the compiler
+// does not make later LDS reads of the other ring tile wait for it; completion
+// is tracked by the explicit vmcnt wait before each barrier.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+    __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :: "s"(lds_base), "v"(voff), "s"(base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((KP_LDS const uint8_t*)p);
+}
+
+// wait until none of this wave's vector-memory operations is outstanding
+// (vmcnt 0; expcnt 7 and lgkmcnt 15 mean "do not wait" on those counters)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// max / sum over the four lanes n, n+16, n+32, n+48 (v_permlane32_swap and
+// v_permlane16_swap with both operands the value: the pair holds the value of
+// the lane and of its partner 32, then 16, lanes away)
+__device__ __forceinline__ float max_over_groups(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// O^T accumulation of PV, kept in the accumulation registers: c += a . b with
+// the accumulator pinned to AGPRs (the whole 256-entry AGPR file holds a
+// wave's O). Every accumulator takes one such MFMA per tile, and its readers
+// (the rare rescale and the final merge) come a full tile later, so no extra
+// wait states are needed around it.
+__device__ __forceinline__ void mfma_acc(f32x4& c, bf16x8 a, bf16x8 b) {
+    __asm__ __volatile__("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 // Barrier that orders LDS traffic between waves but does not wait for the
@@ -106,62 +152,92 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     constexpr int DP = D < 128 ? 128 : D;   // latent width in LDS (zero-padded)
     constexpr int RB = DP * 2;              // LDS bytes per latent row
     constexpr int CH = D / 8;               // 16-byte chunks a gathered row brings
-    constexpr int KSW = DP / 128;           // QK k-steps (32 columns) per wave: a quarter of the columns
-    constexpr int DTW = DP / 128;           // 16-wide O column tiles per wave: an eighth of the columns
-    constexpr int DTA = (DTW + 3) / 4;      // of which PV runs in phase 1 (the rest in phase 2)
+    constexpr int KS = DP / 32;             // QK k-steps (32 columns each)
+    constexpr int CT = DP / 16;             // 16-wide O column tiles
     constexpr int TILE_B = MLA_TK * RB;     // bytes per LDS tile
-    constexpr int IPW = MLA_TK / NW;        // gathered rows per wave per tile
-    constexpr int RPL = (64 / CH) < IPW ? (64 / CH) : IPW;  // rows one wave-wide load covers
-    constexpr int NL = IPW / RPL;           // such loads per wave per tile
-    static_assert(NW == 8 && CH >= 8 && CH <= 64 && 64 % CH == 0 && IPW % RPL == 0, "tile staging split");
-    static_assert((D * 2 + 16) * 64 <= MLA_NBUF * TILE_B, "output staging fits the ring");
+    constexpr int RPW = MLA_TK / NW;        // rows each wave gathers per tile
+    constexpr int XB = (CT / 2) * 2 * 64 * 16;  // bytes of O one wave hands to its partner
+    static_assert(NW == 4 && MLA_TK == 64 && RPW == 16 && CH >= 8 && CH <= 64, "tile split");
+    static_assert(4 * XB <= MLA_NBUF * TILE_B, "row-half merge fits the ring");
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
-    __shared__ int32_t list[MLA_MAX_ROW];
-    __shared__ __align__(16) float spart[4 * 64 * SP_STRIDE];   // partial S, [column quarter][head][row]
-    __shared__ __align__(16) uint8_t ptile[64 * P_STRIDE];      // P, bf16 [head][row]
-    __shared__ __align__(16) float alpha_s[64];                 // per-head rescale of the last softmax tile
-    __shared__ int rebase_tile;                                 // last tile (+1) that moved a reference max
-    __shared__ float lsum[64 * 2];                              // per-head (rounded, exact) sums
-    __shared__ float mref_s[64];                                // per-head final reference max
-    __shared__ int wave_buf[NW];
+    __shared__ __align__(16) int32_t list[MLA_MAX_ROW];   // byte offsets of the listed latent rows
+    __shared__ float mls[2][64][3];   // per row half and head: reference max, sums
+    __shared__ int rcnt[MLA_MAX_ROW / NT * NW];   // valid entries per (round, wave) of the compaction
+    __shared__ int rflag[2];          // a wave saw a score too far above its reference, by step parity
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
+    const int rh = wave >> 1;   // row half of every tile
+    const int hh = wave & 1;    // head half
     const int i = xcd_query(blockIdx.x, gridDim.x);
-    const int cq = wave & 3;    // QK: column quarter
-    const int rh = wave >> 2;   // QK: row half of the tile
+
+    // ---- Q first: its loads overlap the index row's ---------------------------------
+    // B operand of S^T = K . Q^T for this wave's 32 heads
+    // qf[ht][ks]: head 32*hh + 16*ht + n, columns 32*ks + 8*g .. +7
+    // (every lane loads from a valid address, and heads past `heads` and the
+    // columns of a zero-padded narrow latent are zeroed after the load: no branch
+    // holds back the stream of loads)
+    bf16x8 qf[2][KS];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        const int head = 32 * hh + 16 * ht + n;
+        const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int col = 32 * ks + 8 * g;
+            const bool ok = head < heads && (DP == D || col < D);
+            uint4 v = *reinterpret_cast<const uint4*>(qrow + (DP == D ? col : min(col, D - 8)));
+            if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+            qf[ht][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
 
     // ---- compact the index row (valid entries, original order) ----------------
+    // Entry NT*k + tid is read in round k; the loads of all rounds are issued
+    // together (one memory latency), each wave counts its valid entries of a
+    // round with a ballot, and one scan over the (round, wave) counts places
+    // every entry.
+    constexpr int NRND = MLA_MAX_ROW / NT;
     const int32_t* irow = indices + (size_t)i * row_width;
-    const int per = (row_width + NT - 1) / NT;
-    const int j0 = min(row_width, tid * per), j1 = min(row_width, j0 + per);
-    int cnt = 0;
-    for (int j = j0; j < j1; ++j) {
-        int v = irow[j];
-        cnt += (v >= 0 && v < num_kv);
-    }
-    int x = cnt;
+    int ent[NRND];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int u = __shfl_up(x, o, 64);
-        if (lane >= o) x += u;
+    for (int k = 0; k < NRND; ++k) {
+        const int j = NT * k + tid;
+        ent[k] = -1;
+        if (NT * k < row_width && j < row_width) ent[k] = irow[j];
     }
-    if (lane == 63) wave_buf[wave] = x;
-    if (DP != D) {   // zero the padding columns of the ring once; the staging never writes them
+    if (tid < 2) rflag[tid] = 0;
+    if (DP != D) {   // zero the padding columns of the ring once; the gather never writes them
         for (int e = tid; e < MLA_NBUF * TILE_B / 16; e += NT)
             reinterpret_cast<uint4*>(ring)[e] = make_uint4(0u, 0u, 0u, 0u);
     }
-    __syncthreads();
-    int before = x - cnt, n_valid = 0;
+    unsigned long long bal[NRND];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        if (w < wave) before += wave_buf[w];
-        n_valid += wave_buf[w];
+    for (int k = 0; k < NRND; ++k) {
+        bal[k] = __ballot(ent[k] >= 0 && ent[k] < num_kv);
+        if (lane == 0) rcnt[k * NW + wave] = __popcll(bal[k]);
     }
-    for (int j = j0; j < j1; ++j) {
-        int v = irow[j];
-        if (v >= 0 && v < num_kv) list[before++] = v;
+    __syncthreads();
+    int n_valid;
+    {
+        static_assert(NRND * NW == 64, "one count per lane");
+        const int c = rcnt[lane];
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(x, o, 64);
+            if (lane >= o) x += u;
+        }
+        n_valid = __builtin_amdgcn_readfirstlane(__shfl(x, 63, 64));
+        const int excl = x - c;   // entries before (round, wave) = lane's pair
+#pragma unroll
+        for (int k = 0; k < NRND; ++k) {
+            const int base = __shfl(excl, k * NW + wave, 64);
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0u));
+            if (ent[k] >= 0 && ent[k] < num_kv) list[base + below] = ent[k] * (D * 2);   // byte offset
+        }
     }
     __syncthreads();
     // pad the list to whole tiles with a valid row (its scores are masked), so
@@ -179,288 +255,334 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         return;
     }
     const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
-    if (tid == 0) rebase_tile = 0;   // visible after the first barrier below
 
-    // ---- gather: wave w stages tile rows IPW*w .. IPW*w + IPW-1 --------------------
-    // Load j of a tile: lane l (< RPL*CH) covers tile row r = IPW*w + j*RPL + l/CH
-    // and its 16-byte chunk l%CH, which lands in LDS at chunk (l%CH) ^ row_swz(r).
-    const int lrow = lane / CH, lchunk = lane % CH;
-    const bool lact = lane < RPL * CH;
-    const int srow0 = wave * IPW + lrow;     // tile row of this lane's first load
-    int sto[NL];                             // LDS offsets of this lane's staged chunks
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const int r = srow0 + j * RPL;
-        sto[j] = r * RB + ((lchunk ^ row_swz(r)) << 4);
+    // ---- gather: wave w brings tile rows 16w .. 16w+15 straight into the ring;
+    // lane l copies the row's 16-byte chunk l ^ row_swz(r) to LDS chunk l of ring
+    // row r (lanes whose chunk lies in the zero padding of a narrow latent idle)
+    const uint32_t ring_lds = lds_addr(ring);
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
+    const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row, before the chunk xor
+    // KP_ROWS_OF reads the byte offsets of this wave's 16 rows of tile kt_ into rws_[16];
+    // KP_ISSUE_ROW(j_) issues the gather of the wave's row j_ into buffer buf_
+#define KP_ROWS_OF(kt_)                                                                        \
+    int rws_[RPW];   /* wave-uniform: scalar registers */                                      \
+    _Pragma("unroll") for (int c4_ = 0; c4_ < RPW / 4; ++c4_) {                                \
+        const int4 rw_ = *reinterpret_cast<const int4*>(list + (kt_) * MLA_TK + RPW * wave_s + 4 * c4_); \
+        rws_[4 * c4_] = __builtin_amdgcn_readfirstlane(rw_.x);                                 \
+        rws_[4 * c4_ + 1] = __builtin_amdgcn_readfirstlane(rw_.y);                             \
+        rws_[4 * c4_ + 2] = __builtin_amdgcn_readfirstlane(rw_.z);                             \
+        rws_[4 * c4_ + 3] = __builtin_amdgcn_readfirstlane(rw_.w);                             \
     }
-    u32x4 stg[NL];                           // a tile in flight
-    int rows_next[NL];                       // latent rows of the next tile to load
-#define KP_ROWS_OF(kt_)                                                              \
-    _Pragma("unroll") for (int j = 0; j < NL; ++j) {                                 \
-        rows_next[j] = list[(kt_) * MLA_TK + srow0 + j * RPL];                       \
+#define KP_ISSUE_ROW(j_, buf_)                                                                 \
+    {                                                                                          \
+        const int r_ = RPW * wave_s + (j_);   /* r_ % 16 = j_ */                               \
+        const uint32_t off_ = lane16 ^ (uint32_t)(row_swz(j_) << 4);   /* chunk lane ^ swz */  \
+        if (DP == D || (lane < DP / 8 && (off_ >> 4) < (uint32_t)CH))                          \
+            lds_dma16(reinterpret_cast<const uint8_t*>(kv) + (uint32_t)rws_[j_], off_,         \
+                      __builtin_amdgcn_readfirstlane(ring_lds + (uint32_t)((buf_) * TILE_B + r_ * RB))); \
     }
-#define KP_LOAD_TILE()                                                               \
-    if (lact) {                                                                      \
-        _Pragma("unroll") for (int j = 0; j < NL; ++j)                               \
-            stg[j] = *reinterpret_cast<const u32x4*>(                                \
-                reinterpret_cast<const uint8_t*>(kv) +                               \
-                ((uint32_t)rows_next[j] * (uint32_t)(D * 2) + 16u * (uint32_t)lchunk)); \
-    }
-#define KP_STORE_TILE(buf_)                                                          \
-    if (lact) {                                                                      \
-        _Pragma("unroll") for (int j = 0; j < NL; ++j)                               \
-            *reinterpret_cast<u32x4*>(ring + (buf_) * TILE_B + sto[j]) = stg[j];     \
-    }
-
-    // ---- Q of this wave's column quarter for all 64 heads, B-operand layout ---------
-    bf16x8 qf[4][KSW];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-        const int head = 16 * ht + n;
-#pragma unroll
-        for (int s = 0; s < KSW; ++s) {
-            const int col = cq * (DP / 4) + 32 * s + 8 * g;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (head < heads && col < D) v = *reinterpret_cast<const uint4*>(q + ((size_t)i * heads + head) * D + col);
-            qf[ht][s] = __builtin_bit_cast(bf16x8, v);
-        }
+#define KP_ISSUE_TILE(kt_, buf_)                                                               \
+    {                                                                                          \
+        KP_ROWS_OF(kt_)                                                                        \
+        _Pragma("unroll") for (int j = 0; j < RPW; ++j) KP_ISSUE_ROW(j, buf_)                  \
     }
 
-    // PV state: O for heads 16*ht + 4*g + e, columns 16*(wave*DTW + dtl) + n
-    f32x4 o[4][DTW];
+    // O^T accumulators: o[ct][ht] holds columns 16*ct + 4*g + e of head 32*hh + 16*ht + n
+    f32x4 o[CT][2];
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // softmax state: wave w owns heads w, w+8, .., w+56 (lanes 8j..8j+7 hold head
-    // w+8j, rows 4*(lane&7) .. +3; a row-group reduction stays inside 8 lanes)
-    const int hown = wave + 8 * (lane >> 3);
-    const int srow = 4 * (lane & 7);
-    float m_ref = -INFINITY, l_run = 0.f, l_lse = 0.f;
+        for (int ht = 0; ht < 2; ++ht) o[ct][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // softmax state of head 32*hh + 16*ht + n over this wave's rows (the four lanes
+    // of a head hold the same reference max and their own partial sums). O is
+    // never rescaled inside the loop (its accumulators live in AGPRs, and a
+    // rescale there costs more registers than a wave has), so the reference is
+    // fixed for a pass: it is set from the max of the head's first tile with a
+    // valid row, and the weights of later tiles may exceed 1, up to
+    // 2^MLA_HEADROOM. A tile
+    // whose max goes beyond that flags the workgroup, which then drops the pass,
+    // sweeps QK over all tiles for the exact max of every head, and runs the
+    // attention again with that max as the reference. The unset reference is
+    // finite and far below any score, so a row half with no valid row at all
+    // keeps zero weights.
+    float m_ref[2] = {-1e30f, -1e30f}, l_lse[2] = {0.f, 0.f};
+    // the sum of the rounded (bf16) weights of head 32*hh + 16*ht + n over the
+    // wave's rows, accumulated by an MFMA with an all-ones A operand (every entry
+    // of lsum[ht] holds the full sum); l_lse keeps the lane's share of the sum of
+    // the unrounded weights
+    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    // fixed per-lane LDS offsets
-    const int rq = 16 * rh + n;                      // K row this lane feeds
-    int kb[KSW];                                     // K chunk of each k-step
+    // K rows are fed to the MFMA in a permuted order: A row m of sub-tile s is
+    // tile row 32*rh + 8*(m/4) + 4*s + m%4, so that S^T lane (g, n) ends up with
+    // rows 32*rh + 8*g + 4*s + e (s = 0, 1; e = 0..3): the eight rows of its P^T
+    // B operand for PV. K-step ks reads chunk 4*ks + g of that row, stored at
+    // (4*ks + g) ^ row_swz(r) = 16*(ks/4) + (4*(ks%4) ^ (g ^ row_swz(r))): byte
+    // offset kb[s] + 256*(ks/4) + ((64*(ks%4)) ^ kx[s]).
+    int kb[2], kx[2];
 #pragma unroll
-    for (int s = 0; s < KSW; ++s)
-        kb[s] = rq * RB + (((cq * (DP / 32) + 4 * s + g) ^ row_swz(rq)) << 4);
+    for (int s = 0; s < 2; ++s) {
+        const int r = 32 * rh + 8 * (n >> 2) + 4 * s + (n & 3);
+        kb[s] = r * RB;
+        kx[s] = (g ^ row_swz(r)) << 4;
+    }
+    // V^T A operand of column tile ct: lane (g, n) needs rows 32*rh + 8*g .. +7 of
+    // column 16*ct + n; two transposing reads (b = 0, 1) of rows
+    // 32*rh + 8*g + 4*b + e4, 8 bytes of chunk 2*ct + q4/2: byte offset
+    // vb[b] + 256*(ct/8) + ((32*(ct%8)) ^ vx[b]).
     const int e4 = (lane >> 2) & 3, q4 = lane & 3;
-    const int vr0 = 8 * g + e4, vr1 = 8 * g + 4 + e4;  // V rows of the two transposing reads
-    int vb0[DTW], vb1[DTW];                          // V chunk of each column tile
+    int vb[2], vx[2];
 #pragma unroll
-    for (int dtl = 0; dtl < DTW; ++dtl) {
-        const int c = 2 * (wave * DTW + dtl) + (q4 >> 1);
-        vb0[dtl] = vr0 * RB + ((c ^ row_swz(vr0)) << 4) + 8 * (q4 & 1);
-        vb1[dtl] = vr1 * RB + ((c ^ row_swz(vr1)) << 4) + 8 * (q4 & 1);
+    for (int b = 0; b < 2; ++b) {
+        const int r = 32 * rh + 8 * g + 4 * b + e4;
+        vb[b] = r * RB + 8 * (q4 & 1);
+        vx[b] = ((q4 >> 1) ^ row_swz(r)) << 4;
     }
-    float* my_sp = spart + cq * 64 * SP_STRIDE;
+    // (the per-step addresses are one xor-add each; an empty asm statement at the
+    // top of every step keeps the compiler from hoisting all of them out of the
+    // loop into registers a wave does not have)
 
-    // QK of tile kt_ into partial S (LDS)
-#define KP_QK(buf_)                                                                               \
-    {                                                                                             \
-        const uint8_t* tb_ = ring + (buf_) * TILE_B;                                              \
-        u32x4 ka_[KSW];                                                                           \
-        _Pragma("unroll") for (int s = 0; s < KSW; ++s) ka_[s] = *reinterpret_cast<const u32x4*>(tb_ + kb[s]); \
-        _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) sp[ht] = f32x4{0.f, 0.f, 0.f, 0.f};     \
-        _Pragma("unroll") for (int s = 0; s < KSW; ++s) {                                         \
-            const bf16x8 af_ = __builtin_bit_cast(bf16x8, ka_[s]);                                \
-            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) sp[ht] = mfma_bf16_16x16x32(af_, qf[ht][s], sp[ht]); \
-        }                                                                                         \
-    }
-    /* lane holds S^T[rows 16*rh + 4*g + e][head 16*ht + n]; stored as [head][row] */
-#define KP_QK_STORE()                                                                             \
-    _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                              \
-        *reinterpret_cast<f32x4*>(my_sp + (16 * ht + n) * SP_STRIDE + 16 * rh + 4 * g) = sp[ht];
-    // full S of the owned heads (4 rows per lane) for tile kt_: read and sum the partials
-#define KP_SM_READ()                                                                              \
-    sv = *reinterpret_cast<const f32x4*>(spart + (0 * 64 + hown) * SP_STRIDE + srow);             \
-    _Pragma("unroll") for (int w = 1; w < 4; ++w)                                                 \
-        sv += *reinterpret_cast<const f32x4*>(spart + (w * 64 + hown) * SP_STRIDE + srow);
-    // online softmax of tile kt_; P (bf16) and the per-head rescale to LDS
-#define KP_SM_FINISH(kt_)                                                                         \
-    {                                                                                             \
-        if (((kt_) + 1) * MLA_TK > n_valid) {   /* ragged last tile: mask the rows past the end */ \
-            _Pragma("unroll") for (int e = 0; e < 4; ++e)                                         \
-                if ((kt_) * MLA_TK + srow + e >= n_valid) sv[e] = -INFINITY;                      \
-        }                                                                                         \
-        /* the scale is positive: the max of the raw scores, scaled, is the tile max */           \
-        const float mt_ = max4_in_8(sv[0], sv[1], sv[2], sv[3]) * scale_log2;                     \
-        float alpha_ = 1.0f;                                                                      \
-        if (mt_ > m_ref + 8.0f) {                                                                 \
-            alpha_ = __builtin_amdgcn_exp2f(m_ref - mt_);                                         \
-            m_ref = mt_;                                                                          \
-            rebase_tile = (kt_) + 1;   /* any writer stores the same value */                     \
-        }                                                                                         \
-        float w_[4];                                                                              \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e)                                             \
-            w_[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, -m_ref));            \
-        bf16x4 pw_;                                                                               \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e) pw_[e] = (__bf16)w_[e];                     \
-        /* the sum of the rounded weights, from the packed bf16 words */                          \
-        const u32x2 pk_ = __builtin_bit_cast(u32x2, pw_);                                         \
-        const float ps_ = (bf16_lo(pk_[0]) + bf16_hi(pk_[0])) + (bf16_lo(pk_[1]) + bf16_hi(pk_[1])); \
-        const float pe_ = (w_[0] + w_[1]) + (w_[2] + w_[3]);                                      \
-        l_run = l_run * alpha_ + ps_;                                                             \
-        l_lse = l_lse * alpha_ + pe_;                                                             \
-        *reinterpret_cast<bf16x4*>(ptile + hown * P_STRIDE + 2 * srow) = pw_;                     \
-        if ((lane & 7) == 0) alpha_s[hown] = alpha_;                                              \
-    }
-    // O[:, cols] += P . V[:, cols] over the column tiles [d0_, d1_) of tile kt_
-#define KP_PV(buf_, d0_, d1_)                                                                     \
-    {                                                                                             \
-        const uint8_t* tbv_ = ring + (buf_) * TILE_B;                                             \
-        _Pragma("unroll") for (int dtl = (d0_); dtl < (d1_); ++dtl) {                             \
-            const bf16x4 v0_ = lds_read_tr16(tbv_ + vb0[dtl]);                                    \
-            const bf16x4 v1_ = lds_read_tr16(tbv_ + vb1[dtl]);                                    \
-            const bf16x8 vb_ = __builtin_shufflevector(v0_, v1_, 0, 1, 2, 3, 4, 5, 6, 7);         \
-            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
-                o[ht][dtl] = mfma_bf16_16x16x32(pa[ht], vb_, o[ht][dtl]);                         \
-        }                                                                                         \
-    }
-#define KP_READ_P()                                                                               \
-    _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                              \
-        pa[ht] = *reinterpret_cast<const bf16x8*>(ptile + (16 * ht + n) * P_STRIDE + 16 * g);
-    // One pipelined step, for a tile kt with a successor (kt + 1 < ntiles); the
-    // ring buffers of tiles kt, kt+1 and kt+2 are BV, BK and BS (compile-time,
-    // so LDS addresses are immediates):
-    //   phase 1: QK(kt+1) and PV(kt) on the first DTA column tiles (the partial
-    //            S of QK is stored after PV is issued, so PV hides the QK
-    //            latency);
-    //   phase 2: SM(kt+1), PV(kt) on the remaining column tiles, tile kt+2
-    //            from registers into the ring (its buffer last held tile kt-1,
-    //            which every wave finished before the previous barrier) and
-    //            the loads of tile kt+3; the MFMAs of PV run under the LDS
-    //            traffic and the softmax arithmetic.
-    // O is rescaled first when the softmax of tile kt moved a reference max.
-#define KP_STEP(BV, BK, BS)                                                                       \
-    {                                                                                             \
-        const int rb_ = rebase_tile;                                                              \
-        if (kt + 3 < ntiles) {                                                                    \
-            KP_ROWS_OF(kt + 3)                                                                    \
-        }                                                                                         \
-        KP_QK(BK)                                                                                 \
-        KP_READ_P()                                                                               \
-        if (__builtin_amdgcn_readfirstlane(rb_) == kt + 1) {                                      \
-            f32x4 al_[4];                                                                         \
-            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
-                al_[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);             \
-            _Pragma("unroll") for (int ht = 0; ht < 4; ++ht)                                      \
-                _Pragma("unroll") for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al_[ht];      \
-        }                                                                                         \
-        KP_PV(BV, 0, DTA)                                                                         \
-        KP_QK_STORE()                                                                             \
-        lds_barrier();                                                                            \
-        KP_SM_READ()                                                                              \
-        KP_PV(BV, DTA, DTW)                                                                       \
-        if (kt + 2 < ntiles) {                                                                    \
-            KP_STORE_TILE(BS)                                                                     \
-            if (kt + 3 < ntiles) {                                                                \
-                KP_LOAD_TILE()                                                                    \
-            }                                                                                     \
-        }                                                                                         \
-        KP_SM_FINISH(kt + 1)                                                                      \
-        lds_barrier();                                                                            \
-        ++kt;                                                                                     \
+    // K fragments of QK chunk c_ (k-step c_, sub-tiles 0, 1) and the V fragments
+    // of PV chunk c_ (column tiles 2c_, 2c_+1); each chunk is read KP_RING-1
+    // chunks ahead of its MFMAs
+#define KP_RING 4
+#define KP_K_CHUNK(c_)                                                                         \
+    _Pragma("unroll") for (int s_ = 0; s_ < 2; ++s_)                                           \
+        kf_[(c_) % KP_RING][s_] = *reinterpret_cast<const bf16x8*>(                            \
+            tb_ + kb[s_] + 256 * ((c_) >> 2) + ((64 * ((c_) & 3)) ^ kx[s_]));
+#define KP_V_CHUNK(c_)                                                                         \
+    _Pragma("unroll") for (int u_ = 0; u_ < 2; ++u_) {                                         \
+        const int ct_ = 2 * (c_) + u_;                                                         \
+        const bf16x4 v0_ = lds_read_tr16(tb_ + vb[0] + 256 * (ct_ >> 3) + ((32 * (ct_ & 7)) ^ vx[0])); \
+        const bf16x4 v1_ = lds_read_tr16(tb_ + vb[1] + 256 * (ct_ >> 3) + ((32 * (ct_ & 7)) ^ vx[1])); \
+        vf_[(c_) % KP_RING][u_] = __builtin_shufflevector(v0_, v1_, 0, 1, 2, 3, 4, 5, 6, 7);   \
     }
 
-    f32x4 sp[4];
-    f32x4 sv;
-    bf16x8 pa[4];
-
-    // ---- prologue: tiles 0 and 1 into the ring, tile 2 into registers; SM(0) -------
-    KP_ROWS_OF(0)
-    KP_LOAD_TILE()
-    KP_STORE_TILE(0)
-    if (ntiles > 1) {
-        KP_ROWS_OF(1)
-        KP_LOAD_TILE()
-        KP_STORE_TILE(1)
-        if (ntiles > 2) {
-            KP_ROWS_OF(2)
-            KP_LOAD_TILE()
+    // one tile: QK, softmax, PV; the next tile's gather is issued first (its
+    // buffer held tile kt-1, which every wave finished before the last barrier)
+// the start of a step: the gather of the next tile is issued (its buffer held
+// tile kt-1, which every wave finished before the last barrier), then QK of
+// tile kt and the tile max of each head over this wave's rows
+#define KP_QK_MAX()                                                                            \
+        __asm__ __volatile__("" : "+v"(kx[0]), "+v"(kx[1]), "+v"(vx[0]), "+v"(vx[1]));          \
+        const int buf_ = kt & 1;                                                               \
+        /* the gather of the next tile; the last tile gathers its own rows again into the */   \
+        /* free buffer (no branch per row; those rows were just read, from the L2) */          \
+        KP_ROWS_OF(kt + 1 < ntiles ? kt + 1 : kt)                                              \
+        const uint8_t* tb_ = ring + buf_ * TILE_B;                                             \
+        /* QK by k-steps; the K fragments of a step are read three steps ahead of its */       \
+        /* MFMAs (scheduling barriers keep the reads from all being hoisted, which would */    \
+        /* take more registers than a wave has left) */                                        \
+        f32x4 sacc_[2][2];                                                                     \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s)                                          \
+            _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) sacc_[s][ht] = f32x4{0.f, 0.f, 0.f, 0.f}; \
+        bf16x8 kf_[KP_RING][2];                                                                \
+        _Pragma("unroll") for (int c = 0; c < KP_RING - 1; ++c) KP_K_CHUNK(c)                  \
+        _Pragma("unroll") for (int c = 0; c < KS; ++c) {                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            /* the gather of the next tile, spread over the k-steps so that the address */     \
+            /* unit takes it in the background */                                              \
+            _Pragma("unroll") for (int j = c * RPW / KS; j < (c + 1) * RPW / KS; ++j)          \
+                KP_ISSUE_ROW(j, buf_ ^ 1)                                                      \
+            if (c + KP_RING - 1 < KS) KP_K_CHUNK(c + KP_RING - 1)                              \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
+                _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                               \
+                    sacc_[s][ht] = mfma_bf16_16x16x32(kf_[c % KP_RING][s], qf[ht][c], sacc_[s][ht]); \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if ((kt + 1) * MLA_TK > n_valid) {   /* ragged last tile: mask rows past the end */    \
+            const int rb0_ = kt * MLA_TK + 32 * rh + 8 * g;                                    \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e)                                  \
+                    if (rb0_ + 4 * s + e >= n_valid) {                                         \
+                        sacc_[s][0][e] = -INFINITY;                                            \
+                        sacc_[s][1][e] = -INFINITY;                                            \
+                    }                                                                          \
+        }                                                                                      \
+        /* the scale is positive: the max of the raw scores, scaled, is the max of the */     \
+        /* scaled scores */                                                                    \
+        float mt_[2];                                                                          \
+        _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \
+            const float mx_ = fmaxf(fmaxf(fmaxf(sacc_[0][ht][0], sacc_[0][ht][1]), fmaxf(sacc_[0][ht][2], sacc_[0][ht][3])), \
+                                    fmaxf(fmaxf(sacc_[1][ht][0], sacc_[1][ht][1]), fmaxf(sacc_[1][ht][2], sacc_[1][ht][3]))); \
+            mt_[ht] = max_over_groups(mx_) * scale_log2;                                       \
         }
+// the end of a step: this wave's rows of tile kt+1 have landed, then the barrier
+// that publishes them and frees the buffer of tile kt
+#define KP_STEP_END()                                                                          \
+        wait_vm0();                                                                            \
+        lds_barrier();                                                                         \
+        ++kt;
+
+    // one attention step on tile kt; with FIRST, the reference of a head is set by
+    // its first tile with a valid row and a tile too far above it raises the flag
+#define KP_STEP(FIRST)                                                                         \
+    {                                                                                          \
+        KP_QK_MAX()                                                                            \
+        if (FIRST) {                                                                           \
+            bool over_ = false;                                                                \
+            _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                 \
+                if (m_ref[ht] < -1e29f)   /* first tile with a valid row: O is still zero */   \
+                    m_ref[ht] = mt_[ht] > -1e29f ? mt_[ht] + MLA_REF_LIFT : -1e30f;            \
+                else if (mt_[ht] > m_ref[ht] + MLA_HEADROOM)                                   \
+                    over_ = true;                                                              \
+            }                                                                                  \
+            if (over_) rflag[kt & 1] = 1;                                                      \
+        }                                                                                      \
+        /* the first V chunks do not depend on the softmax: read them now */                  \
+        bf16x8 vf_[KP_RING][2];                                                                \
+        _Pragma("unroll") for (int c = 0; c < KP_RING - 1; ++c) KP_V_CHUNK(c)                  \
+        bf16x8 pb_[2];                                                                         \
+        _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \
+            float w_[8];                                                                       \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e)                                  \
+                    w_[4 * s + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc_[s][ht][e], scale_log2, -m_ref[ht])); \
+            _Pragma("unroll") for (int e = 0; e < 8; ++e) pb_[ht][e] = (__bf16)w_[e];         \
+            lsum[ht] = mfma_bf16_16x16x32(ones, pb_[ht], lsum[ht]);                            \
+            l_lse[ht] += ((w_[0] + w_[1]) + (w_[2] + w_[3])) + ((w_[4] + w_[5]) + (w_[6] + w_[7])); \
+        }                                                                                      \
+        /* PV by pairs of column tiles, V read three pairs ahead */                            \
+        _Pragma("unroll") for (int c = 0; c < CT / 2; ++c) {                                   \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (c + KP_RING - 1 < CT / 2) KP_V_CHUNK(c + KP_RING - 1)                          \
+            _Pragma("unroll") for (int u = 0; u < 2; ++u)                                      \
+                _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                               \
+                    mfma_acc(o[2 * c + u][ht], vf_[c % KP_RING][u], pb_[ht]);                  \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        KP_STEP_END()                                                                          \
     }
-    lds_barrier();
-    KP_QK(0)
-    KP_QK_STORE()
-    lds_barrier();
-    KP_SM_READ()
-    KP_SM_FINISH(0)
+    // one step of the exact-max sweep: QK only
+#define KP_MAX_STEP()                                                                          \
+    {                                                                                          \
+        KP_QK_MAX()                                                                            \
+        _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) m_ref[ht] = fmaxf(m_ref[ht], mt_[ht]); \
+        KP_STEP_END()                                                                          \
+    }
+#define KP_FIRST_TILE()                                                                        \
+    KP_ISSUE_TILE(0, 0)                                                                        \
+    wait_vm0();                                                                                \
     lds_barrier();
 
-    // the loop runs three steps per pass so that every ring buffer index is a
-    // compile-time constant
-    int kt = 0;
-    for (;;) {
-        if (kt + 1 >= ntiles) break;
-        KP_STEP(0, 1, 2)
-        if (kt + 1 >= ntiles) break;
-        KP_STEP(1, 2, 0)
-        if (kt + 1 >= ntiles) break;
-        KP_STEP(2, 0, 1)
-    }
-    // last tile: PV only
-    if (__builtin_amdgcn_readfirstlane(rebase_tile) == kt + 1) {
-        f32x4 al[4];
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) al[ht] = *reinterpret_cast<const f32x4*>(alpha_s + 16 * ht + 4 * g);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-            for (int dtl = 0; dtl < DTW; ++dtl) o[ht][dtl] *= al[ht];
-    }
-    KP_READ_P()
-    KP_PV(kt % MLA_NBUF, 0, DTW)
-#undef KP_STEP
-#undef KP_READ_P
-#undef KP_PV
-#undef KP_SM_FINISH
-#undef KP_SM_READ
-#undef KP_QK_STORE
-#undef KP_QK
-
-    // ---- normalise and write ----------------------------------------------------
-    {
-        const float lr = sum_in_8(l_run);
-        const float le = sum_in_8(l_lse);
-        if ((lane & 7) == 0) {
-            lsum[hown * 2] = lr;
-            lsum[hown * 2 + 1] = le;
-            mref_s[hown] = m_ref;
-        }
-    }
+    // (the Q loads above must be complete before the first direct-to-LDS load: the
+    // compiler cannot see those and would otherwise wait for all of them at Q's
+    // first use)
+    wait_vm0();
     compiler_fence();
-    __syncthreads();   // all waves done with the ring; sums visible
-    if (lse && tid < heads)
-        lse[(size_t)i * heads + tid] = (mref_s[tid] + log2f(lsum[tid * 2 + 1])) * 0.69314718055994530942f;
-    // stage O (bf16, [head][D], rows padded by 16 bytes against bank conflicts)
-    // in the ring, then copy the real heads out
-    uint16_t* stage = reinterpret_cast<uint16_t*>(ring);
+    KP_FIRST_TILE()
+    for (int kt = 0;;) {
+        // the flag of the previous step is final (set before the last barrier) and
+        // is not written again before the next one: every wave reads the same value
+        // and leaves the loop at the same step
+        const int over_prev = __builtin_amdgcn_readfirstlane(rflag[(kt & 1) ^ 1]);
+        KP_STEP(true)
+        if (over_prev || kt >= ntiles) break;
+    }
+    // read after the last barrier of the pass: the same value in every wave
+    if (__builtin_amdgcn_readfirstlane(rflag[0] | rflag[1])) {
+        // a score rose too far above its first-tile reference: drop the pass, sweep
+        // for the exact max of every head, and run the attention again with it
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-        f32x4 inv;
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) inv[e] = 1.0f / lsum[(16 * ht + 4 * g + e) * 2];
+            for (int ht = 0; ht < 2; ++ht) o[ct][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dtl = 0; dtl < DTW; ++dtl) {
-            const int col = 16 * (wave * DTW + dtl) + n;
-            if (col < D) {
+        for (int ht = 0; ht < 2; ++ht) {
+            m_ref[ht] = -1e30f;
+            lsum[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+            l_lse[ht] = 0.f;
+        }
+        KP_FIRST_TILE()
+        for (int kt = 0; kt < ntiles;) KP_MAX_STEP()
+        KP_FIRST_TILE()
+        for (int kt = 0; kt < ntiles;) KP_STEP(false)
+    }
+#undef KP_STEP
+#undef KP_MAX_STEP
+#undef KP_QK_MAX
+#undef KP_STEP_END
+#undef KP_FIRST_TILE
+#undef KP_K_CHUNK
+#undef KP_V_CHUNK
+#undef KP_RING
+#undef KP_ISSUE_TILE
+#undef KP_ISSUE_ROW
+#undef KP_ROWS_OF
+
+    // ---- merge the two row halves and write ---------------------------------------
+    // wave (rh, hh) finishes the column half rh of its heads: it hands its O of
+    // the other column half, and its softmax state, to the partner (1-rh, hh)
+    float lr[2], le[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    stage[(16 * ht + 4 * g + e) * (D + 8) + col] = f32_to_bf16_rne(o[ht][dtl][e] * inv[e]);
-            }
+    for (int ht = 0; ht < 2; ++ht) {
+        lr[ht] = lsum[ht][0];
+        le[ht] = sum_over_groups(l_lse[ht]);
+    }
+    // (the accumulator array is only ever indexed with compile-time constants, so
+    // the two row halves take separate code paths)
+#define KP_HAND_OVER(RH)                                                                       \
+    {                                                                                          \
+        uint8_t* xo_ = ring + (2 * hh + (1 - (RH))) * XB;                                      \
+        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
+            _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                                   \
+                *reinterpret_cast<f32x4*>(xo_ + ((2 * j + ht) * 64 + lane) * 16) = o[(CT / 2) * (1 - (RH)) + j][ht]; \
+    }
+    if (rh == 0) KP_HAND_OVER(0) else KP_HAND_OVER(1)
+#undef KP_HAND_OVER
+    if (g == 0) {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            float* m_ = mls[rh][32 * hh + 16 * ht + n];
+            m_[0] = m_ref[ht];
+            m_[1] = lr[ht];
+            m_[2] = le[ht];
         }
     }
     __syncthreads();
-    uint4* dst = reinterpret_cast<uint4*>(orow);
-    const int nvec = heads * D / 8;
-    for (int e = tid; e < nvec; e += NT) {
-        const int h = e / (D / 8), c = e % (D / 8);
-        dst[e] = *reinterpret_cast<const uint4*>(ring + h * (D * 2 + 16) + c * 16);
+    const uint8_t* xi = ring + (2 * hh + rh) * XB;
+    float fa[2], fb[2], finv[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        const int head = 32 * hh + 16 * ht + n;
+        const float* mp = mls[1 - rh][head];
+        const float M = fmaxf(m_ref[ht], mp[0]);
+        fa[ht] = __builtin_amdgcn_exp2f(m_ref[ht] - M);
+        fb[ht] = __builtin_amdgcn_exp2f(mp[0] - M);
+        finv[ht] = 1.0f / (lr[ht] * fa[ht] + mp[1] * fb[ht]);
+        if (lse && rh == 0 && g == 0 && head < heads)
+            lse[(size_t)i * heads + head] = (M + log2f(le[ht] * fa[ht] + mp[2] * fb[ht])) * 0.69314718055994530942f;
     }
-#undef KP_ROWS_OF
-#undef KP_LOAD_TILE
-#undef KP_STORE_TILE
+    // (the output row address is formed here from the scalar query index, so no
+    // 64-bit address stays live, or spilled, across the main loop: a reload of a
+    // spill would wait for every output store issued before it)
+    int i_late = i;
+    __asm__ __volatile__("" : "+s"(i_late));
+#define KP_FINISH(RH)                                                                          \
+    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
+        const int head_ = 32 * hh + 16 * ht + n;                                               \
+        const bool hv_ = head_ < heads;                                                        \
+        uint16_t* dst_ = out + ((size_t)i_late * heads + (hv_ ? head_ : 0)) * D;               \
+        f32x4 op_[CT / 2];                                                                     \
+        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
+            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((2 * j + ht) * 64 + lane) * 16);    \
+        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                                   \
+            const int ct_ = (CT / 2) * (RH) + j;                                               \
+            const int col_ = 16 * ct_ + 4 * g;                                                 \
+            if (hv_ && (DP == D || col_ < D)) {                                                \
+                bf16x4 r_;                                                                     \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e)                                  \
+                    r_[e] = (__bf16)((o[ct_][ht][e] * fa[ht] + op_[j][e] * fb[ht]) * finv[ht]); \
+                *reinterpret_cast<bf16x4*>(dst_ + col_) = r_;                                  \
+            }                                                                                  \
+        }                                                                                      \
+    }
+    if (rh == 0) {
+        KP_FINISH(0)
+    } else {
+        KP_FINISH(1)
+    }
+#undef KP_FINISH
 }
 
 template <int D>
