@@ -172,27 +172,6 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int hh = wave & 1;    // head half
     const int i = xcd_query(blockIdx.x, gridDim.x);
 
-    // ---- Q first: its loads overlap the index row's ---------------------------------
-    // B operand of S^T = K . Q^T for this wave's 32 heads
-    // qf[ht][ks]: head 32*hh + 16*ht + n, columns 32*ks + 8*g .. +7
-    // (every lane loads from a valid address, and heads past `heads` and the
-    // columns of a zero-padded narrow latent are zeroed after the load: no branch
-    // holds back the stream of loads)
-    bf16x8 qf[2][KS];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-        const int head = 32 * hh + 16 * ht + n;
-        const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int col = 32 * ks + 8 * g;
-            const bool ok = head < heads && (DP == D || col < D);
-            uint4 v = *reinterpret_cast<const uint4*>(qrow + (DP == D ? col : min(col, D - 8)));
-            if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
-            qf[ht][ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-
     // ---- compact the index row (valid entries, original order) ----------------
     // Entry NT*k + tid is read in round k; the loads of all rounds are issued
     // together (one memory latency), each wave counts its valid entries of a
@@ -207,6 +186,28 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         ent[k] = -1;
         if (NT * k < row_width && j < row_width) ent[k] = irow[j];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- Q: B operand of S^T = K . Q^T for this wave's 32 heads. Its loads are
+    // issued after the index row's, so the compaction waits for the index row only
+    // (the memory counter retires loads in order) and Q lands under the compaction
+    // and the first tile's gather.
+    // qf[ht][ks]: head 32*hh + 16*ht + n, columns 32*ks + 8*g .. +7
+    // (every lane loads from a valid address; heads past `heads` and the columns
+    // of a zero-padded narrow latent are zeroed once the loads have landed)
+    bf16x8 qf[2][KS];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        const int head = 32 * hh + 16 * ht + n;
+        const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int col = 32 * ks + 8 * g;
+            qf[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                        qrow + (DP == D ? col : min(col, D - 8))));
+        }
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
     if (tid < 2) rflag[tid] = 0;
     if (DP != D) {   // zero the padding columns of the ring once; the gather never writes them
         for (int e = tid; e < MLA_NBUF * TILE_B / 16; e += NT)
@@ -261,6 +262,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // row r (lanes whose chunk lies in the zero padding of a narrow latent idle)
     const uint32_t ring_lds = lds_addr(ring);
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
+    const uint32_t wave_lds = ring_lds + (uint32_t)(RPW * wave_s * RB);   // LDS row 16w of buffer 0
     const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row, before the chunk xor
     // KP_ROWS_OF reads the byte offsets of this wave's 16 rows of tile kt_ into rws_[16];
     // KP_ISSUE_ROW(j_) issues the gather of the wave's row j_ into buffer buf_
@@ -275,11 +277,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     }
 #define KP_ISSUE_ROW(j_, buf_)                                                                 \
     {                                                                                          \
-        const int r_ = RPW * wave_s + (j_);   /* r_ % 16 = j_ */                               \
-        const uint32_t off_ = lane16 ^ (uint32_t)(row_swz(j_) << 4);   /* chunk lane ^ swz */  \
-        if (DP == D || (lane < DP / 8 && (off_ >> 4) < (uint32_t)CH))                          \
-            lds_dma16(reinterpret_cast<const uint8_t*>(kv) + (uint32_t)rws_[j_], off_,         \
-                      __builtin_amdgcn_readfirstlane(ring_lds + (uint32_t)((buf_) * TILE_B + r_ * RB))); \
+        /* lane chunk lane ^ swz(r) of the row (r % 16 = j_) */                                \
+        const uint32_t loff_ = lane16 ^ (uint32_t)(row_swz(j_) << 4);                          \
+        if (DP == D || (lane < DP / 8 && (loff_ >> 4) < (uint32_t)CH))                         \
+            lds_dma16(reinterpret_cast<const uint8_t*>(kv) + (uint32_t)rws_[j_], loff_,        \
+                      __builtin_amdgcn_readfirstlane(wave_lds + (uint32_t)((buf_) * TILE_B + (j_) * RB))); \
     }
 #define KP_ISSUE_TILE(kt_, buf_)                                                               \
     {                                                                                          \
@@ -343,19 +345,22 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // loop into registers a wave does not have)
 
     // K fragments of QK chunk c_ (k-step c_, sub-tiles 0, 1) and the V fragments
-    // of PV chunk c_ (column tiles 2c_, 2c_+1); each chunk is read KP_RING-1
-    // chunks ahead of its MFMAs
-#define KP_RING 4
-#define KP_K_CHUNK(c_)                                                                         \
-    _Pragma("unroll") for (int s_ = 0; s_ < 2; ++s_)                                           \
-        kf_[(c_) % KP_RING][s_] = *reinterpret_cast<const bf16x8*>(                            \
-            tb_ + kb[s_] + 256 * ((c_) >> 2) + ((64 * ((c_) & 3)) ^ kx[s_]));
+    // of PV chunk c_ (column tiles 2c_, 2c_+1); a K chunk is read KP_RING_K-1
+    // chunks ahead of its MFMAs, a V chunk KP_RING_V-1
+#define KP_RING_K 4
+#define KP_RING_V 4
+#define KP_K_FRAG(c_, s_)                                                                      \
+    kf_[(c_) % KP_RING_K][s_] = *reinterpret_cast<const bf16x8*>(                                \
+        tb_ + kb[s_] + 256 * ((c_) >> 2) + ((64 * ((c_) & 3)) ^ kx[s_]));
+#define KP_K_CHUNK(c_) { KP_K_FRAG(c_, 0) KP_K_FRAG(c_, 1) }
+#define KP_V_HALF(c_, u_, b_)                                                                  \
+    lds_read_tr16(tb_ + vb[b_] + 256 * ((2 * (c_) + (u_)) >> 3) + ((32 * ((2 * (c_) + (u_)) & 7)) ^ vx[b_]))
 #define KP_V_CHUNK(c_)                                                                         \
     _Pragma("unroll") for (int u_ = 0; u_ < 2; ++u_) {                                         \
         const int ct_ = 2 * (c_) + u_;                                                         \
         const bf16x4 v0_ = lds_read_tr16(tb_ + vb[0] + 256 * (ct_ >> 3) + ((32 * (ct_ & 7)) ^ vx[0])); \
         const bf16x4 v1_ = lds_read_tr16(tb_ + vb[1] + 256 * (ct_ >> 3) + ((32 * (ct_ & 7)) ^ vx[1])); \
-        vf_[(c_) % KP_RING][u_] = __builtin_shufflevector(v0_, v1_, 0, 1, 2, 3, 4, 5, 6, 7);   \
+        vf_[(c_) % KP_RING_V][u_] = __builtin_shufflevector(v0_, v1_, 0, 1, 2, 3, 4, 5, 6, 7); \
     }
 
     // one tile: QK, softmax, PV; the next tile's gather is issued first (its
@@ -376,18 +381,29 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         f32x4 sacc_[2][2];                                                                     \
         _Pragma("unroll") for (int s = 0; s < 2; ++s)                                          \
             _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) sacc_[s][ht] = f32x4{0.f, 0.f, 0.f, 0.f}; \
-        bf16x8 kf_[KP_RING][2];                                                                \
-        _Pragma("unroll") for (int c = 0; c < KP_RING - 1; ++c) KP_K_CHUNK(c)                  \
+        bf16x8 kf_[KP_RING_K][2];                                                              \
+        _Pragma("unroll") for (int c = 0; c < KP_RING_K - 1; ++c) KP_K_CHUNK(c)                \
+        /* each k-step interleaves its four MFMAs with the reads of a later k-step and */      \
+        /* the gather of one row of the next tile (spread over the k-steps so that the */      \
+        /* address unit takes it in the background), so that those issue while the */         \
+        /* matrix core works */                                                                \
         _Pragma("unroll") for (int c = 0; c < KS; ++c) {                                       \
+            const bool ld_ = c + KP_RING_K - 1 < KS;                                           \
             __builtin_amdgcn_sched_barrier(0);                                                 \
-            /* the gather of the next tile, spread over the k-steps so that the address */     \
-            /* unit takes it in the background */                                              \
+            sacc_[0][0] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][0], qf[0][c], sacc_[0][0]);    \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (ld_) KP_K_FRAG(c + KP_RING_K - 1, 0)                                           \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            sacc_[0][1] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][0], qf[1][c], sacc_[0][1]);    \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (ld_) KP_K_FRAG(c + KP_RING_K - 1, 1)                                           \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            sacc_[1][0] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][1], qf[0][c], sacc_[1][0]);    \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
             _Pragma("unroll") for (int j = c * RPW / KS; j < (c + 1) * RPW / KS; ++j)          \
                 KP_ISSUE_ROW(j, buf_ ^ 1)                                                      \
-            if (c + KP_RING - 1 < KS) KP_K_CHUNK(c + KP_RING - 1)                              \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
-                _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                               \
-                    sacc_[s][ht] = mfma_bf16_16x16x32(kf_[c % KP_RING][s], qf[ht][c], sacc_[s][ht]); \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            sacc_[1][1] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][1], qf[1][c], sacc_[1][1]);    \
         }                                                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                     \
         if ((kt + 1) * MLA_TK > n_valid) {   /* ragged last tile: mask rows past the end */    \
@@ -430,8 +446,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             if (over_) rflag[kt & 1] = 1;                                                      \
         }                                                                                      \
         /* the first V chunks do not depend on the softmax: read them now */                  \
-        bf16x8 vf_[KP_RING][2];                                                                \
-        _Pragma("unroll") for (int c = 0; c < KP_RING - 1; ++c) KP_V_CHUNK(c)                  \
+        bf16x8 vf_[KP_RING_V][2];                                                              \
+        _Pragma("unroll") for (int c = 0; c < KP_RING_V - 1; ++c) KP_V_CHUNK(c)                \
         bf16x8 pb_[2];                                                                         \
         _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \
             float w_[8];                                                                       \
@@ -443,12 +459,24 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             l_lse[ht] += ((w_[0] + w_[1]) + (w_[2] + w_[3])) + ((w_[4] + w_[5]) + (w_[6] + w_[7])); \
         }                                                                                      \
         /* PV by pairs of column tiles, V read three pairs ahead */                            \
+        /* (each pair interleaves its four MFMAs with the four reads of a later pair) */       \
         _Pragma("unroll") for (int c = 0; c < CT / 2; ++c) {                                   \
-            __builtin_amdgcn_sched_barrier(0);                                                 \
-            if (c + KP_RING - 1 < CT / 2) KP_V_CHUNK(c + KP_RING - 1)                          \
-            _Pragma("unroll") for (int u = 0; u < 2; ++u)                                      \
-                _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                               \
-                    mfma_acc(o[2 * c + u][ht], vf_[c % KP_RING][u], pb_[ht]);                  \
+            const bool ld_ = c + KP_RING_V - 1 < CT / 2;                                       \
+            bf16x4 vh_[2][2];                                                                  \
+            _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                    \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                mfma_acc(o[2 * c + u][0], vf_[c % KP_RING_V][u], pb_[0]);                      \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                if (ld_) vh_[u][0] = KP_V_HALF(c + KP_RING_V - 1, u, 0);                      \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                mfma_acc(o[2 * c + u][1], vf_[c % KP_RING_V][u], pb_[1]);                      \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                if (ld_) {                                                                     \
+                    vh_[u][1] = KP_V_HALF(c + KP_RING_V - 1, u, 1);                            \
+                    vf_[(c + KP_RING_V - 1) % KP_RING_V][u] =                                  \
+                        __builtin_shufflevector(vh_[u][0], vh_[u][1], 0, 1, 2, 3, 4, 5, 6, 7);  \
+                }                                                                              \
+            }                                                                                  \
         }                                                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                     \
         KP_STEP_END()                                                                          \
@@ -465,12 +493,19 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     wait_vm0();                                                                                \
     lds_barrier();
 
-    // (the Q loads above must be complete before the first direct-to-LDS load: the
-    // compiler cannot see those and would otherwise wait for all of them at Q's
-    // first use)
-    wait_vm0();
+    // (the explicit wait after the first tile's gather also covers the Q loads, so
+    // the compiler adds no wait of its own at Q's first use inside the loop, where
+    // the gathers of later tiles are in flight)
     compiler_fence();
     KP_FIRST_TILE()
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        const int head = 32 * hh + 16 * ht + n;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (!(head < heads && (DP == D || 32 * ks + 8 * g < D))) qf[ht][ks] = bf16x8{};
+    }
     for (int kt = 0;;) {
         // the flag of the previous step is final (set before the last barrier) and
         // is not written again before the next one: every wave reads the same value
@@ -504,8 +539,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #undef KP_STEP_END
 #undef KP_FIRST_TILE
 #undef KP_K_CHUNK
+#undef KP_K_FRAG
+#undef KP_V_HALF
 #undef KP_V_CHUNK
-#undef KP_RING
+#undef KP_RING_K
+#undef KP_RING_V
 #undef KP_ISSUE_TILE
 #undef KP_ISSUE_ROW
 #undef KP_ROWS_OF
