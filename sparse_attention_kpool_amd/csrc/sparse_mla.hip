@@ -48,6 +48,7 @@ constexpr int MLA_MAX_ROW = 4096;  // index-row entries the LDS list holds
 // first tile are at least 2^-32, far from underflow.
 #define MLA_REF_LIFT 32.0f
 #define MLA_HEADROOM 64.0f
+#define MLA_WEIGHT_MAX 0x1p64f   // 2^MLA_HEADROOM
 
 // Chunk permutation of LDS row r: 16-byte chunk c is stored at c ^ row_swz(r)
 // (within aligned groups of 16 chunks, one pass over the 64 banks).
@@ -367,8 +368,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // buffer held tile kt-1, which every wave finished before the last barrier)
 // the start of a step: the gather of the next tile is issued (its buffer held
 // tile kt-1, which every wave finished before the last barrier), then QK of
-// tile kt and the tile max of each head over this wave's rows
-#define KP_QK_MAX()                                                                            \
+// tile kt (rows past the end of the list masked)
+#define KP_QK()                                                                                \
         __asm__ __volatile__("" : "+v"(kx[0]), "+v"(kx[1]), "+v"(vx[0]), "+v"(vx[1]));          \
         const int buf_ = kt & 1;                                                               \
         /* the gather of the next tile; the last tile gathers its own rows again into the */   \
@@ -415,8 +416,10 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
                         sacc_[s][1][e] = -INFINITY;                                            \
                     }                                                                          \
         }                                                                                      \
-        /* the scale is positive: the max of the raw scores, scaled, is the max of the */     \
-        /* scaled scores */                                                                    \
+
+// the max of each head over this wave's rows of the tile, scaled (the scale is
+// positive: the max of the raw scores, scaled, is the max of the scaled scores)
+#define KP_TILE_MAX()                                                                          \
         float mt_[2];                                                                          \
         _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \
             const float mx_ = fmaxf(fmaxf(fmaxf(sacc_[0][ht][0], sacc_[0][ht][1]), fmaxf(sacc_[0][ht][2], sacc_[0][ht][3])), \
@@ -431,24 +434,25 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         ++kt;
 
     // one attention step on tile kt; with FIRST, the reference of a head is set by
-    // its first tile with a valid row and a tile too far above it raises the flag
+    // its first tile with a valid row and a weight above 2^MLA_HEADROOM raises the
+    // flag. Once set, the reference does not depend on the tile, so the weights
+    // are computed straight from the scores: no cross-lane max on the way to PV.
 #define KP_STEP(FIRST)                                                                         \
     {                                                                                          \
-        KP_QK_MAX()                                                                            \
+        KP_QK()                                                                                \
         if (FIRST) {                                                                           \
-            bool over_ = false;                                                                \
-            _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                 \
-                if (m_ref[ht] < -1e29f)   /* first tile with a valid row: O is still zero */   \
-                    m_ref[ht] = mt_[ht] > -1e29f ? mt_[ht] + MLA_REF_LIFT : -1e30f;            \
-                else if (mt_[ht] > m_ref[ht] + MLA_HEADROOM)                                   \
-                    over_ = true;                                                              \
+            /* a head without a reference takes it from this tile (its O is still zero) */     \
+            if (__ballot(m_ref[0] < -1e29f || m_ref[1] < -1e29f)) {                            \
+                KP_TILE_MAX()                                                                  \
+                _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                               \
+                    if (m_ref[ht] < -1e29f) m_ref[ht] = mt_[ht] > -1e29f ? mt_[ht] + MLA_REF_LIFT : -1e30f; \
             }                                                                                  \
-            if (over_) rflag[kt & 1] = 1;                                                      \
         }                                                                                      \
         /* the first V chunks do not depend on the softmax: read them now */                  \
         bf16x8 vf_[KP_RING_V][2];                                                              \
         _Pragma("unroll") for (int c = 0; c < KP_RING_V - 1; ++c) KP_V_CHUNK(c)                \
         bf16x8 pb_[2];                                                                         \
+        float wmax_ = 0.f;                                                                     \
         _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \
             float w_[8];                                                                       \
             _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
@@ -456,8 +460,14 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
                     w_[4 * s + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc_[s][ht][e], scale_log2, -m_ref[ht])); \
             _Pragma("unroll") for (int e = 0; e < 8; ++e) pb_[ht][e] = (__bf16)w_[e];         \
             lsum[ht] = mfma_bf16_16x16x32(ones, pb_[ht], lsum[ht]);                            \
-            l_lse[ht] += ((w_[0] + w_[1]) + (w_[2] + w_[3])) + ((w_[4] + w_[5]) + (w_[6] + w_[7])); \
+            const float ws_ = ((w_[0] + w_[1]) + (w_[2] + w_[3])) + ((w_[4] + w_[5]) + (w_[6] + w_[7])); \
+            l_lse[ht] += ws_;                                                                  \
+            wmax_ = fmaxf(wmax_, ws_);                                                         \
         }                                                                                      \
+        /* a weight above 2^MLA_HEADROOM (or infinite) means a score too far above the */     \
+        /* reference: flag the workgroup. The lane's sums bound its weights from above */      \
+        /* (a sum over the bound with no single weight over it only costs an exact pass) */   \
+        if (FIRST && __ballot(wmax_ > MLA_WEIGHT_MAX)) rflag[kt & 1] = 1;                      \
         /* PV by pairs of column tiles, V read three pairs ahead */                            \
         /* (each pair interleaves its four MFMAs with the four reads of a later pair) */       \
         _Pragma("unroll") for (int c = 0; c < CT / 2; ++c) {                                   \
@@ -484,7 +494,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // one step of the exact-max sweep: QK only
 #define KP_MAX_STEP()                                                                          \
     {                                                                                          \
-        KP_QK_MAX()                                                                            \
+        KP_QK()                                                                                \
+        KP_TILE_MAX()                                                                          \
         _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) m_ref[ht] = fmaxf(m_ref[ht], mt_[ht]); \
         KP_STEP_END()                                                                          \
     }
@@ -535,7 +546,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     }
 #undef KP_STEP
 #undef KP_MAX_STEP
-#undef KP_QK_MAX
+#undef KP_QK
+#undef KP_TILE_MAX
 #undef KP_STEP_END
 #undef KP_FIRST_TILE
 #undef KP_K_CHUNK
