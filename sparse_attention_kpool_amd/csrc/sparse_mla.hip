@@ -591,7 +591,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     }
     __syncthreads();
     const uint8_t* xi = ring + (2 * hh + rh) * XB;
-    float fa[2], fb[2], finv[2];
+    float fa[2], fb[2];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
         const int head = 32 * hh + 16 * ht + n;
@@ -599,9 +599,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         const float M = fmaxf(m_ref[ht], mp[0]);
         fa[ht] = __builtin_amdgcn_exp2f(m_ref[ht] - M);
         fb[ht] = __builtin_amdgcn_exp2f(mp[0] - M);
-        finv[ht] = 1.0f / (lr[ht] * fa[ht] + mp[1] * fb[ht]);
         if (lse && rh == 0 && g == 0 && head < heads)
             lse[(size_t)i * heads + head] = (M + log2f(le[ht] * fa[ht] + mp[2] * fb[ht])) * 0.69314718055994530942f;
+        const float inv = 1.0f / (lr[ht] * fa[ht] + mp[1] * fb[ht]);
+        fa[ht] *= inv;   // the merge weights with the normaliser folded in
+        fb[ht] *= inv;
     }
     // (the output row address is formed here from the scalar query index, so no
     // 64-bit address stays live, or spilled, across the main loop: a reload of a
@@ -611,19 +613,20 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #define KP_FINISH(RH)                                                                          \
     _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
         const int head_ = 32 * hh + 16 * ht + n;                                               \
-        const bool hv_ = head_ < heads;                                                        \
-        uint16_t* dst_ = out + ((size_t)i_late * heads + (hv_ ? head_ : 0)) * D;               \
+        uint16_t* dst_ = out + ((size_t)i_late * heads + head_) * D;                           \
         f32x4 op_[CT / 2];                                                                     \
         _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
             op_[j] = *reinterpret_cast<const f32x4*>(xi + ((2 * j + ht) * 64 + lane) * 16);    \
-        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                                   \
-            const int ct_ = (CT / 2) * (RH) + j;                                               \
-            const int col_ = 16 * ct_ + 4 * g;                                                 \
-            if (hv_ && (DP == D || col_ < D)) {                                                \
-                bf16x4 r_;                                                                     \
-                _Pragma("unroll") for (int e = 0; e < 4; ++e)                                  \
-                    r_[e] = (__bf16)((o[ct_][ht][e] * fa[ht] + op_[j][e] * fb[ht]) * finv[ht]); \
-                *reinterpret_cast<bf16x4*>(dst_ + col_) = r_;                                  \
+        if (head_ < heads) {                                                                   \
+            _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                               \
+                const int ct_ = (CT / 2) * (RH) + j;                                           \
+                const int col_ = 16 * ct_ + 4 * g;                                             \
+                if (DP == D || col_ < D) {                                                     \
+                    bf16x4 r_;                                                                 \
+                    _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
+                        r_[e] = (__bf16)(__builtin_fmaf(o[ct_][ht][e], fa[ht], op_[j][e] * fb[ht])); \
+                    *reinterpret_cast<bf16x4*>(dst_ + col_) = r_;                              \
+                }                                                                              \
             }                                                                                  \
         }                                                                                      \
     }
