@@ -440,6 +440,12 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #define KP_STEP(FIRST)                                                                         \
     {                                                                                          \
         KP_QK()                                                                                \
+        /* the first V chunks do not depend on the softmax: their reads are issued now, */    \
+        /* ahead of it (the scheduling barrier keeps the compiler from sinking them below */  \
+        /* the exponentials, which would expose their latency at the first PV MFMA) */         \
+        bf16x8 vf_[KP_RING_V][2];                                                              \
+        _Pragma("unroll") for (int c = 0; c < KP_RING_V - 1; ++c) KP_V_CHUNK(c)                \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
         if (FIRST) {                                                                           \
             /* a head without a reference takes it from this tile (its O is still zero) */     \
             if (__ballot(m_ref[0] < -1e29f || m_ref[1] < -1e29f)) {                            \
@@ -448,9 +454,6 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
                     if (m_ref[ht] < -1e29f) m_ref[ht] = mt_[ht] > -1e29f ? mt_[ht] + MLA_REF_LIFT : -1e30f; \
             }                                                                                  \
         }                                                                                      \
-        /* the first V chunks do not depend on the softmax: read them now */                  \
-        bf16x8 vf_[KP_RING_V][2];                                                              \
-        _Pragma("unroll") for (int c = 0; c < KP_RING_V - 1; ++c) KP_V_CHUNK(c)                \
         bf16x8 pb_[2];                                                                         \
         float wmax_ = 0.f;                                                                     \
         _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \

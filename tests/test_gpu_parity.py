@@ -285,6 +285,52 @@ def test_mla_edge_rows(K, oracle_mod, case):
     check_lse(host(g_lse), ref_lse, case)
 
 
+@pytest.mark.parametrize("case", ["d512", "d512_h24", "d64"])
+def test_mla_many_queries(K, oracle_mod, case):
+    """More queries than the GPU has compute units, so that every workgroup
+    takes several queries in turn, with row kinds interleaved so that
+    neighbouring queries of a workgroup differ: empty rows, full rows, ragged
+    short rows, scattered masks, single entries, and rows that force the
+    exact-max passes (from the second tile on, or in the last tile only)."""
+    rng = np.random.default_rng(11)
+    H, D, N, W, Tq = 64, 512, 3000, 192, 777
+    if case == "d512_h24":
+        H = 24
+    if case == "d64":
+        D = 64
+    q = (rng.standard_normal((Tq, H, D))).astype(np.float32)
+    kv = (rng.standard_normal((N, D))).astype(np.float32)
+    kv[N // 2:] *= 100.0   # rows whose scores lie far above those of the others
+    from workloads import f32_to_bf16_bits
+    q, kv = f32_to_bf16_bits(q), f32_to_bf16_bits(kv)
+    small = lambda n: rng.integers(0, N // 2, size=n)
+    idx = np.empty((Tq, W), np.int32)
+    for r in range(Tq):
+        kind = r % 7
+        row = small(W)
+        if kind == 0:
+            row[:] = -1
+        elif kind == 2:   # rising: large rows after the first tile
+            row[64:] = rng.integers(N // 2, N, size=W - 64)
+        elif kind == 3:
+            m = rng.random(W) < 0.4
+            row[m] = rng.choice([-1, N, 2 ** 31 - 1], size=m.sum())
+        elif kind == 4:
+            j = rng.integers(0, W)
+            row[:] = -1
+            row[j] = rng.integers(0, N)
+        elif kind == 5:   # rising in the last tile only
+            row[W - 5:] = rng.integers(N // 2, N, size=5)
+        elif kind == 6:
+            row[70:] = -1
+        idx[r] = row
+    _log("mla many", case, Tq, H, D)
+    g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), 1 / np.sqrt(D))
+    ref_out, ref_lse, ref_abs = oracle_mod.sparse_mla(q, kv, idx, 1 / np.sqrt(D), with_abs=True)
+    check_out(host_bf16_f32(g_out), ref_out, case, ref_abs=ref_abs)
+    check_lse(host(g_lse), ref_lse, case)
+
+
 # ------------------------------------------------------------ end to end -----
 @pytest.mark.parametrize("name", ["tiny_dense", "2k"])
 def test_end_to_end_dense_cover(K, oracle_mod, name):
