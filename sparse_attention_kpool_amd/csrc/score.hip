@@ -12,15 +12,16 @@
 // once, and walks the pools its queries see in chunks of 512 (all of them, or
 // every n-th when there are too few query tiles to fill the GPU); for each chunk,
 // each of its 8 waves holds the E4M3 codes of 64 pools (4 tiles of 16) in
-// registers as the B operand (few enough registers for four waves per SIMD,
-// so one wave's ReLU/weighting overlaps another's MFMAs). The query tile sits in LDS head-major; for each
-// indexer head h, one v_mfma_f32_16x16x128_f8f6f4 per pool tile computes the
-// full 128-wide dots of 16 queries x 16 pools, and each lane folds its 4
-// (query, pool) results into running sums with w*sq of that query and head
-// after the ReLU. The head sum thus stays inside the lane: no cross-lane
-// reduction. Chunks and tiles outside every query's visible range are
-// skipped; query tiles are dispatched last-first so the longest causal rows
-// start early.
+// registers as the B operand (the kernel is held to 128 registers, four waves
+// per SIMD, so one wave's ReLU/weighting overlaps another's MFMAs). The query
+// tile sits in LDS head-major; for each indexer head h, one
+// v_mfma_f32_16x16x128_f8f6f4 per pool tile computes the full 128-wide dots of
+// 16 queries x 16 pools, and each lane folds its 4 (query, pool) results into
+// running sums with w*sq of that query and head after the ReLU; the MFMAs of
+// the next head are issued before that fold. The head sum thus stays inside
+// the lane: no cross-lane reduction. Chunks and waves outside every query's
+// visible range are skipped; query tiles are dispatched last-first so the
+// longest causal rows start early.
 #include "kp_device.h"
 #include "kp_launch.h"
 
@@ -55,43 +56,58 @@ hipError_t launch_fill_f32(float* dst, size_t n, float value, hipStream_t stream
 // values pass unchanged. One instruction, and no quieting of the MFMA result.
 __device__ __forceinline__ float relu_f32(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-template <bool FULL>
+// All heads of one 64-pool block of a wave: acc[j][e] += w*sq(query 4g+e, h) *
+// ReLU(<q8[query, h], k8[pool 16j+n]>) summed over h. The heads run as a
+// two-stage pipeline over two register slots: the MFMAs of head h+1 are issued
+// before the results of head h are folded in (so the matrix core works while
+// the VALU does the ReLU and weighting, and no fold waits on a fresh MFMA), and
+// the A operands of head h+2 are read from LDS meanwhile. The loop body covers
+// two heads, so every slot index is a constant (no register copies).
 __device__ __forceinline__ void score_heads(const uint8_t* __restrict__ q_lds, const float* __restrict__ wq_lds,
-                                            int h_idx, const i32x8 (&b)[SC_NJ], int jlo, int jhi,
-                                            f32x4 (&acc)[SC_NJ]) {
+                                            int h_idx, const i32x8 (&b)[SC_NJ], f32x4 (&acc)[SC_NJ]) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const int sw = (n >> 1) & 7;
     const uint8_t* rowp = q_lds + n * 128;
     const int off0 = ((2 * g) ^ sw) << 4, off1 = ((2 * g + 1) ^ sw) << 4;
-    // operands of head h are read one head ahead
-    uint4 a0 = *reinterpret_cast<const uint4*>(rowp + off0);
-    uint4 a1 = *reinterpret_cast<const uint4*>(rowp + off1);
-    f32x4 wv = *reinterpret_cast<const f32x4*>(wq_lds + 4 * g);
-#pragma unroll 2
-    for (int h = 0; h < h_idx; ++h) {
-        const i32x8 a = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                              (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        const f32x4 wh = wv;
+    i32x8 a[2];
+    f32x4 wv[2];
+    f32x4 c[2][SC_NJ];
+    auto load = [&](int slot, int h) __attribute__((always_inline)) {
+        const uint8_t* r = rowp + h * (16 * 128);
+        const uint4 lo = *reinterpret_cast<const uint4*>(r + off0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(r + off1);
+        a[slot] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        wv[slot] = *reinterpret_cast<const f32x4*>(wq_lds + h * 16 + 4 * g);
+    };
+    auto issue = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < SC_NJ; ++j) c[slot][j] = mfma_fp8_16x16x128(a[slot], b[j], f32x4{0.f, 0.f, 0.f, 0.f});
+    };
+    auto fold = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < SC_NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(wv[slot][e], relu_f32(c[slot][j][e]), acc[j][e]);
+    };
+    load(0, 0);
+    issue(0);
+    if (h_idx > 1) load(1, 1);
+#pragma unroll 1
+    for (int h = 0; h < h_idx; h += 2) {
+        // head h: MFMAs in flight in slot 0; head h+1: operands in slot 1
+        if (h + 1 < h_idx) issue(1);
+        fold(0);
+        if (h + 2 < h_idx) load(0, h + 2);
         if (h + 1 < h_idx) {
-            const uint8_t* r = rowp + (h + 1) * (16 * 128);
-            a0 = *reinterpret_cast<const uint4*>(r + off0);
-            a1 = *reinterpret_cast<const uint4*>(r + off1);
-            wv = *reinterpret_cast<const f32x4*>(wq_lds + (h + 1) * 16 + 4 * g);
+            if (h + 2 < h_idx) issue(0);
+            fold(1);
+            if (h + 3 < h_idx) load(1, h + 3);
         }
-        f32x4 c[SC_NJ];
-#pragma unroll
-        for (int j = 0; j < SC_NJ; ++j)
-            if (FULL || (j >= jlo && j < jhi)) c[j] = mfma_fp8_16x16x128(a, b[j], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int j = 0; j < SC_NJ; ++j)
-            if (FULL || (j >= jlo && j < jhi)) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(wh[e], relu_f32(c[j][e]), acc[j][e]);
-            }
     }
 }
 
-__global__ __launch_bounds__(SC_THREADS) void score_kernel(
+// (at least four waves per SIMD: 128 registers)
+__global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, int num_q, const uint8_t* __restrict__ q8,
     const float* __restrict__ sq, const float* __restrict__ w, int h_idx, int d_idx,
@@ -180,16 +196,10 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
     for (int P0 = P_first; P0 < phi; P0 += SC_PC * nsplit) {
         const int Pw = P0 + wave * SC_PW;
-        // pool tiles [jlo, jhi) of this wave that some query of the tile sees
-        int jlo = SC_NJ, jhi = 0;
-        for (int q = 0; q < SC_QT; ++q) {
-            const int lo = max(lo_s[q], Pw), hi = min(hi_s[q], Pw + SC_PW);
-            if (lo < hi) {
-                jlo = min(jlo, (lo - Pw) >> 4);
-                jhi = max(jhi, (hi - Pw + 15) >> 4);
-            }
-        }
-        if (jlo >= jhi) continue;
+        // skip the block if no query of the tile sees any of its pools
+        bool seen = false;
+        for (int q = 0; q < SC_QT; ++q) seen |= max(lo_s[q], Pw) < min(hi_s[q], Pw + SC_PW);
+        if (!seen) continue;
 
         // this wave's pools: B operands (32 code bytes of column n per lane) and key scales
         i32x8 b[SC_NJ];
@@ -210,13 +220,12 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
             skj[j] = s;
         }
 
+        // (a block with only some tiles visible computes all four: the others'
+        // results are dropped at the store)
         f32x4 acc[SC_NJ];
 #pragma unroll
         for (int j = 0; j < SC_NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (jlo == 0 && jhi == SC_NJ)
-            score_heads<true>(q_lds, wq_lds, h_idx, b, 0, SC_NJ, acc);
-        else
-            score_heads<false>(q_lds, wq_lds, h_idx, b, jlo, jhi, acc);
+        score_heads(q_lds, wq_lds, h_idx, b, acc);
 
         // lane holds queries 4g + e of the tile for pool Pw + 16j + n
 #pragma unroll

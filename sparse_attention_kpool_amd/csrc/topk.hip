@@ -21,7 +21,7 @@
 
 namespace kp {
 
-constexpr int TK_THREADS = 256;
+constexpr int TK_THREADS = 512;
 constexpr int TK_LDS_KEYS = 8192;    // keys cached in LDS (32 KB)
 constexpr int TK_BINS = 2048;        // histogram bins of the widest digit
 
