@@ -85,6 +85,15 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                          :: "s"(lds_base), "v"(voff), "s"(base) : "memory");
 }
 
+// The same copy as a raw-buffer load: the latent is a buffer resource (base,
+// no stride, its size in bytes), the row's byte offset is the scalar offset
+// and the lane's chunk offset the vector offset, so no 64-bit row address is
+// formed per row.
+__device__ __forceinline__ void lds_dma16_row(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+    __asm__ __volatile__("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                         :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)((KP_LDS const uint8_t*)p);
 }
@@ -238,7 +247,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             const int base = __shfl(excl, k * NW + wave, 64);
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0u));
-            if (ent[k] >= 0 && ent[k] < num_kv) list[base + below] = ent[k] * (D * 2);   // byte offset
+            if (ent[k] >= 0 && ent[k] < num_kv)   // byte offset (the latent is below 4 GiB)
+                list[base + below] = (int32_t)((uint32_t)ent[k] * (uint32_t)(D * 2));
         }
     }
     __syncthreads();
@@ -265,6 +275,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
     const uint32_t wave_lds = ring_lds + (uint32_t)(RPW * wave_s * RB);   // LDS row 16w of buffer 0
     const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row, before the chunk xor
+    // the latent as a raw buffer: base (48 bits), stride 0, num_kv * D * 2 bytes
+    // (below 4 GiB), and the default dword format of gfx9 buffer descriptors
+    const uint64_t kv_addr = reinterpret_cast<uint64_t>(kv);
+    const u32x4 kv_rsrc = u32x4{(uint32_t)kv_addr, (uint32_t)(kv_addr >> 32) & 0xFFFFu,
+                                (uint32_t)((uint64_t)num_kv * (D * 2)), 0x00020000u};
     // KP_ROWS_OF reads the byte offsets of this wave's 16 rows of tile kt_ into rws_[16];
     // KP_ISSUE_ROW(j_) issues the gather of the wave's row j_ into buffer buf_
 #define KP_ROWS_OF(kt_)                                                                        \
@@ -281,8 +296,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         /* lane chunk lane ^ swz(r) of the row (r % 16 = j_) */                                \
         const uint32_t loff_ = lane16 ^ (uint32_t)(row_swz(j_) << 4);                          \
         if (DP == D || (lane < DP / 8 && (loff_ >> 4) < (uint32_t)CH))                         \
-            lds_dma16(reinterpret_cast<const uint8_t*>(kv) + (uint32_t)rws_[j_], loff_,        \
-                      __builtin_amdgcn_readfirstlane(wave_lds + (uint32_t)((buf_) * TILE_B + (j_) * RB))); \
+            lds_dma16_row(kv_rsrc, loff_, (uint32_t)rws_[j_],                                   \
+                          __builtin_amdgcn_readfirstlane(wave_lds + (uint32_t)((buf_) * TILE_B + (j_) * RB))); \
     }
 #define KP_ISSUE_TILE(kt_, buf_)                                                               \
     {                                                                                          \
