@@ -61,23 +61,25 @@ void run(float* d, int threads) {
     const int iters = 8192;
     const char* kn[4] = {"VALU fma", "SALU add", "LDS b128", "VALU exp"};
     mfma_issue_kernel<KIND, NV><<<256, threads>>>(d, iters, 1.0001f);
-    hipDeviceSynchronize();
-    hipEvent_t e0, e1; hipEventCreate(&e0); hipEventCreate(&e1);
-    hipEventRecord(e0);
+    if (hipDeviceSynchronize() != hipSuccess) { printf("launch failed\n"); return; }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return;
+    (void)hipEventRecord(e0);
     mfma_issue_kernel<KIND, NV><<<256, threads>>>(d, iters, 1.0001f);
-    hipEventRecord(e1);
+    (void)hipEventRecord(e1);
     hipError_t e = hipDeviceSynchronize();
-    float ms = 0; hipEventElapsedTime(&ms, e0, e1);
+    float ms = 0;
+    (void)hipEventElapsedTime(&ms, e0, e1);
     const double mf = 256.0 * (threads / 64) * iters * 4;
     if (e != hipSuccess) { printf("error %s\n", hipGetErrorString(e)); return; }
     float h[1];
-    hipMemcpy(h, d + 256 * threads, 4, hipMemcpyDeviceToHost);
+    (void)hipMemcpy(h, d + 256 * threads, 4, hipMemcpyDeviceToHost);
     printf("%d waves/SIMD %-9s x%2d per MFMA: %6.1f clock64 per 4 MFMA; kernel %.3f ms = %.0f TFLOP/s bf16 (%.1f%% of 2.5 PF)\n", threads / 256, kn[KIND], NV, h[0], ms, mf * 16384 / ms / 1e9, mf * 16384 / ms / 1e9 / 25.0);
 }
 
 int main() {
     float* d;
-    hipMalloc(&d, (1 << 20) * 4);
+    if (hipMalloc(&d, (1 << 20) * 4) != hipSuccess) return 1;
     for (int t = 256; t <= 512; t += 256) {
         run<0, 0>(d, t); run<0, 2>(d, t); run<0, 4>(d, t); run<0, 8>(d, t);
         run<1, 4>(d, t); run<1, 8>(d, t); run<1, 16>(d, t);
