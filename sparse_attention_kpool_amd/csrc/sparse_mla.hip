@@ -26,12 +26,14 @@
 // are merged once at the end through LDS. The LDS traffic per 32 gathered rows
 // is the 32 KB gather plus 128 KB of K and V reads (each row is read by the
 // two head halves), with one barrier per 64 rows.
-// The softmax reference max of a head is re-based (and O rescaled) only when a
-// tile's max exceeds it by more than 8 (log2 units), so weights stay below 2^8
-// and O is untouched outside the MFMAs on most tiles. LDS rows keep their
-// 16-byte chunks permuted by a per-row xor so the row-wise K reads and the
-// column-wise V reads are both free of bank conflicts. A latent narrower than
-// 128 is zero-padded to 128 in LDS.
+// A head's softmax reference is fixed for a pass, so O is never rescaled: it
+// is the max of the head's first tile, lifted by MLA_REF_LIFT, and later
+// weights may exceed 1 up to 2^MLA_HEADROOM; a weight beyond that makes the
+// workgroup drop the pass, sweep QK for the exact max of every head, and run
+// the attention again. O is normalised by the sum of the weights as rounded to
+// bf16 (the values the PV product used). LDS rows use a padded pitch (see
+// row_base) so the row-wise K reads and the column-wise V reads are both free
+// of bank conflicts. A latent narrower than 128 is zero-padded to 128 in LDS.
 #include "kp_device.h"
 #include "kp_launch.h"
 
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint32_t ring_lds = lds_addr(ring);
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
     const uint32_t wave_lds = ring_lds + (uint32_t)row_base<RB>(RPW * wave_s);   // LDS row 16w of buffer 0
-    const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row, before the chunk xor
+    const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row
     // the latent as a raw buffer: base (48 bits), stride 0, num_kv * D * 2 bytes
     // (below 4 GiB), and the default dword format of gfx9 buffer descriptors
     const uint64_t kv_addr = reinterpret_cast<uint64_t>(kv);
