@@ -82,6 +82,9 @@ def test_invalid_args_rejected_on_host(L):
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 65, 512, 128, C.c_float(0.1), fake, None, None) == 2
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, None, None) == 2
     assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 1
+    # index rows wider than the attention's LDS list
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 4097, C.c_float(0.1), fake, None, None) == 2
+    assert b"row_width" in L.kp_last_error()
     assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
     for bad in (0.0, -0.1, float("inf"), float("nan")):          # the softmax scale must be positive
         assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 128, C.c_float(bad), fake, None, None) == 1

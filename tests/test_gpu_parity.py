@@ -241,7 +241,7 @@ def test_mla_fed_oracle_rows(K, oracle_mod, name):
 
 
 @pytest.mark.parametrize("case", ["scattered_mask", "empty_rows", "single", "duplicates", "heads40",
-                                  "rising", "rising_tail"])
+                                  "rising", "rising_tail", "max_width"])
 def test_mla_edge_rows(K, oracle_mod, case):
     """Edge rows of the attention. "rising" and "rising_tail" put rows whose
     scores lie hundreds of log2 units above those of the first tile after it
@@ -252,6 +252,8 @@ def test_mla_edge_rows(K, oracle_mod, case):
     H, D, N, W, Tq = 64, 512, 3000, 256, 9
     if case == "heads40":
         H = 40
+    if case == "max_width":   # the widest index row the attention accepts: 64 tiles of rows
+        W, Tq = 4096, 3
     q = (rng.standard_normal((Tq, H, D))).astype(np.float32)
     kv = (rng.standard_normal((N, D))).astype(np.float32)
     if case.startswith("rising"):
@@ -275,6 +277,9 @@ def test_mla_edge_rows(K, oracle_mod, case):
         idx[np.arange(Tq), rng.integers(0, W, Tq)] = rng.integers(0, N, Tq)
     if case == "duplicates":
         idx[:, 100:] = idx[:, :W - 100][:, :W - 100]
+    if case == "max_width":   # row 0 full; rows 1, 2 with masked entries spread over the row
+        idx[1:][rng.random((Tq - 1, W)) < 0.3] = -1
+        idx[2, W - 50:] = -1
     _log("mla edge", case)
     g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), 1 / np.sqrt(D))
     # (errors are scaled by sum_j p_j |v_j|, as in the fed-oracle test: the bf16
