@@ -212,6 +212,8 @@ __device__ __forceinline__ void topk_row(const uint32_t* keys_lds, int (*hist)[T
     }
 }
 
+__device__ void mw_init(int32_t* row, int row_width, int n, int k);
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
@@ -230,7 +232,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int doc_start = cu[qp.doc];
     int32_t* row = indices + (size_t)i * row_width;
     const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
-    if (skip_long && n > TK_LDS_KEYS) return;   // a row for topk_long_kernel
+    if (skip_long && n > TK_LDS_KEYS) {   // a row for the long-row kernels
+        if (skip_long == 2) mw_init(row, row_width, n, k);
+        return;
+    }
 
     if (n <= TK_LDS_KEYS) {
         if (k < n && k > 0) {
@@ -264,7 +269,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
 
 // ------------------------------------------------------------- long rows ----
 // Rows with more visible pools than the LDS key cache (decode over a long
-// context) get a workgroup of 1024 threads: the same radix select with the
+// context) go to the many-workgroup kernels below when their index rows have
+// room for the scratch; otherwise each gets a workgroup of 1024 threads: the same radix select with the
 // scores streamed from memory in 16-byte loads, several in flight per thread;
 // when the boundary bin is kept whole (no tie is split) the kept pools are
 // collected in LDS in any order, sorted (bitonic) and written out with
@@ -459,19 +465,296 @@ __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
     if (tid == 0 && num_valid) num_valid[i] = base + n_tail;
 }
 
+// ------------------------------------------------ long rows, many workgroups --
+// A long row (decode over a long context) is cut into chunks of TM_CHUNK pools,
+// one workgroup each, and the radix select runs as a sequence of launches: per
+// digit, every chunk adds its histogram to the row's (global atomics), then one
+// wave per row picks the digit; then every chunk counts its keys above and equal
+// to the threshold, and writes its kept pools at their ranks in pool order. The
+// scratch lives in the row's own index slots, which only the last launches write:
+//   row[0 .. TK_BINS)                  histogram of the current digit
+//   row[W - TM_STATE .. W)             prefix (the threshold when done), digit mask,
+//                                      keys still to choose, done, equal keys kept
+//   row[W - TM_STATE - 2*C .. )        per chunk: keys above, keys equal
+// (C chunks of the widest row). The host takes this path only when the rows have
+// room for it; otherwise topk_long_kernel runs.
+constexpr int TM_CHUNK = 8192;
+constexpr int TM_THREADS = 512;
+constexpr int TM_STATE = 8;
+constexpr int TM_ALL_EQ = 0x7FFFFFFF;
+
+// digit PASS: width and position of its bits in the key
+template <int PASS> struct TmDigit {
+    static constexpr int width = PASS < 2 ? 11 : 10;
+    static constexpr int shift = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
+    static constexpr int nb = 1 << width;
+};
+
+struct TmRow {
+    int n, k, t, tail_start, doc_start;
+    const float* srow;
+    int32_t* row;
+    int32_t* st;   // state
+    int32_t* cc;   // chunk counts
+};
+
+__device__ __forceinline__ TmRow tm_row(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                                       const int32_t* q_pos, const float* scores, int max_pools, int topk,
+                                       int row_width, int32_t* indices, int i) {
+    TmRow r;
+    r.t = q_pos ? q_pos[i] : i;
+    const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, r.t);
+    r.n = qp.n_vis;
+    r.k = r.n < topk ? r.n : topk;
+    r.tail_start = qp.tail_start;
+    r.doc_start = cu[qp.doc];
+    r.srow = scores + (size_t)i * max_pools + qp.pool_lo;
+    r.row = indices + (size_t)i * row_width;
+    r.st = r.row + row_width - TM_STATE;
+    r.cc = r.st - 2 * ((max_pools + TM_CHUNK - 1) / TM_CHUNK);
+    return r;
+}
+
+// by topk_kernel, for a long row: zero histogram, initial state
+__device__ void mw_init(int32_t* row, int row_width, int n, int k) {
+    for (int b = threadIdx.x; b < TK_BINS; b += blockDim.x) row[b] = 0;
+    if (threadIdx.x == 0) {
+        int32_t* st = row + row_width - TM_STATE;
+        const bool done = k == 0 || k >= n;   // nothing to choose: keep none, or every pool
+        st[0] = k == 0 ? (int32_t)0xFFFFFFFFu : 0;   // prefix; once done, the threshold key
+        st[1] = 0;                                 // bits of the key fixed by the prefix
+        st[2] = k;                                 // keys still to choose among the prefix's
+        st[3] = done;
+        st[4] = k == 0 ? 0 : TM_ALL_EQ;            // keys equal to the threshold kept
+    }
+}
+
+template <int PASS>
+__global__ __launch_bounds__(TM_THREADS) void topk_mw_hist_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices) {
+    using Dg = TmDigit<PASS>;
+    __shared__ int h[Dg::nb];
+    const TmRow r = tm_row(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools, topk, row_width, indices,
+                           blockIdx.x);
+    const int c0 = blockIdx.y * TM_CHUNK;
+    if (r.n <= TK_LDS_KEYS || c0 >= r.n || r.st[3]) return;
+    const int c1 = min(r.n, c0 + TM_CHUNK);
+    const uint32_t prefix = (uint32_t)r.st[0], pmask = (uint32_t)r.st[1];
+    const bool aligned = (reinterpret_cast<uintptr_t>(r.srow) & 15) == 0;
+    for (int b = threadIdx.x; b < Dg::nb; b += TM_THREADS) h[b] = 0;
+    __syncthreads();
+#pragma unroll 4
+    for (int j = c0 + 4 * threadIdx.x; j < c1; j += 4 * TM_THREADS) {
+        uint32_t kk[4];
+        fetch4_g(kk, r.srow, j, c1, aligned);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < c1 && (kk[e] & pmask) == prefix) atomicAdd(&h[(kk[e] >> Dg::shift) & (Dg::nb - 1)], 1);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < Dg::nb; b += TM_THREADS)
+        if (h[b]) atomicAdd(&r.row[b], h[b]);
+}
+
+// one wave per row: the digit holding the remaining-th largest key
+template <int PASS>
+__global__ __launch_bounds__(64) void topk_mw_select_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices) {
+    using Dg = TmDigit<PASS>;
+    const TmRow r = tm_row(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools, topk, row_width, indices,
+                           blockIdx.x);
+    if (r.n <= TK_LDS_KEYS || r.st[3]) return;
+    const int lane = threadIdx.x;
+    const int remaining = r.st[2];
+    // lane l owns bins [nb - per*(l+1), nb - per*l); a scan over lanes counts the
+    // keys in the bins above each lane's
+    constexpr int per = Dg::nb >> 6;   // 32 or 16
+    const int base = Dg::nb - per * (lane + 1);
+    int cnt[per];
+    int own = 0;
+#pragma unroll
+    for (int m = 0; m < per; ++m) {
+        cnt[m] = r.row[base + m];
+        own += cnt[m];
+    }
+    const int incl = wave_incl_scan(own);
+    const int before = incl - own;
+    int sdig = 0, sabove = 0, scnt = 0;
+    if (before < remaining && incl >= remaining) {
+        int acc = before;
+#pragma unroll
+        for (int m = per - 1; m >= 0; --m) {
+            if (acc < remaining && acc + cnt[m] >= remaining) {
+                sdig = base + m;
+                sabove = acc;
+                scnt = cnt[m];
+            }
+            acc += cnt[m];
+        }
+    }
+    const unsigned long long who = __ballot(before < remaining && incl >= remaining);
+    const int src = who ? __builtin_ctzll(who) : 0;   // (one lane holds the boundary)
+    sdig = __shfl(sdig, src, 64);
+    sabove = __shfl(sabove, src, 64);
+    scnt = __shfl(scnt, src, 64);
+    for (int b = lane; b < TK_BINS; b += 64) r.row[b] = 0;   // the next digit's histogram
+    if (lane == 0) {
+        const int rem = remaining - sabove;
+        const bool whole = scnt == rem;   // the bin is kept whole: no tie is split
+        r.st[0] = (int32_t)((uint32_t)r.st[0] | ((uint32_t)sdig << Dg::shift));
+        r.st[1] = (int32_t)((uint32_t)r.st[1] | ((uint32_t)(Dg::nb - 1) << Dg::shift));
+        r.st[2] = rem;
+        r.st[3] = whole || PASS == 2;
+        r.st[4] = whole ? TM_ALL_EQ : rem;
+    }
+}
+
+// per chunk: keys above and equal to the threshold
+__global__ __launch_bounds__(TM_THREADS) void topk_mw_count_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices) {
+    __shared__ int wave_buf[TM_THREADS / 64];
+    const TmRow r = tm_row(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools, topk, row_width, indices,
+                           blockIdx.x);
+    const int c0 = blockIdx.y * TM_CHUNK;
+    if (r.n <= TK_LDS_KEYS || c0 >= r.n) return;
+    const int c1 = min(r.n, c0 + TM_CHUNK);
+    const uint32_t thresh = (uint32_t)r.st[0];
+    const bool aligned = (reinterpret_cast<uintptr_t>(r.srow) & 15) == 0;
+    int gt = 0, eq = 0;
+#pragma unroll 4
+    for (int j = c0 + 4 * threadIdx.x; j < c1; j += 4 * TM_THREADS) {
+        uint32_t kk[4];
+        fetch4_g(kk, r.srow, j, c1, aligned);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < c1) {
+                gt += kk[e] > thresh;
+                eq += kk[e] == thresh;
+            }
+    }
+    // (16 bits each: a chunk has at most TM_CHUNK keys)
+    int tot;
+    block_excl_scan(gt | (eq << 16), wave_buf, &tot);
+    if (threadIdx.x == 0) {
+        r.cc[2 * blockIdx.y] = tot & 0xFFFF;
+        r.cc[2 * blockIdx.y + 1] = tot >> 16;
+    }
+}
+
+// per chunk: its kept pools at their ranks, in pool order
+__global__ __launch_bounds__(TM_THREADS) void topk_mw_write_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices) {
+    __shared__ int wave_buf[TM_THREADS / 64];
+    const TmRow r = tm_row(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools, topk, row_width, indices,
+                           blockIdx.x);
+    const int c = blockIdx.y, c0 = c * TM_CHUNK;
+    if (r.n <= TK_LDS_KEYS || c0 >= r.n) return;
+    const int c1 = min(r.n, c0 + TM_CHUNK);
+    const uint32_t thresh = (uint32_t)r.st[0];
+    const int take_eq = r.st[4];
+    // kept pools and keys equal to the threshold in the chunks before this one
+    int pos0 = 0, eqb = 0;
+    for (int q = 0; q < c; ++q) {
+        const int gq = r.cc[2 * q], eqq = r.cc[2 * q + 1];
+        const int keq = take_eq == TM_ALL_EQ ? eqq : max(0, min(eqq, take_eq - eqb));
+        pos0 += gq + keq;
+        eqb += eqq;
+    }
+    // contiguous runs of TM_RUN keys per thread, in pool order, read once
+    constexpr int TM_RUN = TM_CHUNK / TM_THREADS;
+    static_assert(TM_RUN % 4 == 0, "runs of whole 16-byte groups");
+    const int j0 = c0 + (int)threadIdx.x * TM_RUN;
+    const bool aligned = (reinterpret_cast<uintptr_t>(r.srow) & 15) == 0;
+    uint32_t kk[TM_RUN];
+#pragma unroll
+    for (int q = 0; q < TM_RUN; q += 4) {
+        uint32_t k4[4];
+        fetch4_g(k4, r.srow, j0 + q, c1, aligned);   // (keys at or past c1 read as 0 and are skipped)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[q + e] = k4[e];
+    }
+    int tot, n_eq = 0;
+#pragma unroll
+    for (int q = 0; q < TM_RUN; ++q) n_eq += (j0 + q < c1 && kk[q] == thresh);
+    const int eq_before = eqb + block_excl_scan(n_eq, wave_buf, &tot);
+    int e_rank = eq_before, n_sel = 0;
+#pragma unroll
+    for (int q = 0; q < TM_RUN; ++q)
+        if (j0 + q < c1) n_sel += kk[q] > thresh || (kk[q] == thresh && e_rank++ < take_eq);
+    int pos = pos0 + block_excl_scan(n_sel, wave_buf, &tot);
+    e_rank = eq_before;
+#pragma unroll
+    for (int q = 0; q < TM_RUN; ++q) {
+        if (j0 + q < c1 && (kk[q] > thresh || (kk[q] == thresh && e_rank++ < take_eq))) {
+            const int tok = r.doc_start + kpool * (j0 + q);
+            if (kpool == 4) {
+                *reinterpret_cast<int4*>(r.row + 4 * pos) = make_int4(tok, tok + 1, tok + 2, tok + 3);
+            } else {
+                for (int u = 0; u < kpool; ++u) r.row[pos * kpool + u] = tok + u;
+            }
+            ++pos;
+        }
+    }
+}
+
+// the row's own incomplete pool and padding (over the scratch), and its slot count
+__global__ __launch_bounds__(256) void topk_mw_tail_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid) {
+    const TmRow r = tm_row(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools, topk, row_width, indices,
+                           blockIdx.x);
+    if (r.n <= TK_LDS_KEYS) return;
+    const int base = r.k * kpool;
+    const int n_tail = r.t - r.tail_start + 1;
+    for (int q = threadIdx.x; q < row_width - base; q += 256)
+        r.row[base + q] = q < n_tail ? r.tail_start + q : -1;
+    if (threadIdx.x == 0 && num_valid) num_valid[blockIdx.x] = base + n_tail;
+}
+
 hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
                        const int32_t* q_pos, int num_q, const float* scores, int max_pools,
                        int topk, int row_width, int32_t* indices, int32_t* num_valid,
                        hipStream_t stream) {
     if (num_q == 0) return hipSuccess;
-    // rows with more visible pools than the key cache holds go to the long-row kernel
+    // rows with more visible pools than the key cache holds go to the long-row
+    // kernels: many workgroups per row when the rows have room for the scratch
+    // (a histogram in the token slots, the state and chunk counts in the padding),
+    // otherwise one workgroup per row
     const int has_long = max_pools > TK_LDS_KEYS;
+    const int chunks = (max_pools + TM_CHUNK - 1) / TM_CHUNK;
+    const bool many = has_long && (long long)kpool * topk >= TK_BINS &&
+                      (long long)row_width >= (long long)kpool * topk + kpool + TM_STATE + 2 * chunks;
     topk_kernel<<<num_q, TK_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools,
-                                                  topk, row_width, indices, num_valid, has_long);
+                                                  topk, row_width, indices, num_valid,
+                                                  !has_long ? 0 : (many ? 2 : 1));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !has_long) return e;
-    topk_long_kernel<<<num_q, TL_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools,
-                                                       topk, row_width, indices, num_valid);
+    if (!many) {
+        topk_long_kernel<<<num_q, TL_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores,
+                                                           max_pools, topk, row_width, indices, num_valid);
+        return hipGetLastError();
+    }
+    const dim3 cg(num_q, chunks);   // rows on x (up to 2^31 - 1), chunks on y
+#define KP_MW_ARGS cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools, topk, row_width, indices
+    topk_mw_hist_kernel<0><<<cg, TM_THREADS, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_select_kernel<0><<<num_q, 64, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_hist_kernel<1><<<cg, TM_THREADS, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_select_kernel<1><<<num_q, 64, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_hist_kernel<2><<<cg, TM_THREADS, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_select_kernel<2><<<num_q, 64, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_count_kernel<<<cg, TM_THREADS, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_write_kernel<<<cg, TM_THREADS, 0, stream>>>(KP_MW_ARGS);
+    topk_mw_tail_kernel<<<num_q, 256, 0, stream>>>(KP_MW_ARGS, num_valid);
+#undef KP_MW_ARGS
     return hipGetLastError();
 }
 
