@@ -249,10 +249,13 @@ hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools
                         int max_pools, float* scores, hipStream_t stream) {
     if (num_q == 0 || max_pools == 0) return hipSuccess;
     // split the pools of a query tile over several workgroups when the tiles
-    // alone give fewer than ~2048 workgroups
+    // alone give fewer than 512 workgroups: two per compute unit (four waves per
+    // SIMD) on the 256 CUs, so one round of workgroups fills the GPU and each
+    // walks several chunks, which repays staging its 16 queries' codes (more,
+    // shorter splits were slower at decode: 2048 of them took 37 us more)
     const int nqt = (num_q + SC_QT - 1) / SC_QT;
     const int nchunks = (max_pools + SC_PC - 1) / SC_PC;
-    int nsplit = (2048 + nqt - 1) / nqt;
+    int nsplit = (512 + nqt - 1) / nqt;
     if (nsplit > nchunks) nsplit = nchunks;
     if (nsplit < 1) nsplit = 1;
     const long long nblk = (long long)nqt * nsplit;

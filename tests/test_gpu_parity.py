@@ -120,9 +120,12 @@ def _gpu_scores(K, s, wl, cp, k8, sk, rows=None):
     return host(idx), host(nv), host(sc)
 
 
-@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k", "32k_rows", "decode1m_rows"])
+@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k", "32k_rows", "decode1m_rows", "decode1m_tiles2"])
 def test_scores_fed_oracle_keys(K, oracle_mod, name):
-    base = name.replace("_rows", "")
+    """decode1m_tiles2: 17 decode queries make two query tiles, so each tile's
+    pools are split over fewer workgroups than there are 512-pool chunks and
+    every workgroup walks several chunks."""
+    base = name.replace("_rows", "").replace("_tiles2", "")
     s = spec(base)
     wl = Workload(s)
     rng = np.random.default_rng(0)
@@ -130,6 +133,8 @@ def test_scores_fed_oracle_keys(K, oracle_mod, name):
     if name.endswith("_rows"):
         nr = 4 if base == "decode1m" else 12
         rows = np.unique(np.concatenate([rng.choice(s.Tq, nr, replace=False), [0, s.Tq - 1]]))
+    if name.endswith("_tiles2"):
+        rows = np.append(np.arange(0, s.Tq, 4), s.Tq - 1)
     _log("scores", name, "rows", None if rows is None else rows.tolist())
     cp, ps, k8, sk = _oracle_keys(oracle_mod, s, wl)
     _, _, g_sc = _gpu_scores(K, s, wl, cp, k8, sk, rows)
