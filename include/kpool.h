@@ -122,6 +122,25 @@ kp_status kpool_build(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_t
                       hipStream_t stream);
 
 /*
+ * kpool_build_from -- kpool_build for the pools that end at or after token
+ * token_lo, for a pooled-key cache that grows with the context (decode): the
+ * keys of a complete pool depend only on its own kpool tokens [P4-S3], so the
+ * pools whose last token lies before token_lo are the caller's, from an earlier
+ * kpool_build or kpool_build_from over the same documents, and are not written.
+ * Every other output is written exactly as kpool_build writes it: cu_pools in
+ * full, and pool_start, pooled_k_fp8, pooled_k_scale (and pooled_k_f32) of each
+ * pool ending at or after token_lo and of each row past cu_pools[num_docs].
+ * token_lo = 0 is kpool_build. Arguments as for kpool_build, and
+ *   token_lo        0 .. num_tokens (KP_ERR_INVALID_ARG otherwise)
+ */
+kp_status kpool_build_from(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                           const uint16_t* k_idx, const uint16_t* gate, const float* ape,
+                           int32_t d_idx, int32_t kpool, int32_t token_lo,
+                           int32_t* cu_pools, int32_t* pool_start,
+                           uint8_t* pooled_k_fp8, float* pooled_k_scale, float* pooled_k_f32,
+                           hipStream_t stream);
+
+/*
  * indexer_rotate_quant -- the query half of the rotation and FP8 step [P4-S3]:
  * x = H_n q_idx[i,h,:] (as in kpool_build), scale[i,h] = max|x|/448 (1 if x == 0),
  * codes[i,h,c] = e4m3(x[c] / scale[i,h]).

@@ -27,6 +27,7 @@ SIGNATURES = [
     ("kp_version", _I, []),
     ("kp_row_width", _I, [_I, _I]),
     ("kpool_build", _I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    ("kpool_build_from", _I, [_P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     ("indexer_rotate_quant", _I, [_P, _I, _I, _I, _P, _P, _P]),
     ("kp_indexer_workspace_bytes", _Z, [_I, _I, _I, _I]),
     ("indexer_score_topk", _I, [_P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
@@ -124,6 +125,30 @@ def kpool_build(cu_seqlens: torch.Tensor, k_idx: torch.Tensor, gate: torch.Tenso
     _check(lib().kpool_build(_ptr(cu_seqlens), B, T, _ptr(k_idx), _ptr(gate), _ptr(ape), d, kpool,
                              _ptr(cu_pools), _ptr(pool_start), _ptr(k8), _ptr(ks), _ptr(kf), _stream(dev)))
     return cu_pools, pool_start, k8, ks, kf
+
+
+def kpool_build_from(cu_seqlens: torch.Tensor, k_idx: torch.Tensor, gate: torch.Tensor, ape: torch.Tensor,
+                     token_lo: int, out, kpool: int = 4) -> None:
+    """kpool_build for the pools ending at or after token_lo, into `out` =
+    (cu_pools, pool_start, pooled_k_fp8, pooled_k_scale, pooled_k_f32 or None),
+    the tensors of an earlier kpool_build over the same documents (the pooled-key
+    cache); the rows of pools ending before token_lo are left as they are."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(gate, "gate", torch.bfloat16, 2)
+    _need(ape, "ape", torch.float32, 2)
+    T, d = k_idx.shape
+    if gate.shape != k_idx.shape or ape.shape != (kpool, d):
+        raise ValueError("gate must match k_idx and ape must be [kpool, d_idx]")
+    B = cu_seqlens.shape[0] - 1
+    cap = T // kpool
+    cu_pools, pool_start, k8, ks, kf = out
+    if (cu_pools.shape != (B + 1,) or pool_start.shape != (cap,) or k8.shape != (cap, d) or ks.shape != (cap,)
+            or (kf is not None and kf.shape != (cap, d))):
+        raise ValueError("out must hold the outputs of kpool_build for these sizes")
+    _check(lib().kpool_build_from(_ptr(cu_seqlens), B, T, _ptr(k_idx), _ptr(gate), _ptr(ape), d, kpool,
+                                  int(token_lo), _ptr(cu_pools), _ptr(pool_start), _ptr(k8), _ptr(ks), _ptr(kf),
+                                  _stream(k_idx.device)))
 
 
 def indexer_rotate_quant(q_idx: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -77,14 +77,16 @@ int32_t kp_row_width(int32_t kpool, int32_t topk_pools) {
     return (int32_t)w;
 }
 
-kp_status kpool_build(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
-                      const uint16_t* k_idx, const uint16_t* gate, const float* ape,
-                      int32_t d_idx, int32_t kpool,
-                      int32_t* cu_pools, int32_t* pool_start,
-                      uint8_t* pooled_k_fp8, float* pooled_k_scale, float* pooled_k_f32,
-                      hipStream_t stream) {
+kp_status kpool_build_from(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                           const uint16_t* k_idx, const uint16_t* gate, const float* ape,
+                           int32_t d_idx, int32_t kpool, int32_t token_lo,
+                           int32_t* cu_pools, int32_t* pool_start,
+                           uint8_t* pooled_k_fp8, float* pooled_k_scale, float* pooled_k_f32,
+                           hipStream_t stream) {
     g_err.clear();
     if (num_docs < 0 || num_tokens < 0) return fail(KP_ERR_INVALID_ARG, "negative size");
+    if (token_lo < 0 || token_lo > num_tokens)
+        return fail(KP_ERR_INVALID_ARG, "token_lo must be in 0..num_tokens (got %d)", token_lo);
     if (kpool < 1 || kpool > 16) return fail(KP_ERR_UNSUPPORTED, "kpool must be in 1..16 (got %d)", kpool);
     if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
     if (!cu_seqlens || !cu_pools) return fail(KP_ERR_INVALID_ARG, "cu_seqlens and cu_pools are required");
@@ -97,9 +99,19 @@ kp_status kpool_build(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_t
     if (st != KP_OK) return st;
     hipError_t e = kp::launch_layout_pool(cu_seqlens, num_docs, num_tokens, k_idx, gate, ape, d_idx, kpool,
                                           hadamard_norm(d_idx), cu_pools, pool_start, pooled_k_fp8,
-                                          pooled_k_scale, pooled_k_f32, stream);
+                                          pooled_k_scale, pooled_k_f32, token_lo, stream);
     if (e != hipSuccess) return hip_fail(e, "kpool_build launch");
     return ok();
+}
+
+kp_status kpool_build(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                      const uint16_t* k_idx, const uint16_t* gate, const float* ape,
+                      int32_t d_idx, int32_t kpool,
+                      int32_t* cu_pools, int32_t* pool_start,
+                      uint8_t* pooled_k_fp8, float* pooled_k_scale, float* pooled_k_f32,
+                      hipStream_t stream) {
+    return kpool_build_from(cu_seqlens, num_docs, num_tokens, k_idx, gate, ape, d_idx, kpool, 0, cu_pools,
+                            pool_start, pooled_k_fp8, pooled_k_scale, pooled_k_f32, stream);
 }
 
 kp_status indexer_rotate_quant(const uint16_t* q_idx, int32_t num_q, int32_t h_idx, int32_t d_idx,

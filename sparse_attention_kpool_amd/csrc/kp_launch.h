@@ -12,7 +12,7 @@ namespace kp {
 hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, const uint16_t* k_idx,
                               const uint16_t* gate, const float* ape, int d_idx, int kpool,
                               float norm, int32_t* cu_pools, int32_t* pool_start, uint8_t* k8,
-                              float* ks, float* kf32, hipStream_t stream);
+                              float* ks, float* kf32, int token_lo, hipStream_t stream);
 
 // Rotated FP8 indexer queries: rows = num_q * h_idx vectors of d_idx channels.
 hipError_t launch_rotate_quant(const uint16_t* q_idx, long long rows, int d_idx, float norm,

@@ -90,11 +90,11 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
     const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ gate,
     const float* __restrict__ ape, int kpool, int pool_cap, float norm,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ k8, float* __restrict__ ks,
-    float* __restrict__ kf32) {
+    float* __restrict__ kf32, int p_base, int token_lo) {
     constexpr int N = 4 * L;
     const int lane = threadIdx.x & 63;
     const int j = lane % L;
-    const int p = (blockIdx.x * blockDim.x + threadIdx.x) / L;
+    const int p = p_base + (int)((blockIdx.x * blockDim.x + threadIdx.x) / L);
     if (p >= pool_cap) return;
     const int total = cu_pools[num_docs];
     if (p >= total) {
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
     // document of pool p: the d with cu_pools[d] <= p < cu_pools[d+1]
     int d = find_doc(cu_pools, num_docs, p);
     const int s = cu[d] + kpool * (p - cu_pools[d]);
+    if (s + kpool - 1 < token_lo) return;   // a pool of the caller's cache
 
     // per-channel softmax over the kpool tokens of the pool, then the weighted sum
     float x[4];
@@ -193,19 +194,22 @@ template <int KP>
 static void launch_pool_keys(int blocks, hipStream_t stream, int d_idx, const int32_t* cu, int num_docs,
                              const int32_t* cu_pools, const uint16_t* k_idx, const uint16_t* gate,
                              const float* ape, int kpool, int pool_cap, float norm, int32_t* pool_start,
-                             uint8_t* k8, float* ks, float* kf32) {
+                             uint8_t* k8, float* ks, float* kf32, int p_base, int token_lo) {
     switch (d_idx) {
         case 32:
             pool_keys_kernel<8, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
-                                                            pool_cap, norm, pool_start, k8, ks, kf32);
+                                                            pool_cap, norm, pool_start, k8, ks, kf32, p_base,
+                                                            token_lo);
             break;
         case 64:
             pool_keys_kernel<16, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
-                                                             pool_cap, norm, pool_start, k8, ks, kf32);
+                                                             pool_cap, norm, pool_start, k8, ks, kf32, p_base,
+                                                            token_lo);
             break;
         default:
             pool_keys_kernel<32, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
-                                                             pool_cap, norm, pool_start, k8, ks, kf32);
+                                                             pool_cap, norm, pool_start, k8, ks, kf32, p_base,
+                                                            token_lo);
             break;
     }
 }
@@ -213,19 +217,30 @@ static void launch_pool_keys(int blocks, hipStream_t stream, int d_idx, const in
 hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, const uint16_t* k_idx,
                               const uint16_t* gate, const float* ape, int d_idx, int kpool,
                               float norm, int32_t* cu_pools, int32_t* pool_start, uint8_t* k8,
-                              float* ks, float* kf32, hipStream_t stream) {
+                              float* ks, float* kf32, int token_lo, hipStream_t stream) {
     layout_scan_kernel<<<1, 1024, 0, stream>>>(cu, num_docs, kpool, cu_pools);
     const int pool_cap = num_tokens / kpool;
     if (pool_cap == 0) return hipGetLastError();
+    // With token_lo > 0 only pools ending at or after token_lo (and the rows past
+    // the last pool) are written. Every such pool has a global number of at least
+    // (token_lo - (kpool-1) - num_docs*(kpool-1)) / kpool, since each document
+    // leaves fewer than kpool of its tokens out of its pools; the launch starts
+    // there, and the pools between that bound and token_lo return at once.
+    int p_base = 0;
+    if (token_lo > 0) {
+        const long long lb = ((long long)token_lo - (kpool - 1) - (long long)num_docs * (kpool - 1)) / kpool;
+        p_base = (int)(lb > 0 ? (lb < pool_cap ? lb : pool_cap) : 0);
+    }
+    if (p_base >= pool_cap) return hipGetLastError();
     const int L = d_idx / 4;
-    const long long threads = (long long)pool_cap * L;
+    const long long threads = (long long)(pool_cap - p_base) * L;
     const int blocks = (int)((threads + 255) / 256);
     if (kpool == 4)
         launch_pool_keys<4>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
-                            norm, pool_start, k8, ks, kf32);
+                            norm, pool_start, k8, ks, kf32, p_base, token_lo);
     else
         launch_pool_keys<0>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
-                            norm, pool_start, k8, ks, kf32);
+                            norm, pool_start, k8, ks, kf32, p_base, token_lo);
     return hipGetLastError();
 }
 

@@ -65,6 +65,10 @@ def test_invalid_args_rejected_on_host(L):
     assert L.kpool_build(fake, -1, 64, fake, fake, fake, 128, 4, fake, fake, fake, fake, None, None) == 1
     # empty row: a no-op
     assert L.kpool_build(fake, 0, 0, None, None, None, 128, 4, fake, None, None, None, None, None) == 0
+    # the first token of the pooled-key tail must lie in 0 .. num_tokens
+    for lo in (-1, 65):
+        assert L.kpool_build_from(fake, 1, 64, fake, fake, fake, 128, 4, lo, fake, fake, fake, fake, None, None) == 1
+    assert b"token_lo" in L.kp_last_error()
     # indexer: row width not a multiple of 128 / too narrow / max_pools mismatch
     args = lambda W, mp=16, nq=64, qpos=None: (fake, 1, 64, fake, mp, fake, fake, qpos, nq, fake, fake, 2, 32, 4,
                                                4, W, fake, None, None, fake, 1 << 30, None)

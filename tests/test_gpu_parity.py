@@ -85,6 +85,41 @@ def test_pooled_keys(K, oracle_mod, name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "2k", "packed4k"])
+def test_pooled_keys_from_token(K, name):
+    """kpool_build_from rebuilds exactly the pools that end at or after token_lo
+    (bit for bit as kpool_build writes them) and the rows past the last pool,
+    and leaves the rows of earlier pools (the caller's cache) as they were."""
+    s = spec(name)
+    wl = Workload(s)
+    args = (dev(s.cu), dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")), dev(wl.ape()))
+    ref = [host(t) for t in K.kpool_build(*args, s.kpool, with_f32=True)]
+    ref_cp, ref_ps = ref[0], ref[1]
+    P = int(ref_cp[-1])
+    ends = np.full(len(ref_ps), -1, np.int64)
+    ends[:P] = ref_ps[:P].astype(np.int64) + s.kpool - 1
+    starts = s.cu[:-1]
+    cases = sorted({0, 1, s.T // 2, s.T // 2 + 1, int(starts[-1]), s.T - 1, s.T - s.kpool, s.T})
+    for token_lo in cases:
+        out = K.kpool_build(*args, s.kpool, with_f32=True)
+        cached = ends < token_lo          # rows of pools the call must not write (rows >= P are rebuilt)
+        cached[P:] = False
+        # sentinels everywhere: the cache rows must keep theirs, every other row must be rebuilt
+        out[0].fill_(-7)
+        out[1].fill_(-9)
+        out[2].fill_(0x5A)
+        out[3].fill_(3.5)
+        out[4].fill_(-1.25)
+        K.kpool_build_from(*args, token_lo, out, s.kpool)
+        got = [host(t) for t in out]
+        _log("keys from", name, token_lo, int(cached.sum()), "cached of", len(ends))
+        assert np.array_equal(got[0], ref_cp)
+        keep = ~cached
+        for g, r, sentinel in zip(got[1:], ref[1:], (-9, 0x5A, 3.5, -1.25)):
+            assert np.array_equal(g[keep], r[keep]), f"token_lo {token_lo}: a rebuilt row differs"
+            assert np.all(g[cached] == sentinel), f"token_lo {token_lo}: a cached row was written"
+
+
+@pytest.mark.parametrize("name", ["tiny", "2k", "packed4k"])
 def test_query_codes_bitexact(K, oracle_mod, name):
     s = spec(name)
     wl = Workload(s)
