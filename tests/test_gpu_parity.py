@@ -332,19 +332,25 @@ def test_mla_edge_rows(K, oracle_mod, case):
     check_lse(host(g_lse), ref_lse, case)
 
 
-@pytest.mark.parametrize("case", ["d512", "d512_h24", "d64"])
+@pytest.mark.parametrize("case", ["d512", "d512_h24", "d64", "d512_few", "d64_few", "d512_h40_few"])
 def test_mla_many_queries(K, oracle_mod, case):
     """More queries than the GPU has compute units, so that every workgroup
     takes several queries in turn, with row kinds interleaved so that
     neighbouring queries of a workgroup differ: empty rows, full rows, ragged
     short rows, scattered masks, single entries, and rows that force the
-    exact-max passes (from the second tile on, or in the last tile only)."""
+    exact-max passes (from the second tile on, or in the last tile only).
+    The *_few cases have fewer workgroups than twice the compute units (a
+    decode-sized launch), one of them with 40 heads."""
     rng = np.random.default_rng(11)
     H, D, N, W, Tq = 64, 512, 3000, 192, 777
     if case == "d512_h24":
         H = 24
-    if case == "d64":
+    if case.startswith("d64"):
         D = 64
+    if case.endswith("_few"):
+        Tq = 300
+    if case == "d512_h40_few":
+        H = 40
     q = (rng.standard_normal((Tq, H, D))).astype(np.float32)
     kv = (rng.standard_normal((N, D))).astype(np.float32)
     kv[N // 2:] *= 100.0   # rows whose scores lie far above those of the others

@@ -11,7 +11,8 @@ but the next MFMA of the same accumulation touches its result registers fewer
 than RESULT_WAIT wait states after it (each instruction issued in between is
 one wait state, s_nop N is N + 1). The scan follows the instructions in the
 order they are laid out, which is how straight-line code and the fall-through
-of a branch issue.
+of a branch issue; it does not cross an unconditional branch (what follows one
+in the layout is reached only by jumps).
 """
 import os
 import re
@@ -86,6 +87,10 @@ def instructions(asm_lines):
     return instrs
 
 
+def unconditional(line):
+    return line.startswith(("s_branch", "s_setpc", "s_endpgm"))
+
+
 def wait_states(line):
     m = re.match(r"s_nop\s+(\d+)", line)
     return int(m.group(1)) + 1 if m else 1
@@ -104,6 +109,8 @@ def test_inline_mfma_operands_not_written_by_recent_valu(asm_lines):
         j = k - 1
         while j >= 0 and waits < MIN_WAIT:
             prev = instrs[j][0]
+            if unconditional(prev):
+                break
             hit = valu_dest(prev) & operands
             if hit:
                 bad.append(f"{prev!r} then {line!r} ({waits} wait states)")
@@ -128,7 +135,7 @@ def test_inline_mfma_results_left_alone_until_done(asm_lines):
         j = k + 1
         while j < len(instrs) and waits < RESULT_WAIT:
             nxt, nxt_asm = instrs[j]
-            if nxt.startswith("s_endpgm"):
+            if unconditional(nxt):
                 break
             parts = nxt.split(None, 1)
             touched = regs(parts[1]) if len(parts) > 1 else set()
