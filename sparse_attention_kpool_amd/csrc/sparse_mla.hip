@@ -77,24 +77,20 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
 }
 
-// Direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane l copies the 16
-// bytes at global address base + voff (base wave-uniform, in SGPRs; voff the
-// lane's 32-bit byte offset) to LDS byte address lds_base + 16*l; lds_base is
-// wave-uniform and travels in M0. Issued as inline assembly so the compiler
-// does not make later LDS reads of the other ring tile wait for it; completion
-// is tracked by the explicit vmcnt wait before each barrier.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_base) {
-    __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                         :: "s"(lds_base), "v"(voff), "s"(base) : "memory");
-}
-
-// The same copy as a raw-buffer load: the latent is a buffer resource (base,
-// no stride, its size in bytes), the row's byte offset is the scalar offset
-// and the lane's chunk offset the vector offset, so no 64-bit row address is
-// formed per row.
-__device__ __forceinline__ void lds_dma16_row(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-    __asm__ __volatile__("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                         :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base) : "memory");
+// Direct-to-LDS copy of one latent row (gfx950 buffer_load_dwordx4 ... lds): lane
+// l copies the 16 bytes at rsrc base + soff + voff + OFF to LDS byte M0 + OFF +
+// 16*l. The latent is a raw buffer resource, the row's byte offset the scalar
+// offset and the lane's chunk offset the vector offset, so no 64-bit address is
+// formed per row. The immediate OFF moves both the memory and the LDS address:
+// rows that share M0 (the LDS address of a group's first row, passed as an
+// operand so that the compiler writes M0 once per group) land OFF bytes above
+// it, and their scalar offsets carry -OFF. Issued as inline assembly so the
+// compiler does not make LDS reads of the other ring tile wait for it;
+// completion is tracked by the explicit vmcnt wait before each barrier.
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_row_at(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t m0) {
+    __asm__ __volatile__("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+                         :: "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -272,6 +268,12 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     {
         const int pad_end = (n_valid + MLA_TK - 1) / MLA_TK * MLA_TK;
         if (n_valid > 0 && tid < pad_end - n_valid) list[n_valid + tid] = list[0];
+        __syncthreads();
+        // entry p is loaded at immediate offset row_base(p % 4) within its group of
+        // four rows, through a descriptor based 4 KB below the latent (all offsets stay
+        // positive): the list holds byte offset + 4096 - row_base(p % 4)
+        for (int p = tid; p < pad_end; p += NT)
+            list[p] = (int32_t)((uint32_t)list[p] + 4096u - (uint32_t)row_base<RB>(p & 3));
     }
     __syncthreads();
 
@@ -290,13 +292,16 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
     const uint32_t wave_lds = ring_lds + (uint32_t)row_base<RB>(RPW * wave_s);   // LDS row 16w of buffer 0
     const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row
-    // the latent as a raw buffer: base (48 bits), stride 0, num_kv * D * 2 bytes
-    // (below 4 GiB), and the default dword format of gfx9 buffer descriptors
+    // the latent as a raw buffer: base (48 bits) 4 KiB below the latent, so that the
+    // adjusted scalar offsets of the list stay positive; stride 0; num_kv * D * 2
+    // + 4 KiB bytes (at most 4 GiB); the default dword format of gfx9 descriptors
     const uint64_t kv_addr = reinterpret_cast<uint64_t>(kv);
-    const u32x4 kv_rsrc = u32x4{(uint32_t)kv_addr, (uint32_t)(kv_addr >> 32) & 0xFFFFu,
-                                (uint32_t)((uint64_t)num_kv * (D * 2)), 0x00020000u};
-    // KP_ROWS_OF reads the byte offsets of this wave's 16 rows of tile kt_ into rws_[16];
-    // KP_ISSUE_ROW(j_) issues the gather of the wave's row j_ into buffer buf_
+    const uint64_t kv_base = kv_addr - 4096u;
+    const u32x4 kv_rsrc = u32x4{(uint32_t)kv_base, (uint32_t)(kv_base >> 32) & 0xFFFFu,
+                                (uint32_t)((uint64_t)num_kv * (D * 2) + 4096u), 0x00020000u};
+    // KP_ROWS_OF reads the (adjusted) byte offsets of this wave's 16 rows of tile kt_
+    // into rws_[16]; KP_ISSUE_ROW(j_) issues the gather of the wave's row j_ into
+    // buffer buf_ (rows 4m .. 4m+3 share M0)
 #define KP_ROWS_OF(kt_)                                                                        \
     int rws_[RPW];   /* wave-uniform: scalar registers */                                      \
     _Pragma("unroll") for (int c4_ = 0; c4_ < RPW / 4; ++c4_) {                                \
@@ -306,17 +311,21 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         rws_[4 * c4_ + 2] = __builtin_amdgcn_readfirstlane(rw_.z);                             \
         rws_[4 * c4_ + 3] = __builtin_amdgcn_readfirstlane(rw_.w);                             \
     }
-#define KP_ISSUE_ROW(j_, buf_)                                                                 \
+#define KP_ISSUE_ROW(j_, buf_)                                                                \
     {                                                                                          \
-        /* (row 16w + j_ starts at row_base(16w) + row_base(j_): 16w is even) */               \
-        if (DP == D || lane < CH)                                                              \
-            lds_dma16_row(kv_rsrc, lane16, (uint32_t)rws_[j_],                                 \
-                          __builtin_amdgcn_readfirstlane(wave_lds + (uint32_t)((buf_) * TILE_B + row_base<RB>(j_)))); \
+        if (DP == D || lane < CH) {                                                            \
+            const uint32_t m0_ = __builtin_amdgcn_readfirstlane(                                \
+                wave_lds + (uint32_t)((buf_) * TILE_B + row_base<RB>((j_) & ~3)));              \
+            if (((j_) & 3) == 0) lds_dma16_row_at<0>(kv_rsrc, lane16, (uint32_t)rws_[j_], m0_);  \
+            else if (((j_) & 3) == 1) lds_dma16_row_at<row_base<RB>(1)>(kv_rsrc, lane16, (uint32_t)rws_[j_], m0_); \
+            else if (((j_) & 3) == 2) lds_dma16_row_at<row_base<RB>(2)>(kv_rsrc, lane16, (uint32_t)rws_[j_], m0_); \
+            else lds_dma16_row_at<row_base<RB>(3)>(kv_rsrc, lane16, (uint32_t)rws_[j_], m0_);    \
+        }                                                                                      \
     }
 #define KP_ISSUE_TILE(kt_, buf_)                                                               \
     {                                                                                          \
         KP_ROWS_OF(kt_)                                                                        \
-        _Pragma("unroll") for (int j = 0; j < RPW; ++j) KP_ISSUE_ROW(j, buf_)                  \
+        _Pragma("unroll") for (int j = 0; j < RPW; ++j) KP_ISSUE_ROW(j, buf_)                 \
     }
 
     // O^T accumulators: o[ct][ht] holds columns 16*ct + 4*g + e of head 32*hh + 16*ht + n
@@ -419,7 +428,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             sacc_[1][0] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][1], qf[0][c], sacc_[1][0]);    \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             _Pragma("unroll") for (int j = c * RPW / KS; j < (c + 1) * RPW / KS; ++j)          \
-                KP_ISSUE_ROW(j, buf_ ^ 1)                                                      \
+                KP_ISSUE_ROW(j, buf_ ^ 1)                                                     \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             sacc_[1][1] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][1], qf[1][c], sacc_[1][1]);    \
         }                                                                                      \

@@ -86,6 +86,9 @@ def test_invalid_args_rejected_on_host(L):
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 65, 512, 128, C.c_float(0.1), fake, None, None) == 2
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, None, None) == 2
     assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 1
+    # a latent of more than 4 GiB - 4 KiB (the row loads address it from 4 KiB below)
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 1 << 22, 64, 512, 128, C.c_float(0.1), fake, None, None) == 2
+    assert b"4 GiB" in L.kp_last_error()
     # index rows wider than the attention's LDS list
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 4097, C.c_float(0.1), fake, None, None) == 2
     assert b"row_width" in L.kp_last_error()
