@@ -93,6 +93,15 @@ __device__ __forceinline__ void lds_dma16_row_at(u32x4 rsrc, uint32_t voff, uint
                          :: "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF), "{m0}"(m0) : "memory");
 }
 
+// Five wait states after VALU writes (v_readfirstlane) of these 16 scalar
+// registers, which vector-memory instructions read next (gfx9 needs five).
+__device__ __forceinline__ void kp_sgpr_settle(int (&r)[16]) {
+    __asm__ __volatile__("s_nop 4"
+                         : "+s"(r[0]), "+s"(r[1]), "+s"(r[2]), "+s"(r[3]), "+s"(r[4]), "+s"(r[5]), "+s"(r[6]),
+                           "+s"(r[7]), "+s"(r[8]), "+s"(r[9]), "+s"(r[10]), "+s"(r[11]), "+s"(r[12]),
+                           "+s"(r[13]), "+s"(r[14]), "+s"(r[15]));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)((KP_LDS const uint8_t*)p);
 }
@@ -310,7 +319,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         rws_[4 * c4_ + 1] = __builtin_amdgcn_readfirstlane(rw_.y);                             \
         rws_[4 * c4_ + 2] = __builtin_amdgcn_readfirstlane(rw_.z);                             \
         rws_[4 * c4_ + 3] = __builtin_amdgcn_readfirstlane(rw_.w);                             \
-    }
+    }                                                                                          \
+    /* the row loads read these scalar registers, which v_readfirstlane (VALU) wrote: */      \
+    /* five wait states here, and the values are opaque from here on, so no later */          \
+    /* VALU write can land closer to a load */                                                 \
+    kp_sgpr_settle(rws_);
 #define KP_ISSUE_ROW(j_, buf_)                                                                \
     {                                                                                          \
         if (DP == D || lane < CH) {                                                            \

@@ -1,4 +1,4 @@
-"""Wait states in front of the attention kernel's inline-assembly MFMAs.
+"""Wait states around the attention kernel's inline assembly.
 
 The compiler inserts the wait states an MFMA needs after a VALU write of one
 of its operands only for MFMAs it generates itself; the PV MFMAs of the
@@ -12,7 +12,9 @@ than RESULT_WAIT wait states after it (each instruction issued in between is
 one wait state, s_nop N is N + 1). The scan follows the instructions in the
 order they are laid out, which is how straight-line code and the fall-through
 of a branch issue; it does not cross an unconditional branch (what follows one
-in the layout is reached only by jumps).
+in the layout is reached only by jumps). The same scan checks the row loads
+(inline-assembly buffer loads into LDS): no VALU instruction may write a scalar
+register they read fewer than SGPR_WAIT wait states before them.
 """
 import os
 import re
@@ -26,6 +28,19 @@ SRC = os.path.join(ROOT, "sparse_attention_kpool_amd", "csrc", "sparse_mla.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 MIN_WAIT = 2       # VALU write of a VGPR/AGPR -> MFMA read of it (gfx950)
 RESULT_WAIT = 18   # MFMA result -> read or write by another instruction (16-pass bound)
+SGPR_WAIT = 5      # VALU write of an SGPR -> vector-memory read of it (gfx9)
+
+SREG = re.compile(r"\bs(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def sregs(text):
+    out = set()
+    for m in SREG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
 
 REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)\b)")
 
@@ -150,3 +165,28 @@ def test_inline_mfma_results_left_alone_until_done(asm_lines):
             j += 1
     assert checked > 0, "no inline-assembly MFMA found"
     assert not bad, "inline-assembly MFMA result touched too soon:\n" + "\n".join(bad[:10])
+
+
+def test_row_load_sgprs_settled(asm_lines):
+    instrs = instructions(asm_lines)
+    loads = 0
+    bad = []
+    for k, (line, in_asm) in enumerate(instrs):
+        if not (in_asm and line.startswith("buffer_load") and line.endswith("lds")):
+            continue
+        loads += 1
+        read = sregs(line.split(None, 1)[1])
+        waits = 0
+        j = k - 1
+        while j >= 0 and waits < SGPR_WAIT:
+            prev = instrs[j][0]
+            if unconditional(prev):
+                break
+            parts = prev.split(None, 1)
+            if parts[0].startswith("v_") and len(parts) > 1 and sregs(parts[1].split(",")[0]) & read:
+                bad.append(f"{prev!r} then {line!r} ({waits} wait states)")
+                break
+            waits += wait_states(prev)
+            j -= 1
+    assert loads > 0, "no row load found"
+    assert not bad, "VALU write of an SGPR too close to a row load:\n" + "\n".join(bad[:10])
