@@ -14,7 +14,8 @@ order they are laid out, which is how straight-line code and the fall-through
 of a branch issue; it does not cross an unconditional branch (what follows one
 in the layout is reached only by jumps). The same scan checks the row loads
 (inline-assembly buffer loads into LDS): no VALU instruction may write a scalar
-register they read fewer than SGPR_WAIT wait states before them.
+register they read fewer than SGPR_WAIT wait states before them, and M0 may not
+be written right before them.
 """
 import os
 import re
@@ -29,6 +30,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 MIN_WAIT = 2       # VALU write of a VGPR/AGPR -> MFMA read of it (gfx950)
 RESULT_WAIT = 18   # MFMA result -> read or write by another instruction (16-pass bound)
 SGPR_WAIT = 5      # VALU write of an SGPR -> vector-memory read of it (gfx9)
+M0_WAIT = 1        # write of M0 -> a load into LDS that takes its address from it
 
 SREG = re.compile(r"\bs(?:\[(\d+):(\d+)\]|(\d+)\b)")
 
@@ -184,6 +186,10 @@ def test_row_load_sgprs_settled(asm_lines):
                 break
             parts = prev.split(None, 1)
             if parts[0].startswith("v_") and len(parts) > 1 and sregs(parts[1].split(",")[0]) & read:
+                bad.append(f"{prev!r} then {line!r} ({waits} wait states)")
+                break
+            # M0 (the LDS address) written by a scalar move right before the load
+            if waits < M0_WAIT and len(parts) > 1 and parts[1].split(",")[0].strip() == "m0":
                 bad.append(f"{prev!r} then {line!r} ({waits} wait states)")
                 break
             waits += wait_states(prev)
