@@ -49,6 +49,20 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------- rotate + quantise -----------
+// Butterfly stages across lanes at distances B, 2B, ... < L, in that order.
+template <int L, int B>
+__device__ __forceinline__ void fwht4_lanes(float (&x)[4], int lane) {
+    if constexpr (B < L) {
+        const bool upper = (lane & B) != 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float y = lane_xor<B>(x[e]);
+            x[e] = upper ? (y - x[e]) : (x[e] + y);
+        }
+        fwht4_lanes<L, 2 * B>(x, lane);
+    }
+}
+
 // x holds channels 4*j .. 4*j+3 of a vector of n = 4*L channels spread over L
 // consecutive lanes (j = lane % L). Orthonormal Walsh-Hadamard transform in
 // Sylvester order: stride 1, 2 in-lane, 4 .. n/2 across lanes; then one
@@ -57,15 +71,7 @@ template <int L>
 __device__ __forceinline__ void fwht4(float (&x)[4], int lane, float norm) {
     float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
     x[0] = a0 + a2; x[2] = a0 - a2; x[1] = a1 + a3; x[3] = a1 - a3;
-#pragma unroll
-    for (int b = 1; b < L; b <<= 1) {
-        const bool upper = (lane & b) != 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float y = shfl_xor(x[e], b);
-            x[e] = upper ? (y - x[e]) : (x[e] + y);
-        }
-    }
+    fwht4_lanes<L, 1>(x, lane);
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = x[e] * norm;
 }
@@ -170,23 +176,39 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
 
 // ---------------------------------------------------------- queries ---------
 // One (query, head) vector per L lanes: bf16 -> fp32 (exact), rotate, quantise.
-template <int L>
+// A block covers R groups of 256/L consecutive vectors and each lane loads its
+// R pieces before any shuffle, so R loads per lane are in flight at once (one
+// per lane leaves too few bytes in flight to cover HBM latency). Vectors past
+// `rows` are computed on zeros and not stored; every lane stays active for the
+// shuffles.
+template <int L, int R>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(const uint16_t* __restrict__ q_idx,
                                                            long long rows, float norm,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ scales) {
     constexpr int N = 4 * L;
+    constexpr int GROUP = 256 / L;   // vectors per block per step
     const int lane = threadIdx.x & 63;
     const int j = lane % L;
-    const long long r = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / L;
-    if (r >= rows) return;
-    uint2 q = reinterpret_cast<const uint2*>(q_idx + (size_t)r * N)[j];
-    float x[4] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y)};
-    fwht4<L>(x, lane, norm);
-    float sc;
-    uint32_t c = quant4<L>(x, &sc);
-    reinterpret_cast<uint32_t*>(codes + (size_t)r * N)[j] = c;
-    if (j == 0) scales[r] = sc;
+    const long long r0 = (long long)blockIdx.x * (GROUP * R) + threadIdx.x / L;
+    uint2 q[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const long long r = r0 + (long long)k * GROUP;
+        q[k] = r < rows ? reinterpret_cast<const uint2*>(q_idx + (size_t)r * N)[j] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const long long r = r0 + (long long)k * GROUP;
+        float x[4] = {bf16_lo(q[k].x), bf16_hi(q[k].x), bf16_lo(q[k].y), bf16_hi(q[k].y)};
+        fwht4<L>(x, lane, norm);
+        float sc;
+        uint32_t c = quant4<L>(x, &sc);
+        if (r < rows) {
+            reinterpret_cast<uint32_t*>(codes + (size_t)r * N)[j] = c;
+            if (j == 0) scales[r] = sc;
+        }
+    }
 }
 
 // ------------------------------------------------------------ launchers -----
@@ -247,13 +269,14 @@ hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, c
 hipError_t launch_rotate_quant(const uint16_t* q_idx, long long rows, int d_idx, float norm,
                                uint8_t* codes, float* scales, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
+    constexpr int R = 4;
     const int L = d_idx / 4;
-    const long long threads = rows * L;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const long long per_block = (256 / L) * R;
+    const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
     switch (d_idx) {
-        case 32: rotate_quant_kernel<8><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
-        case 64: rotate_quant_kernel<16><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
-        default: rotate_quant_kernel<32><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
+        case 32: rotate_quant_kernel<8, R><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
+        case 64: rotate_quant_kernel<16, R><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
+        default: rotate_quant_kernel<32, R><<<blocks, 256, 0, stream>>>(q_idx, rows, norm, codes, scales); break;
     }
     return hipGetLastError();
 }

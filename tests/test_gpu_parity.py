@@ -131,6 +131,24 @@ def test_query_codes_bitexact(K, oracle_mod, name):
     assert np.array_equal(host(scales), qs)
 
 
+@pytest.mark.parametrize("tq,h,d", [(7, 3, 128), (5, 5, 64), (3, 7, 32), (1, 1, 128), (1001, 32, 128),
+                                    (333, 9, 64)])
+def test_query_codes_ragged(K, oracle_mod, tq, h, d):
+    """Vector counts that leave the last block of the rotation partly filled,
+    for each supported width, with one all-zero vector (scale 1, zero codes)."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(1000 + tq * 31 + h * 7 + d)
+    x = rng.standard_normal((tq, h, d)).astype(np.float32) * 3.0
+    x[tq // 2, h // 2] = 0.0
+    q_idx = f32_to_bf16_bits(x)
+    _log("query codes ragged", (tq, h, d))
+    codes, scales = K.indexer_rotate_quant(dev_bf16(q_idx))
+    qc, qs = oracle_mod.queries(q_idx)
+    assert np.array_equal(host(codes), qc)
+    assert np.array_equal(host(scales), qs)
+    assert qs[tq // 2, h // 2] == 1.0
+
+
 # ---------------------------------------------------------------- scoring ----
 def _oracle_keys(oracle_mod, s, wl):
     cp, ps = oracle_mod.layout(s.cu, s.T, s.kpool)
