@@ -227,7 +227,7 @@ kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, 
  *   kv       device bf16 [num_kv, d_latent]
  *   indices  device int32 [num_q, row_width]
  *   heads    1 .. 64;  d_latent 64 or 512;  row_width 1 .. 4096;
- *            num_kv * d_latent * 2 <= 4 GiB - 4 KiB;  softmax_scale finite and > 0
+ *            num_kv * d_latent * 2 < 4 GiB - 4 KiB;  softmax_scale finite and > 0
  *   out      device bf16 [num_q, heads, d_latent]   (out)
  *   lse      device fp32 [num_q, heads]             (out, NULLABLE)
  */

@@ -76,17 +76,38 @@ def _stream(dev: torch.device):
     return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+def _need(t: torch.Tensor, name: str, dtype, shape) -> None:
+    """dtype, rank and shape of one tensor argument (``shape`` holds None for a
+    dimension checked elsewhere); devices and contiguity are checked by _on."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != len(shape):
+        raise ValueError(f"{name} must have {len(shape)} dims, got shape {tuple(t.shape)}")
+    for got, want in zip(t.shape, shape):
+        if want is not None and got != want:
+            want_s = tuple("*" if w is None else w for w in shape)
+            raise ValueError(f"{name} must have shape {want_s}, got {tuple(t.shape)}")
+
+
+def _on(*named) -> torch.device:
+    """Every (name, tensor) pair (None tensors skipped) is a contiguous tensor on
+    one and the same GPU; returns that device. Runs after the shape checks, so a
+    shape mismatch is reported whatever the device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return dev
 
 
 # ------------------------------------------------------------------ helpers ---
@@ -107,15 +128,13 @@ def kpool_build(cu_seqlens: torch.Tensor, k_idx: torch.Tensor, gate: torch.Tenso
                 kpool: int = 4, with_f32: bool = False):
     """Pool layout and rotated FP8 pooled keys.
     Returns (cu_pools, pool_start, pooled_k_fp8, pooled_k_scale, pooled_k_f32 or None)."""
-    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
-    _need(k_idx, "k_idx", torch.bfloat16, 2)
-    _need(gate, "gate", torch.bfloat16, 2)
-    _need(ape, "ape", torch.float32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    _need(k_idx, "k_idx", torch.bfloat16, (None, None))
     T, d = k_idx.shape
-    if gate.shape != k_idx.shape or ape.shape != (kpool, d):
-        raise ValueError("gate must match k_idx and ape must be [kpool, d_idx]")
+    _need(gate, "gate", torch.bfloat16, (T, d))
+    _need(ape, "ape", torch.float32, (kpool, d))
     B = cu_seqlens.shape[0] - 1
-    dev = k_idx.device
+    dev = _on(("cu_seqlens", cu_seqlens), ("k_idx", k_idx), ("gate", gate), ("ape", ape))
     cap = T // kpool
     cu_pools = torch.empty(B + 1, dtype=torch.int32, device=dev)
     pool_start = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)[:cap]
@@ -133,19 +152,22 @@ def kpool_build_from(cu_seqlens: torch.Tensor, k_idx: torch.Tensor, gate: torch.
     (cu_pools, pool_start, pooled_k_fp8, pooled_k_scale, pooled_k_f32 or None),
     the tensors of an earlier kpool_build over the same documents (the pooled-key
     cache); the rows of pools ending before token_lo are left as they are."""
-    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
-    _need(k_idx, "k_idx", torch.bfloat16, 2)
-    _need(gate, "gate", torch.bfloat16, 2)
-    _need(ape, "ape", torch.float32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    _need(k_idx, "k_idx", torch.bfloat16, (None, None))
     T, d = k_idx.shape
-    if gate.shape != k_idx.shape or ape.shape != (kpool, d):
-        raise ValueError("gate must match k_idx and ape must be [kpool, d_idx]")
+    _need(gate, "gate", torch.bfloat16, (T, d))
+    _need(ape, "ape", torch.float32, (kpool, d))
     B = cu_seqlens.shape[0] - 1
     cap = T // kpool
     cu_pools, pool_start, k8, ks, kf = out
-    if (cu_pools.shape != (B + 1,) or pool_start.shape != (cap,) or k8.shape != (cap, d) or ks.shape != (cap,)
-            or (kf is not None and kf.shape != (cap, d))):
-        raise ValueError("out must hold the outputs of kpool_build for these sizes")
+    _need(cu_pools, "cu_pools", torch.int32, (B + 1,))
+    _need(pool_start, "pool_start", torch.int32, (cap,))
+    _need(k8, "pooled_k_fp8", torch.uint8, (cap, d))
+    _need(ks, "pooled_k_scale", torch.float32, (cap,))
+    if kf is not None:
+        _need(kf, "pooled_k_f32", torch.float32, (cap, d))
+    _on(("cu_seqlens", cu_seqlens), ("k_idx", k_idx), ("gate", gate), ("ape", ape), ("cu_pools", cu_pools),
+        ("pool_start", pool_start), ("pooled_k_fp8", k8), ("pooled_k_scale", ks), ("pooled_k_f32", kf))
     _check(lib().kpool_build_from(_ptr(cu_seqlens), B, T, _ptr(k_idx), _ptr(gate), _ptr(ape), d, kpool,
                                   int(token_lo), _ptr(cu_pools), _ptr(pool_start), _ptr(k8), _ptr(ks), _ptr(kf),
                                   _stream(k_idx.device)))
@@ -153,7 +175,8 @@ def kpool_build_from(cu_seqlens: torch.Tensor, k_idx: torch.Tensor, gate: torch.
 
 def indexer_rotate_quant(q_idx: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """Rotated FP8 indexer queries: (codes uint8 [Tq,H_I,D_I], scales f32 [Tq,H_I])."""
-    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(q_idx, "q_idx", torch.bfloat16, (None, None, None))
+    _on(("q_idx", q_idx))
     Tq, h, d = q_idx.shape
     codes = torch.empty((Tq, h, d), dtype=torch.uint8, device=q_idx.device)
     scales = torch.empty((Tq, h), dtype=torch.float32, device=q_idx.device)
@@ -168,17 +191,24 @@ def indexer_score_topk(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, pooled_
                        return_scores: bool = False, workspace: Optional[torch.Tensor] = None):
     """FP8 indexer scoring and top-k index rows.
     Returns (indices int32 [Tq,W], num_valid int32 [Tq], scores f32 [Tq,max_pools] or None)."""
-    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
-    _need(cu_pools, "cu_pools", torch.int32, 1)
-    _need(pooled_k_fp8, "pooled_k_fp8", torch.uint8, 2)
-    _need(pooled_k_scale, "pooled_k_scale", torch.float32, 1)
-    _need(q_idx, "q_idx", torch.bfloat16, 3)
-    _need(w_idx, "w_idx", torch.float32, 2)
-    if q_pos is not None:
-        _need(q_pos, "q_pos", torch.int32, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    B = cu_seqlens.shape[0] - 1
+    _need(q_idx, "q_idx", torch.bfloat16, (None, None, None))
     Tq, h, d = q_idx.shape
-    dev = q_idx.device
     max_pools = num_tokens // kpool
+    _need(cu_pools, "cu_pools", torch.int32, (B + 1,))
+    _need(pooled_k_fp8, "pooled_k_fp8", torch.uint8, (max_pools, d))
+    _need(pooled_k_scale, "pooled_k_scale", torch.float32, (max_pools,))
+    _need(w_idx, "w_idx", torch.float32, (Tq, h))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (Tq,))
+    elif Tq != num_tokens:
+        raise ValueError(f"without q_pos every token is a query: q_idx must have {num_tokens} rows, got {Tq}")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, (None,))
+    dev = _on(("cu_seqlens", cu_seqlens), ("cu_pools", cu_pools), ("pooled_k_fp8", pooled_k_fp8),
+              ("pooled_k_scale", pooled_k_scale), ("q_idx", q_idx), ("w_idx", w_idx), ("q_pos", q_pos),
+              ("workspace", workspace))
     W = row_width if row_width is not None else kp_row_width(kpool, topk_pools)
     indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
     num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
@@ -198,13 +228,16 @@ def indexer_topk_from_scores(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, s
                              num_tokens: int, kpool: int = 4, topk_pools: int = 512,
                              row_width: Optional[int] = None, q_pos: Optional[torch.Tensor] = None):
     """Top-k index rows of a given score tensor [Tq, num_tokens // kpool]."""
-    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
-    _need(cu_pools, "cu_pools", torch.int32, 1)
-    _need(scores, "scores", torch.float32, 2)
-    if q_pos is not None:
-        _need(q_pos, "q_pos", torch.int32, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    B = cu_seqlens.shape[0] - 1
+    _need(cu_pools, "cu_pools", torch.int32, (B + 1,))
+    _need(scores, "scores", torch.float32, (None, num_tokens // kpool))
     Tq, max_pools = scores.shape
-    dev = scores.device
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (Tq,))
+    elif Tq != num_tokens:
+        raise ValueError(f"without q_pos every token is a query: scores must have {num_tokens} rows, got {Tq}")
+    dev = _on(("cu_seqlens", cu_seqlens), ("cu_pools", cu_pools), ("scores", scores), ("q_pos", q_pos))
     W = row_width if row_width is not None else kp_row_width(kpool, topk_pools)
     indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
     num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
@@ -217,17 +250,15 @@ def indexer_topk_from_scores(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, s
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, softmax_scale: float,
                    return_lse: bool = True, out: Optional[torch.Tensor] = None):
     """Absorbed sparse latent attention: (out bf16 [Tq,H,D], lse f32 [Tq,H] or None)."""
-    _need(q, "q", torch.bfloat16, 3)
-    _need(kv, "kv", torch.bfloat16, 2)
-    _need(indices, "indices", torch.int32, 2)
+    _need(q, "q", torch.bfloat16, (None, None, None))
     Tq, H, D = q.shape
-    if kv.shape[1] != D or indices.shape[0] != Tq:
-        raise ValueError("kv must be [num_kv, d_latent] and indices [num_q, row_width]")
-    dev = q.device
+    _need(kv, "kv", torch.bfloat16, (None, D))
+    _need(indices, "indices", torch.int32, (Tq, None))
+    if out is not None:
+        _need(out, "out", torch.bfloat16, (Tq, H, D))
+    dev = _on(("q", q), ("kv", kv), ("indices", indices), ("out", out))
     if out is None:
         out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
-    else:
-        _need(out, "out", torch.bfloat16, 3)
     lse = torch.empty((Tq, H), dtype=torch.float32, device=dev) if return_lse else None
     _check(lib().sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), Tq, kv.shape[0], H, D, indices.shape[1],
                                 float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev)))
@@ -235,7 +266,10 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sof
 
 
 def kp_check_inputs(cu_seqlens: torch.Tensor, num_tokens: int, q_pos: Optional[torch.Tensor] = None) -> None:
-    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (None,))
+    _on(("cu_seqlens", cu_seqlens), ("q_pos", q_pos))
     nq = 0 if q_pos is None else q_pos.shape[0]
     _check(lib().kp_check_inputs(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, num_tokens, _ptr(q_pos), nq,
                                  _stream(cu_seqlens.device)))

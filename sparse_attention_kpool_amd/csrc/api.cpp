@@ -238,8 +238,10 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
         return fail(KP_ERR_UNSUPPORTED, "row_width above %d (got %d)", kp::sparse_mla_max_row_width(), row_width);
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
         return fail(KP_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
-    if ((uint64_t)num_kv * (uint64_t)d_latent * 2u + 4096u > (1ull << 32))
-        return fail(KP_ERR_UNSUPPORTED, "latent of %d rows x %d exceeds 4 GiB - 4 KiB", num_kv, d_latent);
+    // the row loads address the latent through a buffer descriptor based 4 KiB below
+    // it, whose 32-bit record count must hold the latent's bytes plus those 4 KiB
+    if ((uint64_t)num_kv * (uint64_t)d_latent * 2u + 4096u > 0xFFFFFFFFull)
+        return fail(KP_ERR_UNSUPPORTED, "latent of %d rows x %d is not below 4 GiB - 4 KiB", num_kv, d_latent);
     if (num_q == 0) return ok();
     if (!q || !indices || !out || (num_kv > 0 && !kv))
         return fail(KP_ERR_INVALID_ARG, "q, kv, indices and out are required");

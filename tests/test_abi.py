@@ -89,6 +89,11 @@ def test_invalid_args_rejected_on_host(L):
     # a latent of more than 4 GiB - 4 KiB (the row loads address it from 4 KiB below)
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 1 << 22, 64, 512, 128, C.c_float(0.1), fake, None, None) == 2
     assert b"4 GiB" in L.kp_last_error()
+    # the boundary: 4,194,300 rows of 1 KiB are exactly 4 GiB - 4 KiB (the descriptor's
+    # record count would wrap to 0), one row fewer fits (checked with no queries: no launch)
+    edge = ((1 << 32) - 4096) // 1024
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, edge, 64, 512, 128, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, edge - 1, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
     # index rows wider than the attention's LDS list
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 4097, C.c_float(0.1), fake, None, None) == 2
     assert b"row_width" in L.kp_last_error()

@@ -14,8 +14,8 @@ order they are laid out, which is how straight-line code and the fall-through
 of a branch issue; it does not cross an unconditional branch (what follows one
 in the layout is reached only by jumps). The same scan checks the row loads
 (inline-assembly buffer loads into LDS): no VALU instruction may write a scalar
-register they read fewer than SGPR_WAIT wait states before them, and M0 may not
-be written right before them.
+register they read, M0 included, fewer than SGPR_WAIT wait states before them,
+and a scalar write of M0 may not come right before them.
 """
 import os
 import re
@@ -33,15 +33,19 @@ SGPR_WAIT = 5      # VALU write of an SGPR -> vector-memory read of it (gfx9)
 M0_WAIT = 1        # write of M0 -> a load into LDS that takes its address from it
 
 SREG = re.compile(r"\bs(?:\[(\d+):(\d+)\]|(\d+)\b)")
+M0 = re.compile(r"\bm0\b")
 
 
 def sregs(text):
+    """Scalar registers named in an operand string: SGPR numbers, and "m0"."""
     out = set()
     for m in SREG.finditer(text):
         if m.group(3) is not None:
             out.add(int(m.group(3)))
         else:
             out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    if M0.search(text):
+        out.add("m0")
     return out
 
 REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)\b)")
@@ -177,7 +181,8 @@ def test_row_load_sgprs_settled(asm_lines):
         if not (in_asm and line.startswith("buffer_load") and line.endswith("lds")):
             continue
         loads += 1
-        read = sregs(line.split(None, 1)[1])
+        # the SGPRs the load names, and M0 (the LDS address it writes to)
+        read = sregs(line.split(None, 1)[1]) | {"m0"}
         waits = 0
         j = k - 1
         while j >= 0 and waits < SGPR_WAIT:
