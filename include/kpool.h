@@ -197,6 +197,32 @@ kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * indexer_score_topk_noalloc -- indexer_score_topk for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): the same arguments without the workspace,
+ * and the same outputs, bit for bit. Its workspace is a device buffer the
+ * library holds, KP_NOALLOC_SCRATCH_BYTES on each GPU it runs on, from the
+ * library's load until the process ends; the call itself allocates nothing.
+ * Sizes whose workspace (kp_indexer_workspace_bytes) exceeds that return
+ * KP_ERR_UNSUPPORTED before anything is launched: the 64 decode queries of a
+ * 1,048,576-token context fit (64.3 MiB). Every call on one GPU shares that
+ * GPU's buffer, which keeps the last call's contents (no byte of it needs to
+ * start at zero): calls that overlap on one GPU (on different streams, or
+ * from different host threads) race and give undefined results; calls in one
+ * stream are ordered and safe.
+ */
+#define KP_NOALLOC_SCRATCH_BYTES (72u << 20)
+kp_status indexer_score_topk_noalloc(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                     const int32_t* cu_pools, int32_t max_pools,
+                                     const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
+                                     const int32_t* q_pos, int32_t num_q,
+                                     const uint16_t* q_idx, const float* w_idx,
+                                     int32_t h_idx, int32_t d_idx, int32_t kpool,
+                                     int32_t topk_pools, int32_t row_width,
+                                     int32_t* indices, int32_t* num_valid, float* scores,
+                                     hipStream_t stream);
+
+/*
  * indexer_topk_from_scores -- the selection step alone, on a given score
  * tensor [P4-S3]: the same index rows indexer_score_topk builds, with
  * scores[i, p] read for the visible pools only (other entries are ignored).

@@ -32,6 +32,8 @@ SIGNATURES = [
     ("kp_indexer_workspace_bytes", _Z, [_I, _I, _I, _I]),
     ("indexer_score_topk", _I, [_P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                 _P, _P, _P, _P, _Z, _P]),
+    ("indexer_score_topk_noalloc", _I, [_P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                        _P, _P, _P, _P]),
     ("indexer_topk_from_scores", _I, [_P, _I, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
     ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     ("kp_check_inputs", _I, [_P, _I, _I, _P, _I, _P]),
@@ -221,6 +223,49 @@ def indexer_score_topk(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, pooled_
                                     _ptr(q_idx), _ptr(w_idx), h, d, kpool, topk_pools, W, _ptr(indices),
                                     _ptr(num_valid), _ptr(scores), _ptr(workspace), workspace.numel(),
                                     _stream(dev)))
+    return indices, num_valid, scores
+
+
+def indexer_score_topk_noalloc(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, pooled_k_fp8: torch.Tensor,
+                               pooled_k_scale: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,
+                               num_tokens: int, kpool: int = 4, topk_pools: int = 512,
+                               row_width: Optional[int] = None, q_pos: Optional[torch.Tensor] = None,
+                               out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                               return_scores: bool = False):
+    """indexer_score_topk with the library's own device scratch as its workspace
+    (no workspace argument). ``out`` = (indices, num_valid) to write into
+    caller tensors (e.g. inside graph capture, where this call allocates
+    nothing). Returns (indices, num_valid, scores or None)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    B = cu_seqlens.shape[0] - 1
+    _need(q_idx, "q_idx", torch.bfloat16, (None, None, None))
+    Tq, h, d = q_idx.shape
+    max_pools = num_tokens // kpool
+    _need(cu_pools, "cu_pools", torch.int32, (B + 1,))
+    _need(pooled_k_fp8, "pooled_k_fp8", torch.uint8, (max_pools, d))
+    _need(pooled_k_scale, "pooled_k_scale", torch.float32, (max_pools,))
+    _need(w_idx, "w_idx", torch.float32, (Tq, h))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (Tq,))
+    elif Tq != num_tokens:
+        raise ValueError(f"without q_pos every token is a query: q_idx must have {num_tokens} rows, got {Tq}")
+    W = row_width if row_width is not None else kp_row_width(kpool, topk_pools)
+    if out is not None:
+        _need(out[0], "indices", torch.int32, (Tq, W))
+        _need(out[1], "num_valid", torch.int32, (Tq,))
+    dev = _on(("cu_seqlens", cu_seqlens), ("cu_pools", cu_pools), ("pooled_k_fp8", pooled_k_fp8),
+              ("pooled_k_scale", pooled_k_scale), ("q_idx", q_idx), ("w_idx", w_idx), ("q_pos", q_pos),
+              ("indices", None if out is None else out[0]), ("num_valid", None if out is None else out[1]))
+    if out is None:
+        indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
+        num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
+    else:
+        indices, num_valid = out
+    scores = torch.empty((Tq, max_pools), dtype=torch.float32, device=dev) if return_scores else None
+    _check(lib().indexer_score_topk_noalloc(_ptr(cu_seqlens), B, num_tokens, _ptr(cu_pools), max_pools,
+                                            _ptr(pooled_k_fp8), _ptr(pooled_k_scale), _ptr(q_pos), Tq,
+                                            _ptr(q_idx), _ptr(w_idx), h, d, kpool, topk_pools, W, _ptr(indices),
+                                            _ptr(num_valid), _ptr(scores), _stream(dev)))
     return indices, num_valid, scores
 
 

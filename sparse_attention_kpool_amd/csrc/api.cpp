@@ -158,33 +158,34 @@ static kp_status check_topk_args(const int32_t* cu_seqlens, int32_t num_docs, in
     return KP_OK;
 }
 
-kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
-                             const int32_t* cu_pools, int32_t max_pools,
-                             const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
-                             const int32_t* q_pos, int32_t num_q,
-                             const uint16_t* q_idx, const float* w_idx,
-                             int32_t h_idx, int32_t d_idx, int32_t kpool,
-                             int32_t topk_pools, int32_t row_width,
-                             int32_t* indices, int32_t* num_valid, float* scores,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    g_err.clear();
+// Argument checks of indexer_score_topk other than its workspace.
+static kp_status check_score_topk_args(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                       const int32_t* cu_pools, int32_t max_pools, const uint8_t* pooled_k_fp8,
+                                       const float* pooled_k_scale, const int32_t* q_pos, int32_t num_q,
+                                       const uint16_t* q_idx, const float* w_idx, int32_t h_idx, int32_t d_idx,
+                                       int32_t kpool, int32_t topk_pools, int32_t row_width,
+                                       const int32_t* indices) {
     kp_status st = check_topk_args(cu_seqlens, num_docs, num_tokens, cu_pools, max_pools, q_pos, num_q, kpool,
                                    topk_pools, row_width, indices);
     if (st != KP_OK) return st;
     if (h_idx < 1 || h_idx > 64) return fail(KP_ERR_UNSUPPORTED, "h_idx must be in 1..64 (got %d)", h_idx);
     if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
-    if (num_q == 0) return ok();
+    if (num_q == 0) return KP_OK;
     if (!q_idx || !w_idx) return fail(KP_ERR_INVALID_ARG, "q_idx and w_idx are required");
     if (max_pools > 0 && (!pooled_k_fp8 || !pooled_k_scale))
         return fail(KP_ERR_INVALID_ARG, "pooled_k_fp8 and pooled_k_scale are required");
-    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx);
-    if (!workspace || workspace_bytes < need)
-        return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
-    if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    st = device_check();
-    if (st != KP_OK) return st;
+    return KP_OK;
+}
 
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+// The launches of indexer_score_topk on a checked workspace of at least
+// kp_indexer_workspace_bytes bytes (none of it needs clearing: every byte a
+// kernel reads was written by an earlier kernel of the same call).
+static kp_status score_topk_launch(const int32_t* cu_seqlens, int32_t num_docs, const int32_t* cu_pools,
+                                   int32_t max_pools, const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
+                                   const int32_t* q_pos, int32_t num_q, const uint16_t* q_idx, const float* w_idx,
+                                   int32_t h_idx, int32_t d_idx, int32_t kpool, int32_t topk_pools,
+                                   int32_t row_width, int32_t* indices, int32_t* num_valid, float* scores,
+                                   uint8_t* ws, hipStream_t stream) {
     uint8_t* q8 = ws;
     float* sq = reinterpret_cast<float*>(ws + align256((size_t)num_q * h_idx * d_idx));
     float* sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4));
@@ -203,7 +204,99 @@ kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_
     e = kp::launch_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, sc, max_pools, topk_pools, row_width,
                         indices, num_valid, stream);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
-    return ok();
+    return KP_OK;
+}
+
+kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                             const int32_t* cu_pools, int32_t max_pools,
+                             const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
+                             const int32_t* q_pos, int32_t num_q,
+                             const uint16_t* q_idx, const float* w_idx,
+                             int32_t h_idx, int32_t d_idx, int32_t kpool,
+                             int32_t topk_pools, int32_t row_width,
+                             int32_t* indices, int32_t* num_valid, float* scores,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    kp_status st = check_score_topk_args(cu_seqlens, num_docs, num_tokens, cu_pools, max_pools, pooled_k_fp8,
+                                         pooled_k_scale, q_pos, num_q, q_idx, w_idx, h_idx, d_idx, kpool,
+                                         topk_pools, row_width, indices);
+    if (st != KP_OK) return st;
+    if (num_q == 0) return ok();
+    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx);
+    if (!workspace || workspace_bytes < need)
+        return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    st = device_check();
+    if (st != KP_OK) return st;
+    return score_topk_launch(cu_seqlens, num_docs, cu_pools, max_pools, pooled_k_fp8, pooled_k_scale, q_pos,
+                             num_q, q_idx, w_idx, h_idx, d_idx, kpool, topk_pools, row_width, indices, num_valid,
+                             scores, static_cast<uint8_t*>(workspace), stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free variant ---------------------------------------------
+// Its workspace is this file-scope device array: each GPU the library runs on
+// holds one copy, at its own address, from the code object's load until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host the name stands for a host-side shadow, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[KP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // device address of `scratch` on each device (null until looked up)
+
+kp_status scratch_address(uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(KP_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(KP_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+    return KP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kp_status indexer_score_topk_noalloc(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                     const int32_t* cu_pools, int32_t max_pools,
+                                     const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
+                                     const int32_t* q_pos, int32_t num_q,
+                                     const uint16_t* q_idx, const float* w_idx,
+                                     int32_t h_idx, int32_t d_idx, int32_t kpool,
+                                     int32_t topk_pools, int32_t row_width,
+                                     int32_t* indices, int32_t* num_valid, float* scores,
+                                     hipStream_t stream) {
+    g_err.clear();
+    kp_status st = check_score_topk_args(cu_seqlens, num_docs, num_tokens, cu_pools, max_pools, pooled_k_fp8,
+                                         pooled_k_scale, q_pos, num_q, q_idx, w_idx, h_idx, d_idx, kpool,
+                                         topk_pools, row_width, indices);
+    if (st != KP_OK) return st;
+    if (num_q == 0) return ok();
+    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx);
+    if (need > (size_t)KP_NOALLOC_SCRATCH_BYTES)
+        return fail(KP_ERR_UNSUPPORTED,
+                    "indexer_score_topk_noalloc: these sizes need %zu bytes of workspace, above the library's "
+                    "%zu-byte device scratch (use indexer_score_topk with a caller workspace)",
+                    need, (size_t)KP_NOALLOC_SCRATCH_BYTES);
+    st = device_check();
+    if (st != KP_OK) return st;
+    uint8_t* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != KP_OK) return st;
+    return score_topk_launch(cu_seqlens, num_docs, cu_pools, max_pools, pooled_k_fp8, pooled_k_scale, q_pos,
+                             num_q, q_idx, w_idx, h_idx, d_idx, kpool, topk_pools, row_width, indices, num_valid,
+                             scores, ws, stream);
 }
 
 kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,

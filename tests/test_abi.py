@@ -100,5 +100,14 @@ def test_invalid_args_rejected_on_host(L):
     assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
     for bad in (0.0, -0.1, float("inf"), float("nan")):          # the softmax scale must be positive
         assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 128, C.c_float(bad), fake, None, None) == 1
+    # the allocation-free variant: argument checks as indexer_score_topk's, and sizes
+    # whose workspace exceeds the library's device scratch are refused before launch
+    nargs = lambda T, nq, qpos: (fake, 1, T, fake, T // 4, fake, fake, qpos, nq, fake, fake, 32, 128, 4, 512, 2176,
+                                 fake, None, None, None)
+    assert L.indexer_score_topk_noalloc(*nargs(4096, 0, None)) == 0           # empty shard
+    assert L.indexer_score_topk_noalloc(*nargs(4096, 10, None)) == 1          # q_pos NULL needs num_q == T
+    assert L.indexer_score_topk_noalloc(*nargs(32768, 32768, None)) == 2      # 32K: 671 MB of workspace
+    assert b"scratch" in L.kp_last_error()
+    assert L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128) <= 72 << 20     # 1M-token decode fits
     assert L.indexer_rotate_quant(fake, 4, 2, 48, fake, fake, None) == 2
     assert L.indexer_topk_from_scores(fake, 1, 64, fake, 16, None, 64, None, 4, 4, 128, fake, None, None) == 1
