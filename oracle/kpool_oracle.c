@@ -288,33 +288,35 @@ void kpo_topk(const int32_t* cu, int32_t num_docs, const int32_t* cu_pools, int3
 /* ------------------------------------------------------------ sparse MLA -- */
 
 /* Dense attention restricted to the named rows, in float64: the dense SDPA
- * reference path of [P1-AB] with the index row as its mask. */
-void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t num_q,
-                    int32_t num_kv, int32_t heads, int32_t d_latent, int32_t row_width,
-                    float scale, float* out, float* lse, float* out_abs) {
+ * reference path of [P1-AB] with the index row as its mask. Keys are the whole
+ * d_qk-wide latent rows; values are their first d_v columns (d_v == d_qk is the
+ * NoPE form of [P4-S2]; d_qk = 576, d_v = 512 the RoPE-tail contract of [P2-CL]). */
+void kpo_sparse_mla_dv(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t num_q,
+                       int32_t num_kv, int32_t heads, int32_t d_qk, int32_t d_v, int32_t row_width,
+                       float scale, float* out, float* lse, float* out_abs) {
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int32_t i = 0; i < num_q; ++i) {
         for (int32_t h = 0; h < heads; ++h) {
             const int32_t* row = indices + (int64_t)i * row_width;
-            const uint16_t* qh = q + ((int64_t)i * heads + h) * d_latent;
+            const uint16_t* qh = q + ((int64_t)i * heads + h) * d_qk;
             double* s = (double*)malloc(sizeof(double) * (size_t)row_width + 1);
-            double* o = (double*)calloc((size_t)d_latent, sizeof(double));
-            double* oa = (double*)calloc((size_t)d_latent, sizeof(double));
+            double* o = (double*)calloc((size_t)d_v, sizeof(double));
+            double* oa = (double*)calloc((size_t)d_v, sizeof(double));
             double m = -INFINITY;
             for (int32_t j = 0; j < row_width; ++j) {
                 int32_t r = row[j];
                 if (r < 0 || r >= num_kv) { s[j] = -INFINITY; continue; }
                 double dot = 0.0;
-                for (int32_t c = 0; c < d_latent; ++c)
-                    dot += bf16_value(qh[c]) * bf16_value(kv[(int64_t)r * d_latent + c]);
+                for (int32_t c = 0; c < d_qk; ++c)
+                    dot += bf16_value(qh[c]) * bf16_value(kv[(int64_t)r * d_qk + c]);
                 s[j] = (double)scale * dot;
                 if (s[j] > m) m = s[j];
             }
-            float* oh = out + ((int64_t)i * heads + h) * d_latent;
-            float* oah = out_abs ? out_abs + ((int64_t)i * heads + h) * d_latent : NULL;
+            float* oh = out + ((int64_t)i * heads + h) * d_v;
+            float* oah = out_abs ? out_abs + ((int64_t)i * heads + h) * d_v : NULL;
             if (m == -INFINITY) {
-                for (int32_t c = 0; c < d_latent; ++c) oh[c] = 0.0f;
-                if (oah) for (int32_t c = 0; c < d_latent; ++c) oah[c] = 0.0f;
+                for (int32_t c = 0; c < d_v; ++c) oh[c] = 0.0f;
+                if (oah) for (int32_t c = 0; c < d_v; ++c) oah[c] = 0.0f;
                 if (lse) lse[(int64_t)i * heads + h] = -INFINITY;
             } else {
                 double den = 0.0;
@@ -323,14 +325,14 @@ void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indice
                     if (r < 0 || r >= num_kv) continue;
                     double p = exp(s[j] - m);
                     den += p;
-                    for (int32_t c = 0; c < d_latent; ++c) {
-                        double v = bf16_value(kv[(int64_t)r * d_latent + c]);
+                    for (int32_t c = 0; c < d_v; ++c) {
+                        double v = bf16_value(kv[(int64_t)r * d_qk + c]);
                         o[c] += p * v;
                         oa[c] += p * fabs(v);
                     }
                 }
-                for (int32_t c = 0; c < d_latent; ++c) oh[c] = (float)(o[c] / den);
-                if (oah) for (int32_t c = 0; c < d_latent; ++c) oah[c] = (float)(oa[c] / den);
+                for (int32_t c = 0; c < d_v; ++c) oh[c] = (float)(o[c] / den);
+                if (oah) for (int32_t c = 0; c < d_v; ++c) oah[c] = (float)(oa[c] / den);
                 if (lse) lse[(int64_t)i * heads + h] = (float)(m + log(den));
             }
             free(s);
@@ -338,6 +340,112 @@ void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indice
             free(oa);
         }
     }
+}
+
+void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t num_q,
+                    int32_t num_kv, int32_t heads, int32_t d_latent, int32_t row_width,
+                    float scale, float* out, float* lse, float* out_abs) {
+    kpo_sparse_mla_dv(q, kv, indices, num_q, num_kv, heads, d_latent, d_latent, row_width, scale, out, lse,
+                      out_abs);
+}
+
+/* Gradients of kpo_sparse_mla_dv for a loss whose gradient with respect to the
+ * output is d_out (the training path of [P1-AB]: the sparse kernel's backward,
+ * with the indexer frozen and its index rows fixed [P4-S3]). For query i, head
+ * h and the valid entries j of its row (latent row r_j, key k_j = kv[r_j],
+ * value v_j = its first d_v columns):
+ *   p_j   = softmax_j(scale <q, k_j>)             (the forward's weights)
+ *   dp_j  = <d_out, v_j>,   delta = sum_j p_j dp_j
+ *   ds_j  = p_j (dp_j - delta)                    (the softmax's Jacobian)
+ *   dq    = scale sum_j ds_j k_j
+ *   dkv[r_j] += scale ds_j q  (all d_qk columns: the key)
+ *             + p_j d_out     (first d_v columns: the value)
+ * Repeated entries contribute once per occurrence; rows of queries with no valid
+ * entry contribute nothing and get dq = 0. float64 throughout; each thread
+ * accumulates its own copy of dkv, summed in thread order at the end. */
+void kpo_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const uint16_t* d_out,
+                        int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_qk, int32_t d_v,
+                        int32_t row_width, float scale, float* d_q, float* d_kv) {
+    int nt = 1;
+#ifdef _OPENMP
+    nt = omp_get_max_threads();
+#endif
+    const size_t kvn = (size_t)num_kv * (size_t)d_qk;
+    double* part = (double*)calloc((size_t)nt * kvn + 1, sizeof(double));
+#pragma omp parallel
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double* acc = part + (size_t)tid * kvn;
+        double* p = (double*)malloc(sizeof(double) * (size_t)row_width + 1);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)row_width + 1);
+        double* dq = (double*)malloc(sizeof(double) * (size_t)d_qk + 1);
+#pragma omp for collapse(2) schedule(dynamic, 1)
+        for (int32_t i = 0; i < num_q; ++i) {
+            for (int32_t h = 0; h < heads; ++h) {
+                const int32_t* row = indices + (int64_t)i * row_width;
+                const uint16_t* qh = q + ((int64_t)i * heads + h) * d_qk;
+                const uint16_t* gh = d_out + ((int64_t)i * heads + h) * d_v;
+                double m = -INFINITY;
+                for (int32_t j = 0; j < row_width; ++j) {
+                    int32_t r = row[j];
+                    if (r < 0 || r >= num_kv) { p[j] = -INFINITY; continue; }
+                    double dot = 0.0;
+                    for (int32_t c = 0; c < d_qk; ++c)
+                        dot += bf16_value(qh[c]) * bf16_value(kv[(int64_t)r * d_qk + c]);
+                    p[j] = (double)scale * dot;
+                    if (p[j] > m) m = p[j];
+                }
+                float* dqo = d_q + ((int64_t)i * heads + h) * d_qk;
+                if (m == -INFINITY) {
+                    for (int32_t c = 0; c < d_qk; ++c) dqo[c] = 0.0f;
+                    continue;
+                }
+                double den = 0.0;
+                for (int32_t j = 0; j < row_width; ++j) {
+                    int32_t r = row[j];
+                    if (r < 0 || r >= num_kv) continue;
+                    p[j] = exp(p[j] - m);
+                    den += p[j];
+                }
+                double delta = 0.0;
+                for (int32_t j = 0; j < row_width; ++j) {
+                    int32_t r = row[j];
+                    if (r < 0 || r >= num_kv) continue;
+                    p[j] /= den;
+                    double d = 0.0;
+                    for (int32_t c = 0; c < d_v; ++c)
+                        d += bf16_value(gh[c]) * bf16_value(kv[(int64_t)r * d_qk + c]);
+                    dp[j] = d;
+                    delta += p[j] * d;
+                }
+                for (int32_t c = 0; c < d_qk; ++c) dq[c] = 0.0;
+                for (int32_t j = 0; j < row_width; ++j) {
+                    int32_t r = row[j];
+                    if (r < 0 || r >= num_kv) continue;
+                    double ds = p[j] * (dp[j] - delta);
+                    double* ar = acc + (int64_t)r * d_qk;
+                    for (int32_t c = 0; c < d_qk; ++c) {
+                        dq[c] += ds * bf16_value(kv[(int64_t)r * d_qk + c]);
+                        ar[c] += (double)scale * ds * bf16_value(qh[c]);
+                    }
+                    for (int32_t c = 0; c < d_v; ++c) ar[c] += p[j] * bf16_value(gh[c]);
+                }
+                for (int32_t c = 0; c < d_qk; ++c) dqo[c] = (float)((double)scale * dq[c]);
+            }
+        }
+        free(p);
+        free(dp);
+        free(dq);
+    }
+    for (size_t e = 0; e < kvn; ++e) {
+        double sum = 0.0;
+        for (int t = 0; t < nt; ++t) sum += part[(size_t)t * kvn + e];
+        d_kv[e] = (float)sum;
+    }
+    free(part);
 }
 
 int32_t kpo_num_threads(void) {

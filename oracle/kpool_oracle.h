@@ -100,6 +100,21 @@ void kpo_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indice
                     int32_t num_kv, int32_t heads, int32_t d_latent, int32_t row_width,
                     float scale, float* out, float* lse, float* out_abs);
 
+/* The same with values narrower than keys: keys are the d_qk-wide latent rows,
+ * values their first d_v columns, out [num_q, heads, d_v] ([P2-CL]: the GLM-5.2
+ * contract, d_qk = 576 with a RoPE tail, d_v = 512). */
+void kpo_sparse_mla_dv(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t num_q,
+                       int32_t num_kv, int32_t heads, int32_t d_qk, int32_t d_v, int32_t row_width,
+                       float scale, float* out, float* lse, float* out_abs);
+
+/* Backward of kpo_sparse_mla_dv [P1-AB, P4-S3]: given d_out [num_q, heads, d_v],
+ * writes d_q [num_q, heads, d_qk] and d_kv [num_kv, d_qk] (fp32; computed in
+ * float64). The key and the value are the same latent rows, so d_kv holds both
+ * contributions. */
+void kpo_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const uint16_t* d_out,
+                        int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_qk, int32_t d_v,
+                        int32_t row_width, float scale, float* d_q, float* d_kv);
+
 /* Threads the OpenMP runtime will use (for reporting). */
 int32_t kpo_num_threads(void);
 

@@ -50,6 +50,10 @@ def lib():
         L.kpo_topk.restype = None
         L.kpo_sparse_mla.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, P]
         L.kpo_sparse_mla.restype = None
+        L.kpo_sparse_mla_dv.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, P, P, P]
+        L.kpo_sparse_mla_dv.restype = None
+        L.kpo_sparse_mla_bwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, P, P]
+        L.kpo_sparse_mla_bwd.restype = None
         L.kpo_num_threads.argtypes = []
         L.kpo_num_threads.restype = i32
         _lib = L
@@ -214,6 +218,37 @@ def sparse_mla(q, kv, indices, scale: float, with_abs: bool = False):
     lib().kpo_sparse_mla(_p(q), _p(kv), _p(indices), Tq, kv.shape[0], H, D, indices.shape[1],
                          float(scale), _p(out), _p(lse), _p(oabs))
     return (out, lse, oabs) if with_abs else (out, lse)
+
+
+def sparse_mla_dv(q, kv, indices, scale: float, d_v: int, with_abs: bool = False):
+    """Sparse MLA with values narrower than keys: keys are the kv rows (width of
+    q), values their first d_v columns. (out [Tq,H,d_v] f32, lse [Tq,H] f32)."""
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    indices = _c(indices, np.int32)
+    Tq, H, D = q.shape
+    out = np.zeros((Tq, H, d_v), np.float32)
+    lse = np.zeros((Tq, H), np.float32)
+    oabs = np.zeros((Tq, H, d_v), np.float32) if with_abs else None
+    lib().kpo_sparse_mla_dv(_p(q), _p(kv), _p(indices), Tq, kv.shape[0], H, D, d_v, indices.shape[1],
+                            float(scale), _p(out), _p(lse), _p(oabs))
+    return (out, lse, oabs) if with_abs else (out, lse)
+
+
+def sparse_mla_bwd(q, kv, indices, d_out, scale: float):
+    """Gradients of sparse_mla / sparse_mla_dv for output gradient d_out
+    [Tq,H,d_v] (bf16 bits): (d_q [Tq,H,D] f32, d_kv [N,D] f32)."""
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    indices = _c(indices, np.int32)
+    d_out = _c(d_out, np.uint16)
+    Tq, H, D = q.shape
+    d_v = d_out.shape[-1]
+    dq = np.zeros((Tq, H, D), np.float32)
+    dkv = np.zeros(kv.shape, np.float32)
+    lib().kpo_sparse_mla_bwd(_p(q), _p(kv), _p(indices), _p(d_out), Tq, kv.shape[0], H, D, d_v,
+                             indices.shape[1], float(scale), _p(dq), _p(dkv))
+    return dq, dkv
 
 
 # ------------------------------------------------------------- pipeline -----
