@@ -262,6 +262,42 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
                          int32_t row_width, float softmax_scale,
                          uint16_t* out, float* lse, hipStream_t stream);
 
+/* Bytes of workspace sparse_mla_bwd needs for these sizes. */
+size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width);
+
+/*
+ * sparse_mla_bwd -- backward of sparse_mla_fwd: the gradients of a loss with
+ * respect to q and kv, given its gradient d_out with respect to the output
+ * [P1-AB: the training path runs a sparse backward; P2-MLA: its dQ and dKV are
+ * validated against a dense reference]. The index rows are constants (the
+ * indexer is frozen [P4-S3]). For query i, head h and the valid entries j of
+ * row i (latent row r_j, as in sparse_mla_fwd), with p_j = exp(s_j - lse[i,h]):
+ *   dp_j = <d_out[i,h], kv[r_j]>,  delta = <d_out[i,h], out[i,h]>,
+ *   ds_j = p_j (dp_j - delta),
+ *   d_q[i,h]   = softmax_scale * sum_j ds_j kv[r_j]
+ *   d_kv[r_j] += softmax_scale * ds_j q[i,h] + p_j d_out[i,h]   (key and value)
+ * summed over every query, head and valid entry (repeats count each time).
+ * bf16 inputs, fp32 accumulation; p and ds enter the products rounded to bf16.
+ * d_kv is written in full (zeroed, then accumulated with fp32 atomic adds: its
+ * value is exact to fp32 rounding, its last bits may differ between runs);
+ * d_q is bit-reproducible. A row with no valid entry gives d_q = 0.
+ *
+ *   q, kv, indices  as passed to sparse_mla_fwd
+ *   out, lse        the outputs of that sparse_mla_fwd call (lse required)
+ *   d_out           device bf16 [num_q, heads, d_latent]
+ *   heads           1 .. 64;  d_latent 64 or 512;  row_width 1 .. 4096
+ *   d_q             device bf16 [num_q, heads, d_latent]   (out)
+ *   d_kv            device fp32 [num_kv, d_latent]         (out)
+ *   workspace       device memory of kp_mla_bwd_workspace_bytes(num_q, row_width)
+ *                   bytes, 256-byte aligned (the per-slot softmax coefficients)
+ */
+kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
+                         const uint16_t* out, const float* lse, const uint16_t* d_out,
+                         int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_latent,
+                         int32_t row_width, float softmax_scale,
+                         uint16_t* d_q, float* d_kv, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /*
  * kp_check_inputs -- debug helper: verifies on the device that cu_seqlens is
  * well formed (starts at 0, non-decreasing, ends at num_tokens) and that

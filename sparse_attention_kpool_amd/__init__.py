@@ -5,8 +5,10 @@ of ``include/kpool.h``); this package is its Python binding.
 """
 from ._lib import (KpoolError, dsa_forward, indexer_rotate_quant, indexer_score_topk,
                    indexer_score_topk_noalloc, indexer_topk_from_scores, kp_check_inputs, kp_indexer_workspace_bytes,
-                   kp_row_width, kp_version, kpool_build, kpool_build_from, lib, sparse_mla_fwd)
+                   kp_mla_bwd_workspace_bytes, kp_row_width, kp_version, kpool_build, kpool_build_from, lib,
+                   sparse_mla_bwd, sparse_mla_fwd)
 
 __all__ = ["KpoolError", "dsa_forward", "indexer_rotate_quant", "indexer_score_topk",
            "indexer_score_topk_noalloc", "indexer_topk_from_scores", "kp_check_inputs", "kp_indexer_workspace_bytes", "kp_row_width",
-           "kp_version", "kpool_build", "kpool_build_from", "lib", "sparse_mla_fwd"]
+           "kp_version", "kpool_build", "kpool_build_from", "lib", "kp_mla_bwd_workspace_bytes",
+           "sparse_mla_bwd", "sparse_mla_fwd"]

@@ -36,6 +36,8 @@ SIGNATURES = [
                                         _P, _P, _P, _P]),
     ("indexer_topk_from_scores", _I, [_P, _I, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
     ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    ("kp_mla_bwd_workspace_bytes", _Z, [_I, _I]),
+    ("sparse_mla_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _P]),
     ("kp_check_inputs", _I, [_P, _I, _I, _P, _I, _P]),
 ]
 
@@ -308,6 +310,37 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sof
     _check(lib().sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), Tq, kv.shape[0], H, D, indices.shape[1],
                                 float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
+
+
+def kp_mla_bwd_workspace_bytes(num_q: int, row_width: int) -> int:
+    return int(lib().kp_mla_bwd_workspace_bytes(num_q, row_width))
+
+
+def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, out: torch.Tensor,
+                   lse: torch.Tensor, d_out: torch.Tensor, softmax_scale: float,
+                   workspace: Optional[torch.Tensor] = None):
+    """Backward of sparse_mla_fwd: (d_q bf16 [Tq,H,D], d_kv f32 [N,D])."""
+    _need(q, "q", torch.bfloat16, (None, None, None))
+    Tq, H, D = q.shape
+    _need(kv, "kv", torch.bfloat16, (None, D))
+    _need(indices, "indices", torch.int32, (Tq, None))
+    _need(out, "out", torch.bfloat16, (Tq, H, D))
+    _need(lse, "lse", torch.float32, (Tq, H))
+    _need(d_out, "d_out", torch.bfloat16, (Tq, H, D))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, (None,))
+    dev = _on(("q", q), ("kv", kv), ("indices", indices), ("out", out), ("lse", lse), ("d_out", d_out),
+              ("workspace", workspace))
+    W = indices.shape[1]
+    need = kp_mla_bwd_workspace_bytes(Tq, W)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    d_q = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
+    d_kv = torch.empty((kv.shape[0], D), dtype=torch.float32, device=dev)
+    _check(lib().sparse_mla_bwd(_ptr(q), _ptr(kv), _ptr(indices), _ptr(out), _ptr(lse), _ptr(d_out), Tq,
+                                kv.shape[0], H, D, W, float(softmax_scale), _ptr(d_q), _ptr(d_kv),
+                                _ptr(workspace), workspace.numel(), _stream(dev)))
+    return d_q, d_kv
 
 
 def kp_check_inputs(cu_seqlens: torch.Tensor, num_tokens: int, q_pos: Optional[torch.Tensor] = None) -> None:

@@ -347,6 +347,44 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
     return ok();
 }
 
+size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width) {
+    if (num_q <= 0 || row_width < 1) return 0;
+    return align256(kp::sparse_mla_bwd_coef_bytes(num_q, row_width));
+}
+
+kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
+                         const uint16_t* out, const float* lse, const uint16_t* d_out,
+                         int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_latent,
+                         int32_t row_width, float softmax_scale,
+                         uint16_t* d_q, float* d_kv, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    g_err.clear();
+    if (num_q < 0 || num_kv < 0 || row_width < 1) return fail(KP_ERR_INVALID_ARG, "bad size");
+    if (heads < 1 || heads > 64) return fail(KP_ERR_UNSUPPORTED, "heads must be in 1..64 (got %d)", heads);
+    if (d_latent != 512 && d_latent != 64)
+        return fail(KP_ERR_UNSUPPORTED, "d_latent must be 512 or 64 (got %d)", d_latent);
+    if (row_width > kp::sparse_mla_max_row_width())
+        return fail(KP_ERR_UNSUPPORTED, "row_width above %d (got %d)", kp::sparse_mla_max_row_width(), row_width);
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+        return fail(KP_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
+    if ((uint64_t)num_kv * (uint64_t)d_latent * 2u + 4096u > 0xFFFFFFFFull)
+        return fail(KP_ERR_UNSUPPORTED, "latent of %d rows x %d is not below 4 GiB - 4 KiB", num_kv, d_latent);
+    if (num_kv > 0 && !d_kv) return fail(KP_ERR_INVALID_ARG, "d_kv is required");
+    if (num_q > 0 && (!q || !kv || !indices || !out || !lse || !d_out || !d_q))
+        return fail(KP_ERR_INVALID_ARG, "q, kv, indices, out, lse, d_out and d_q are required");
+    const size_t need = kp_mla_bwd_workspace_bytes(num_q, row_width);
+    if (num_q > 0 && (!workspace || workspace_bytes < need))
+        return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (num_q == 0 && num_kv == 0) return ok();
+    kp_status st = device_check();
+    if (st != KP_OK) return st;
+    hipError_t e = kp::launch_sparse_mla_bwd(q, kv, indices, out, lse, d_out, num_q, num_kv, heads, d_latent,
+                                             row_width, softmax_scale, d_q, d_kv, workspace, stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse_mla_bwd launch");
+    return ok();
+}
+
 kp_status kp_check_inputs(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
                           const int32_t* q_pos, int32_t num_q, hipStream_t stream) {
     g_err.clear();

@@ -25,7 +25,10 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "sparse_attention_kpool_amd", "csrc", "sparse_mla.hip")
+CSRC = os.path.join(ROOT, "sparse_attention_kpool_amd", "csrc")
+SRC = os.path.join(CSRC, "sparse_mla.hip")
+# files whose kernels gather latent rows with inline-assembly loads into LDS
+ROW_LOAD_SRCS = ["sparse_mla.hip", "sparse_mla_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 MIN_WAIT = 2       # VALU write of a VGPR/AGPR -> MFMA read of it (gfx950)
 RESULT_WAIT = 18   # MFMA result -> read or write by another instruction (16-pass bound)
@@ -75,18 +78,21 @@ def valu_dest(line):
     return regs(first)
 
 
-@pytest.fixture(scope="module")
-def asm_lines():
+def _assemble(src, extra):
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = "/tmp/kp_mla_hazard_check.s"
+    out = "/tmp/kp_hazard_check_" + os.path.basename(src) + ".s"
     subprocess.check_call([HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
-                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                           "-mllvm", "-amdgpu-mfma-vgpr-form", "-x", "hip", SRC,
-                           "-I" + os.path.join(ROOT, "include"),
-                           "-I" + os.path.join(ROOT, "sparse_attention_kpool_amd", "csrc"), "-o", out],
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *extra, "-x", "hip", src,
+                           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-o", out],
                           stderr=subprocess.DEVNULL)
     return open(out).read().splitlines()
+
+
+@pytest.fixture(scope="module")
+def asm_lines():
+    # the flags the library build uses for the attention forward
+    return _assemble(SRC, ["-mllvm", "-amdgpu-mfma-vgpr-form"])
 
 
 def instructions(asm_lines):
@@ -173,8 +179,11 @@ def test_inline_mfma_results_left_alone_until_done(asm_lines):
     assert not bad, "inline-assembly MFMA result touched too soon:\n" + "\n".join(bad[:10])
 
 
-def test_row_load_sgprs_settled(asm_lines):
-    instrs = instructions(asm_lines)
+@pytest.mark.parametrize("src", ROW_LOAD_SRCS)
+def test_row_load_sgprs_settled(src):
+    from sparse_attention_kpool_amd import build
+    lines = _assemble(os.path.join(CSRC, src), build.EXTRA.get(src, []))
+    instrs = instructions(lines)
     loads = 0
     bad = []
     for k, (line, in_asm) in enumerate(instrs):
