@@ -1,12 +1,14 @@
 """Benchmark of the KPool-DSA forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 32k] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 32k] [--no-cpu-baseline] [--backward]
 
 One step = one whole forward of the hot path over one batch of synthetic input
 resident in HBM: kpool_build (pool layout, pooled FP8 keys) + indexer_score_topk
 (query rotation, FP8 scoring, top-k index rows) + sparse_mla_fwd (absorbed
 sparse latent attention). Prints one JSON line on stdout; a per-stage
-breakdown goes to stderr.
+breakdown goes to stderr. Besides the step, the line reports the key pooling
+with cold caches and, with --backward, the sparse-MLA backward on the same
+index rows (its own stage, not part of the step).
 """
 from __future__ import annotations
 
@@ -26,6 +28,9 @@ METRIC = "DSA fwd query-tokens/sec at 32K packed; sparse-MLA TFLOP/s & % bf16 MF
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# the highest bf16 MFMA rate the issue-rate microbenchmark reaches on one MI355X (two
+# waves per SIMD, MFMA only; sparse_attention_kpool_amd/microbench, summary in profiles/)
+MFMA_MEASURED_TFLOPS = 2293.0
 
 # HBM bytes per sparse_mla_fwd launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # passes scaled by the same counters' reading of a plain 1 GiB device copy (the
@@ -76,7 +81,8 @@ def work_counts(s):
 
 def cpu_baseline(s, wl, budget_s: float = 12.0):
     """The oracle as it stands, on a bounded sample of the same workload: the
-    per-forward key pass over the whole row, then query rows in batches until
+    per-forward key pass over the whole row, then blocks of 32 consecutive
+    query rows at random positions (each block's inputs generated once) until
     the time budget is spent. Scaled to query-tokens/s of a whole forward."""
     from oracle import oracle as O
     O.lib()
@@ -85,28 +91,29 @@ def cpu_baseline(s, wl, budget_s: float = 12.0):
     kc, ks, _ = O.keys(wl.full("k_idx"), wl.full("gate"), wl.ape(), ps, s.kpool)
     t_keys = time.perf_counter() - t0
     rng = np.random.default_rng(123)
-    order = rng.permutation(s.Tq)
-    done, t_q, b = 0, 0.0, 32
+    b = min(32, s.Tq)
+    starts = rng.permutation(np.arange(0, s.Tq - b + 1, b))
+    done, t_q = 0, 0.0
     kv = wl.full("kv")
-    while t_q < budget_s and done < s.Tq:
-        rows = np.sort(order[done:done + b])
+    for r0 in starts:
+        if t_q >= budget_s:
+            break
+        rows = np.arange(r0, r0 + b)
         qpos = s.query_positions()[rows]
-        q_idx = np.concatenate([wl.rows("q_idx", int(r), int(r) + 1) for r in rows])
-        w = np.concatenate([wl.rows("w", int(r), int(r) + 1) for r in rows])
-        q = np.concatenate([wl.rows("q", int(r), int(r) + 1) for r in rows])
+        q_idx, w, q = wl.rows("q_idx", r0, r0 + b), wl.rows("w", r0, r0 + b), wl.rows("q", r0, r0 + b)
         t1 = time.perf_counter()
         qc, qs = O.queries(q_idx)
         sc = O.scores(s.cu, cu_pools, s.kpool, qpos, s.max_pools, w, qc, qs, kc, ks)
         idx, _ = O.topk(s.cu, cu_pools, s.kpool, qpos, sc, s.topk, s.row_width)
         O.sparse_mla(q, kv, idx, s.scale)
         t_q += time.perf_counter() - t1
-        done += len(rows)
+        done += b
     per_q = t_q / done
     fwd = t_keys + per_q * s.Tq
     return {"value": s.Tq / fwd, "unit": "query-tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"key pass over all {s.T} tokens ({t_keys:.2f} s) + {done} random query rows of "
-                      f"{s.Tq} through scoring, top-k and attention ({t_q:.1f} s); whole-forward time "
-                      f"extrapolated as keys + per-query time x {s.Tq}"}
+            "sample": f"key pass over all {s.T} tokens ({t_keys:.2f} s) + {done} query rows of {s.Tq} "
+                      f"(blocks of {b} consecutive rows at random positions) through scoring, top-k and "
+                      f"attention ({t_q:.1f} s); whole-forward time extrapolated as keys + per-query time x {s.Tq}"}
 
 
 def main():
@@ -119,6 +126,10 @@ def main():
     ap.add_argument("--full-pool", action="store_true",
                     help="decode: pool the whole context every step instead of the pools of the new tokens")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time sparse_mla_bwd (dQ, dKV for a random output gradient) on the same rows")
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="kpool_build launches timed after a 512 MB write each (cold L2 and Infinity Cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
                          "reading for rocprofv3's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -222,7 +233,24 @@ def main():
     wall = time.perf_counter() - t_start
     st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
     ms_stage = st.mean(axis=0)
+    ms_med, ms_min = np.median(st, axis=0), st.min(axis=0)
     ms_step = wall * 1e3 / args.steps
+
+    # kpool_build cold: a 512 MB write before each launch evicts the L2s and the
+    # Infinity Cache, so the launch reads its k_idx and gate rows from HBM
+    cold = []
+    if args.cold_reps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(L.kpool_build_from(ptr(cu), s.B, s.T, ptr(k_idx), ptr(gate), ptr(ape), s.D_I, s.kpool, 0,
+                                    ptr(cu_pools), ptr(pool_start), ptr(k8), ptr(ks), None, sp))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
 
     wc = work_counts(s)
     assert int(nv.sum().item()) == wc["sum_n_valid"], "index rows disagree with the closed-form slot count"
@@ -234,6 +262,41 @@ def main():
     log(f"sparse MLA {mla_tflops:.1f} TFLOP/s ({100 * mla_tflops / BF16_PEAK_TFLOPS:.1f}% bf16 peak); gathered "
         f"{wc['gather_bytes'] / mla_s / 1e9:.0f} GB/s effective; pooling {wc['pool_bytes'] / (ms_stage[0] / 1e3) / 1e9:.0f} GB/s;"
         f" scoring+top-k {wc['score_flop'] / (ms_stage[1] / 1e3) / 1e12:.1f} TFLOP/s (FP8)")
+
+    bwd = None
+    if args.backward:
+        g = torch.Generator(device=dev)
+        g.manual_seed(17)
+        d_out = torch.randn((s.Tq, s.H, s.D), generator=g, device=dev).to(torch.bfloat16)
+        d_q = torch.empty_like(d_out)
+        d_kv = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
+        bws = K.kp_mla_bwd_workspace_bytes(s.Tq, W)
+        bw_ws = torch.empty(bws, dtype=torch.uint8, device=dev)
+
+        def bstep():
+            call(L.sparse_mla_bwd(ptr(q), ptr(kv), ptr(idx), ptr(out), ptr(lse), ptr(d_out), s.Tq, s.T, s.H, s.D,
+                                  W, C.c_float(s.scale), ptr(d_q), ptr(d_kv), ptr(bw_ws), bws, sp))
+
+        for _ in range(args.warmup):
+            bstep()
+        torch.cuda.synchronize()
+        bt = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bt.append(e0.elapsed_time(e1))
+        # flop: S, dP and dQ products (6*H*D per valid slot) + the dKV product (4*H*D)
+        bflop = float(10 * s.H * s.D) * wc["sum_n_valid"]
+        bmed = float(np.median(bt))
+        btf = bflop / (bmed / 1e3) / 1e12
+        bwd = {"ms_median": bmed, "ms_min": float(min(bt)), "tflops": btf, "frac_bf16_peak": btf / BF16_PEAK_TFLOPS,
+               "algorithmic": f"10*H*D = {10 * s.H * s.D} flop per valid slot x {wc['sum_n_valid']} slots",
+               "workspace_bytes": bws, "kernels": "mla_bwd_dq_kernel + mla_bwd_dkv_kernel (+ dKV zero fill)"}
+        log(f"sparse MLA backward: {bmed:.3f} ms median, {btf:.1f} TFLOP/s ({100 * btf / BF16_PEAK_TFLOPS:.1f}% "
+            f"bf16 peak)")
 
     res = {
         "metric": METRIC,
@@ -253,14 +316,30 @@ def main():
                    "topk_pools": s.topk, "row_width": W, "heads": s.H, "d_latent": s.D, "h_idx": s.H_I,
                    "d_idx": s.D_I, "pools_rebuilt_from_token": token_lo},
         "stages_ms": {"kpool_build": ms_stage[0], "indexer_score_topk": ms_stage[1], "sparse_mla_fwd": ms_stage[2]},
+        "stages_ms_median": {"kpool_build": float(ms_med[0]), "indexer_score_topk": float(ms_med[1]),
+                             "sparse_mla_fwd": float(ms_med[2])},
+        "stages_ms_min": {"kpool_build": float(ms_min[0]), "indexer_score_topk": float(ms_min[1]),
+                          "sparse_mla_fwd": float(ms_min[2])},
         "sparse_mla_tflops": mla_tflops,
         "sparse_mla_pct_bf16_peak": 100 * mla_tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": mla_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": mla_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
                      "traffic_unit": "bytes per launch (HBM read + write)",
                      "kernel": "sparse_mla_kernel<512>", "kernel_source_sha256": mla_sha,
+                     "measured_peak": MFMA_MEASURED_TFLOPS,
+                     "measured_peak_note": "bf16 MFMA-only issue rate, two waves per SIMD (microbenchmark)",
                      "algorithmic": f"4*H*D = {4 * s.H * s.D} flop per valid slot x {wc['sum_n_valid']} slots"},
     }
+    if cold:
+        pool_bytes = float(s.T * s.D_I * 2 * 2 + wc["pools"] * (s.D_I + 4))
+        cmed = float(np.median(cold))
+        res["pooling_cold"] = {"ms_median": cmed, "hbm_gbs": pool_bytes / (cmed / 1e3) / 1e9,
+                               "frac_hbm": pool_bytes / (cmed / 1e3) / 1e9 / HBM_PEAK_GBS,
+                               "warm_ms_median": float(ms_med[0]), "bytes": pool_bytes,
+                               "note": "kpool_build over all tokens after a 512 MB write (L2 and Infinity Cache "
+                                       "evicted); warm = the step's own launch"}
+    if bwd is not None:
+        res["backward"] = bwd
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(s, wl, args.cpu_budget)
