@@ -54,6 +54,15 @@
  *     verifies the integer ones on demand.
  *   - Positions and index-row entries are global token indices of the packed
  *     row (rows of the latent).
+ *   - Shared layers (IndexShare): a DSA layer that shares its selection with
+ *     the previous full layer ("GLM-5 / GLM-5.1 / GLM-5.2 / GLM-5.3 (MoE +
+ *     DSA)" page, Key Features: shared layers reuse the previous full layer's
+ *     top-k sparse-attention selection) skips kpool_build and
+ *     indexer_score_topk and calls sparse_mla_fwd (and sparse_mla_bwd) with
+ *     its own q and latent and the index rows the full layer's
+ *     indexer_score_topk wrote. Index rows depend only on the indexer inputs
+ *     and the layout, never on q or the latent, so they are valid for any
+ *     layer over the same packed row.
  */
 #ifndef KPOOL_H
 #define KPOOL_H
@@ -243,8 +252,12 @@ kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, 
  * P2-MLA]. For query i, head h and the valid entries j of row i
  * (0 <= indices[i,j] < num_kv; every other entry is masked, wherever it sits):
  *   s_j      = softmax_scale * <q[i,h,:], kv[indices[i,j],:]>
- *   out[i,h] = sum_j softmax(s)_j * kv[indices[i,j],:]      (K = V = the latent)
+ *   out[i,h] = sum_j softmax(s)_j * kv[indices[i,j], :d_v]  (K = V = the latent)
  *   lse[i,h] = log(sum_j exp(s_j))                          (natural log)
+ * with d_v = d_latent, except d_latent = 576: keys 576 wide (512 + a 64-wide
+ * RoPE tail), values their first 512 columns, d_v = 512 -- the GLM-5.2 contract
+ * the NeMo PR keeps (Changelog: D=576, top-k at most 2048); GLM-5.3-Flash itself
+ * has no tail (d_latent 512 [P4-S2]).
  * bf16 inputs, fp32 accumulation, bf16 output (round to nearest even). A row
  * with no valid entry gives out = 0 and lse = -inf. Repeated entries count
  * repeatedly.
@@ -252,9 +265,10 @@ kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, 
  *   q        device bf16 [num_q, heads, d_latent]   (the K projection already absorbed)
  *   kv       device bf16 [num_kv, d_latent]
  *   indices  device int32 [num_q, row_width]
- *   heads    1 .. 64;  d_latent 64 or 512;  row_width 1 .. 4096;
- *            num_kv * d_latent * 2 < 4 GiB - 4 KiB;  softmax_scale finite and > 0
- *   out      device bf16 [num_q, heads, d_latent]   (out)
+ *   heads    1 .. 64;  d_latent 64, 512 or 576;  row_width 1 .. 4096 (1 .. 2048
+ *            for d_latent 576); num_kv * d_latent * 2 < 4 GiB - 4 KiB;
+ *            softmax_scale finite and > 0
+ *   out      device bf16 [num_q, heads, d_v]        (out)
  *   lse      device fp32 [num_q, heads]             (out, NULLABLE)
  */
 kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,

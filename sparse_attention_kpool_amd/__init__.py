@@ -3,12 +3,12 @@
 The compute lives in ``libkpool.so`` (hand-written HIP kernels behind the C ABI
 of ``include/kpool.h``); this package is its Python binding.
 """
-from ._lib import (KpoolError, dsa_forward, indexer_rotate_quant, indexer_score_topk,
+from ._lib import (KpoolError, dsa_forward, dsa_forward_shared, indexer_rotate_quant, indexer_score_topk,
                    indexer_score_topk_noalloc, indexer_topk_from_scores, kp_check_inputs, kp_indexer_workspace_bytes,
                    kp_mla_bwd_workspace_bytes, kp_row_width, kp_version, kpool_build, kpool_build_from, lib,
                    sparse_mla_bwd, sparse_mla_fwd)
 
-__all__ = ["KpoolError", "dsa_forward", "indexer_rotate_quant", "indexer_score_topk",
+__all__ = ["KpoolError", "dsa_forward", "dsa_forward_shared", "indexer_rotate_quant", "indexer_score_topk",
            "indexer_score_topk_noalloc", "indexer_topk_from_scores", "kp_check_inputs", "kp_indexer_workspace_bytes", "kp_row_width",
            "kp_version", "kpool_build", "kpool_build_from", "lib", "kp_mla_bwd_workspace_bytes",
            "sparse_mla_bwd", "sparse_mla_fwd"]

@@ -296,16 +296,18 @@ def indexer_topk_from_scores(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, s
 
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, softmax_scale: float,
                    return_lse: bool = True, out: Optional[torch.Tensor] = None):
-    """Absorbed sparse latent attention: (out bf16 [Tq,H,D], lse f32 [Tq,H] or None)."""
+    """Absorbed sparse latent attention: (out bf16 [Tq,H,d_v], lse f32 [Tq,H] or None);
+    d_v = D, except 512 for 576-wide keys (a 64-wide RoPE tail)."""
     _need(q, "q", torch.bfloat16, (None, None, None))
     Tq, H, D = q.shape
+    d_v = 512 if D == 576 else D
     _need(kv, "kv", torch.bfloat16, (None, D))
     _need(indices, "indices", torch.int32, (Tq, None))
     if out is not None:
-        _need(out, "out", torch.bfloat16, (Tq, H, D))
+        _need(out, "out", torch.bfloat16, (Tq, H, d_v))
     dev = _on(("q", q), ("kv", kv), ("indices", indices), ("out", out))
     if out is None:
-        out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((Tq, H, d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Tq, H), dtype=torch.float32, device=dev) if return_lse else None
     _check(lib().sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), Tq, kv.shape[0], H, D, indices.shape[1],
                                 float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev)))
@@ -351,6 +353,13 @@ def kp_check_inputs(cu_seqlens: torch.Tensor, num_tokens: int, q_pos: Optional[t
     nq = 0 if q_pos is None else q_pos.shape[0]
     _check(lib().kp_check_inputs(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, num_tokens, _ptr(q_pos), nq,
                                  _stream(cu_seqlens.device)))
+
+
+def dsa_forward_shared(q, kv, indices, *, softmax_scale):
+    """A shared DSA layer (IndexShare): attention with the index rows of the
+    previous full layer (its dsa_forward's ``indices``); no pooling, scoring or
+    selection. Returns (out, lse)."""
+    return sparse_mla_fwd(q, kv, indices, softmax_scale)
 
 
 def dsa_forward(cu_seqlens, k_idx, gate, ape, q_idx, w_idx, q, kv, *, kpool=4, topk_pools=512,

@@ -325,10 +325,11 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
     g_err.clear();
     if (num_q < 0 || num_kv < 0 || row_width < 1) return fail(KP_ERR_INVALID_ARG, "bad size");
     if (heads < 1 || heads > 64) return fail(KP_ERR_UNSUPPORTED, "heads must be in 1..64 (got %d)", heads);
-    if (d_latent != 512 && d_latent != 64)
-        return fail(KP_ERR_UNSUPPORTED, "d_latent must be 512 or 64 (got %d)", d_latent);
-    if (row_width > kp::sparse_mla_max_row_width())
-        return fail(KP_ERR_UNSUPPORTED, "row_width above %d (got %d)", kp::sparse_mla_max_row_width(), row_width);
+    if (d_latent != 512 && d_latent != 64 && d_latent != 576)
+        return fail(KP_ERR_UNSUPPORTED, "d_latent must be 512, 576 or 64 (got %d)", d_latent);
+    if (row_width > kp::sparse_mla_max_row_width(d_latent))
+        return fail(KP_ERR_UNSUPPORTED, "row_width above %d for d_latent %d (got %d)",
+                    kp::sparse_mla_max_row_width(d_latent), d_latent, row_width);
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
         return fail(KP_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
     // the row loads address the latent through a buffer descriptor based 4 KiB below
@@ -363,8 +364,9 @@ kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
     if (heads < 1 || heads > 64) return fail(KP_ERR_UNSUPPORTED, "heads must be in 1..64 (got %d)", heads);
     if (d_latent != 512 && d_latent != 64)
         return fail(KP_ERR_UNSUPPORTED, "d_latent must be 512 or 64 (got %d)", d_latent);
-    if (row_width > kp::sparse_mla_max_row_width())
-        return fail(KP_ERR_UNSUPPORTED, "row_width above %d (got %d)", kp::sparse_mla_max_row_width(), row_width);
+    if (row_width > kp::sparse_mla_max_row_width(d_latent))
+        return fail(KP_ERR_UNSUPPORTED, "row_width above %d (got %d)", kp::sparse_mla_max_row_width(d_latent),
+                    row_width);
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
         return fail(KP_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
     if ((uint64_t)num_kv * (uint64_t)d_latent * 2u + 4096u > 0xFFFFFFFFull)

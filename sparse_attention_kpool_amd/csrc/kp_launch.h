@@ -38,8 +38,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              int num_kv, int heads, int d_latent, int row_width, float scale_log2,
                              uint16_t* out, float* lse, hipStream_t stream);
 
-// Largest index row sparse_mla_fwd accepts.
-int sparse_mla_max_row_width();
+// Largest index row sparse_mla_fwd accepts for this key width.
+int sparse_mla_max_row_width(int d_latent);
 
 // Backward of the sparse latent attention: dq (bf16) and dkv (fp32, zeroed, then
 // accumulated); workspace of sparse_mla_bwd_coef_bytes bytes.

@@ -86,7 +86,25 @@ __device__ __forceinline__ void kp_pin_weights(bf16x8& a, bf16x8& b) {
     __asm__ __volatile__("s_nop 2" : "+v"(a), "+v"(b));
 }
 
-template <int D>
+// The 64-column RoPE tail of a latent row (keys 576 wide, the GLM-5.2
+// contract) sits in its own LDS tile: row r at r*128 bytes, its 16-byte chunk c
+// at position c ^ rope_swz(r). Under gfx950's 16-byte read passes (see
+// row_base) the K reads of a pass (16 rows, two chunk columns) then hit 16
+// distinct bank groups.
+__device__ __forceinline__ constexpr int rope_swz(int r) { return ((r >> 1) & 7) ^ (2 * ((r >> 4) & 1)); }
+
+// Direct-to-LDS copy with a per-lane memory offset: lane l copies the 16 bytes
+// at rsrc base + voff to LDS byte M0 + 16*l (the RoPE tails of 8 rows, 128
+// bytes each, per instruction).
+__device__ __forceinline__ void lds_dma16_lane(u32x4 rsrc, uint32_t voff, uint32_t m0) {
+    __asm__ __volatile__("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :: "v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+
+// D: width of the values and of the keys' NoPE part; DR: width of the keys'
+// RoPE tail (0, or 64 for the 576-wide keys of the GLM-5.2 contract, whose
+// values are the first 512 columns).
+template <int D, int DR>
 __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ indices,
     int num_kv, int heads, int row_width, float scale_log2, uint16_t* __restrict__ out,
@@ -101,14 +119,23 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     constexpr int TILE_B = MLA_TK * (RB + 48);   // bytes per LDS tile (row_base of row 64)
     constexpr int RPW = MLA_TK / NW;        // rows each wave gathers per tile
     constexpr int XB = (CT / 2) * 2 * 64 * 16;  // bytes of O one wave hands to its partner
+    constexpr int DQK = D + DR;             // key (and q) width in memory
+    constexpr int RK = DR / 32;             // QK k-steps over the RoPE tail
+    constexpr int ROPE_RB = DR * 2;         // LDS bytes per RoPE tail row
+    constexpr int ROPE_TB = MLA_TK * ROPE_RB;
+    // the index list: 4096 entries, or 2048 with a RoPE tail (its top-k is at most
+    // 2048 tokens) so that the tail's LDS tiles fit
+    constexpr int MAXR = DR > 0 ? 2048 : MLA_MAX_ROW;
     static_assert(NW == 4 && MLA_TK == 64 && RPW == 16 && CH >= 8 && CH <= 64, "tile split");
     static_assert(4 * XB <= MLA_NBUF * TILE_B, "row-half merge fits the ring");
+    static_assert(DR == 0 || (D == 512 && DR == 64), "RoPE tail: 512 + 64 only");
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
-    __shared__ __align__(16) int32_t list[MLA_MAX_ROW];   // byte offsets of the listed latent rows
+    __shared__ __align__(16) int32_t list[MAXR];   // byte offsets of the listed latent rows
     __shared__ float mls[2][64][3];   // per row half and head: reference max, sums
-    __shared__ int rcnt[MLA_MAX_ROW / NT * NW];   // valid entries per (round, wave) of the compaction
+    __shared__ int rcnt[MAXR / NT * NW];   // valid entries per (round, wave) of the compaction
     __shared__ int rflag[2];          // a wave saw a score too far above its reference, by step parity
+    __shared__ __align__(16) uint8_t rope[DR > 0 ? MLA_NBUF * ROPE_TB : 16];   // RoPE tail tiles
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -121,7 +148,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // together (one memory latency), each wave counts its valid entries of a
     // round with a ballot, and one scan over the (round, wave) counts places
     // every entry.
-    constexpr int NRND = MLA_MAX_ROW / NT;
+    constexpr int NRND = MAXR / NT;
     const int32_t* irow = indices + (size_t)i * row_width;
     int ent[NRND];
 #pragma unroll
@@ -142,13 +169,23 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
         const int head = 32 * hh + 16 * ht + n;
-        const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * D;
+        const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * DQK;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int col = 32 * ks + 8 * g;
             qf[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
                                                         qrow + (DP == D ? col : min(col, D - 8))));
         }
+    }
+    // the RoPE tail of Q: qr[ht][c] holds columns D + 32*c + 8*g .. +7
+    bf16x8 qr[2][RK > 0 ? RK : 1];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        const int head = 32 * hh + 16 * ht + n;
+        const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * DQK;
+#pragma unroll
+        for (int c = 0; c < RK; ++c)
+            qr[ht][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + D + 32 * c + 8 * g));
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -166,8 +203,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     __syncthreads();
     int n_valid;
     {
-        static_assert(NRND * NW == 64, "one count per lane");
-        const int c = rcnt[lane];
+        static_assert(NRND * NW <= 64, "one count per lane");
+        const int c = lane < NRND * NW ? rcnt[lane] : 0;
         int x = c;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -182,7 +219,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0u));
             if (ent[k] >= 0 && ent[k] < num_kv)   // byte offset (the latent is below 4 GiB)
-                list[base + below] = (int32_t)((uint32_t)ent[k] * (uint32_t)(D * 2));
+                list[base + below] = (int32_t)((uint32_t)ent[k] * (uint32_t)(DQK * 2));
         }
     }
     __syncthreads();
@@ -215,13 +252,14 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
     const uint32_t wave_lds = ring_lds + (uint32_t)row_base<RB>(RPW * wave_s);   // LDS row 16w of buffer 0
     const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row
+    const uint32_t rope_lds = lds_addr(rope);
     // the latent as a raw buffer: base (48 bits) 4 KiB below the latent, so that the
     // adjusted scalar offsets of the list stay positive; stride 0; num_kv * D * 2
     // + 4 KiB bytes (at most 4 GiB); the default dword format of gfx9 descriptors
     const uint64_t kv_addr = reinterpret_cast<uint64_t>(kv);
     const uint64_t kv_base = kv_addr - 4096u;
     const u32x4 kv_rsrc = u32x4{(uint32_t)kv_base, (uint32_t)(kv_base >> 32) & 0xFFFFu,
-                                (uint32_t)((uint64_t)num_kv * (D * 2) + 4096u), 0x00020000u};
+                                (uint32_t)((uint64_t)num_kv * (DQK * 2) + 4096u), 0x00020000u};
     // KP_ROWS_OF reads the (adjusted) byte offsets of this wave's 16 rows of tile kt_
     // into rws_[16]; KP_ISSUE_ROW(j_) issues the gather of the wave's row j_ into
     // buffer buf_ (rows 4m .. 4m+3 share M0)
@@ -249,10 +287,25 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             else lds_dma16_row_at<row_base<RB>(3)>(kv_rsrc, lane16, (uint32_t)rws_[j_], m0_);    \
         }                                                                                      \
     }
+// KP_ISSUE_ROPE(kt_, m_, buf_): the RoPE tails of the wave's rows 8m_ .. 8m_+7 of
+// tile kt_ into RoPE tile buf_: lane l brings chunk position l % 8 of row
+// 16w + 8m_ + l / 8 (source chunk (l % 8) ^ rope_swz(row)); its list entry gives
+// the row's offset (the list's adjustment undone by row_base(row % 4))
+#define KP_ISSUE_ROPE(kt_, m_, buf_)                                                           \
+    if (DR > 0) {                                                                              \
+        const int jr_ = RPW * wave + 8 * (m_) + (lane >> 3);                                   \
+        const uint32_t voff_ = (uint32_t)list[(kt_) * MLA_TK + jr_] + (uint32_t)row_base<RB>(jr_ & 3) + \
+                               (uint32_t)(2 * D) + 16u * (uint32_t)((lane & 7) ^ rope_swz(jr_)); \
+        const uint32_t m0r_ = __builtin_amdgcn_readfirstlane(                                   \
+            rope_lds + (uint32_t)((buf_) * ROPE_TB + (RPW * wave_s + 8 * (m_)) * ROPE_RB));     \
+        lds_dma16_lane(kv_rsrc, voff_, m0r_);                                                  \
+    }
 #define KP_ISSUE_TILE(kt_, buf_)                                                               \
     {                                                                                          \
         KP_ROWS_OF(kt_)                                                                        \
         _Pragma("unroll") for (int j = 0; j < RPW; ++j) KP_ISSUE_ROW(j, buf_)                 \
+        KP_ISSUE_ROPE(kt_, 0, buf_)                                                            \
+        KP_ISSUE_ROPE(kt_, 1, buf_)                                                            \
     }
 
     // O^T accumulators: o[ct][ht] holds columns 16*ct + 4*g + e of head 32*hh + 16*ht + n
@@ -289,6 +342,15 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     int kb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) kb[s] = row_base<RB>(32 * rh + 8 * (n >> 2) + 4 * s + (n & 3)) + 16 * g;
+    // the same rows' RoPE tails, k-step c (columns D + 32*c + 8*g: chunk 4*c + g)
+    int rkb[2][RK > 0 ? RK : 1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int c = 0; c < RK; ++c) {
+            const int r = 32 * rh + 8 * (n >> 2) + 4 * s + (n & 3);
+            rkb[s][c] = r * ROPE_RB + 16 * ((4 * c + g) ^ rope_swz(r));
+        }
     // V^T A operand of column tile ct: lane (g, n) needs rows 32*rh + 8*g .. +7 of
     // column 16*ct + n; two transposing reads (b = 0, 1) of rows
     // 32*rh + 8*g + 4*b + e4, 8 bytes at column 16*ct + 8*(q4/2) + 4*(q4%2): byte
@@ -324,7 +386,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         const int buf_ = kt & 1;                                                               \
         /* the gather of the next tile; the last tile gathers its own rows again into the */   \
         /* free buffer (no branch per row; those rows were just read, from the L2) */          \
-        KP_ROWS_OF(kt + 1 < ntiles ? kt + 1 : kt)                                              \
+        const int ktn_ = kt + 1 < ntiles ? kt + 1 : kt;                                        \
+        KP_ROWS_OF(ktn_)                                                                       \
         const uint8_t* tb_ = ring + buf_ * TILE_B;                                             \
         /* per-lane bases of the K and V reads in this tile (each read adds a constant) */     \
         const uint8_t* tbk_[2] = {tb_ + kb[0], tb_ + kb[1]};                                   \
@@ -356,8 +419,21 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             __builtin_amdgcn_sched_barrier(0);                                                 \
             _Pragma("unroll") for (int j = c * RPW / KS; j < (c + 1) * RPW / KS; ++j)          \
                 KP_ISSUE_ROW(j, buf_ ^ 1)                                                     \
+            if (c == 1) KP_ISSUE_ROPE(ktn_, 0, buf_ ^ 1)                                       \
+            if (c == KS / 2 + 1) KP_ISSUE_ROPE(ktn_, 1, buf_ ^ 1)                              \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             sacc_[1][1] = mfma_bf16_16x16x32(kf_[c % KP_RING_K][1], qf[1][c], sacc_[1][1]);    \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        /* the RoPE tail's k-steps: both sub-tiles' K fragments from the RoPE tile */          \
+        _Pragma("unroll") for (int c = 0; c < RK; ++c) {                                       \
+            const uint8_t* rt_ = rope + buf_ * ROPE_TB;                                        \
+            const bf16x8 kr0_ = *reinterpret_cast<const bf16x8*>(rt_ + rkb[0][c]);             \
+            const bf16x8 kr1_ = *reinterpret_cast<const bf16x8*>(rt_ + rkb[1][c]);             \
+            sacc_[0][0] = mfma_bf16_16x16x32(kr0_, qr[0][c], sacc_[0][0]);                     \
+            sacc_[0][1] = mfma_bf16_16x16x32(kr0_, qr[1][c], sacc_[0][1]);                     \
+            sacc_[1][0] = mfma_bf16_16x16x32(kr1_, qr[0][c], sacc_[1][0]);                     \
+            sacc_[1][1] = mfma_bf16_16x16x32(kr1_, qr[1][c], sacc_[1][1]);                     \
         }                                                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                     \
         if ((kt + 1) * MLA_TK > n_valid) {   /* ragged last tile: mask rows past the end */    \
@@ -473,6 +549,9 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             if (!(head < heads && (DP == D || 32 * ks + 8 * g < D))) qf[ht][ks] = bf16x8{};
+#pragma unroll
+        for (int c = 0; c < RK; ++c)
+            if (!(head < heads)) qr[ht][c] = bf16x8{};
     }
     for (int kt = 0;;) {
         // the flag of the previous step is final (set before the last barrier) and
@@ -514,6 +593,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #undef KP_RING_K
 #undef KP_RING_V
 #undef KP_ISSUE_TILE
+#undef KP_ISSUE_ROPE
 #undef KP_ISSUE_ROW
 #undef KP_ROWS_OF
 
@@ -595,24 +675,26 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #undef KP_FINISH
 }
 
-template <int D>
+template <int D, int DR>
 static hipError_t launch_mla_t(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int num_q,
                                int num_kv, int heads, int row_width, float scale_log2, uint16_t* out,
                                float* lse, hipStream_t stream) {
-    sparse_mla_kernel<D><<<num_q, 64 * MLA_NW, 0, stream>>>(q, kv, indices, num_kv, heads, row_width, scale_log2,
-                                                             out, lse);
+    sparse_mla_kernel<D, DR><<<num_q, 64 * MLA_NW, 0, stream>>>(q, kv, indices, num_kv, heads, row_width,
+                                                                 scale_log2, out, lse);
     return hipGetLastError();
 }
 
-int sparse_mla_max_row_width() { return MLA_MAX_ROW; }
+int sparse_mla_max_row_width(int d_latent) { return d_latent == 576 ? 2048 : MLA_MAX_ROW; }
 
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int num_q,
                              int num_kv, int heads, int d_latent, int row_width, float scale_log2,
                              uint16_t* out, float* lse, hipStream_t stream) {
     if (num_q == 0) return hipSuccess;
+    if (d_latent == 576)
+        return launch_mla_t<512, 64>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
     if (d_latent == 512)
-        return launch_mla_t<512>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
-    return launch_mla_t<64>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
+        return launch_mla_t<512, 0>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
+    return launch_mla_t<64, 0>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
 }
 
 }  // namespace kp

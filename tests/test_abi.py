@@ -84,7 +84,13 @@ def test_invalid_args_rejected_on_host(L):
     assert b"workspace" in L.kp_last_error()
     # unsupported head count / latent width
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 65, 512, 128, C.c_float(0.1), fake, None, None) == 2
-    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 640, 128, C.c_float(0.1), fake, None, None) == 2
+    # 576-wide keys (the RoPE-tail contract) take index rows of at most 2048 entries
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 576, 2048, C.c_float(0.1), fake, None, None) == 0
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 2176, C.c_float(0.1), fake, None, None) == 2
+    # the backward takes 64- and 512-wide latents
+    assert L.sparse_mla_bwd(fake, fake, fake, fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, fake,
+                            fake, 1 << 30, None) == 2
     assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 1
     # a latent of more than 4 GiB - 4 KiB (the row loads address it from 4 KiB below)
     assert L.sparse_mla_fwd(fake, fake, fake, 4, 1 << 22, 64, 512, 128, C.c_float(0.1), fake, None, None) == 2

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._util import (check_key_codes, check_lse, check_out, check_scores, dev, dev_bf16, host, host_bf16_f32)
+from tests._util import (OUT_MAX, check_key_codes, check_lse, check_out, check_scores, dev, dev_bf16, host, host_bf16_f32)
 from workloads import Workload, custom, spec
 
 pytestmark = pytest.mark.gpu
@@ -450,3 +450,94 @@ def test_end_to_end_selection_agreement(K, oracle_mod, name):
         jac.append(len(a & b) / len(a | b))
     _log("  jaccard mean", np.mean(jac), "min", np.min(jac), "identical", np.mean(np.array(jac) == 1.0))
     assert np.mean(jac) >= 0.97
+
+
+# -------------------------------------------------------- shared layers -----
+@pytest.mark.parametrize("name", ["tiny_dense", "2k", "packed4k"])
+def test_index_share(K, oracle_mod, name):
+    """IndexShare: a second layer with its own q and latent reuses the first
+    layer's index rows (no pooling, scoring or selection of its own). Its
+    output must equal the oracle's attention of the second layer's q and
+    latent over those same rows, and differ from the first layer's."""
+    s = spec(name)
+    wl = Workload(s)
+    _log("index share", name)
+    out_a, _, idx, nv = K.dsa_forward(dev(s.cu), dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")),
+                                      dev(wl.ape()), dev_bf16(wl.full("q_idx")), dev(wl.full("w")),
+                                      dev_bf16(wl.full("q")), dev_bf16(wl.full("kv")), kpool=s.kpool,
+                                      topk_pools=s.topk, softmax_scale=s.scale)
+    # the second layer: fresh q and latent of the same shapes (another seed)
+    wl_b = Workload(spec(name).__class__(**{**spec(name).__dict__, "seed": s.seed + 100}))
+    q_b, kv_b = wl_b.full("q"), wl_b.full("kv")
+    out_b, lse_b = K.dsa_forward_shared(dev_bf16(q_b), dev_bf16(kv_b), idx, softmax_scale=s.scale)
+    rows = np.arange(s.Tq) if s.Tq <= 64 else np.unique(np.concatenate([np.arange(0, s.Tq, 127), [s.Tq - 1]]))
+    g_idx = host(idx)[rows]
+    ref_out, ref_lse = oracle_mod.sparse_mla(q_b[rows], kv_b, g_idx, s.scale)
+    info = check_out(host_bf16_f32(out_b)[rows], ref_out, name)
+    info["lse"] = check_lse(host(lse_b)[rows], ref_lse, name)
+    assert not torch.equal(out_a, out_b)
+    # the full layer's rows are the oracle's where selection covers every pool
+    if name != "packed4k":
+        assert np.array_equal(g_idx, oracle_mod.dsa_forward(wl, q_rows=rows, with_mla=False)["indices"])
+    _log("  ", info)
+
+
+# ----------------------------------------------- 576-wide keys (RoPE tail) --
+@pytest.mark.parametrize("case", ["dense_2k_rows", "scattered_mask", "single", "duplicates", "heads40",
+                                  "rising", "max_width", "many_queries"])
+def test_mla_rope_tail(K, oracle_mod, case):
+    """Keys 576 wide (512 + a 64-wide RoPE tail), values their first 512
+    columns: the GLM-5.2 contract (top-k at most 2048 tokens) the NeMo PR keeps,
+    against the oracle's narrow-value attention. The tail is gathered and read
+    through its own LDS tile, so every case checks that its columns count."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(13)
+    H, DQ, N, W, Tq = 64, 576, 3000, 256, 9
+    if case == "heads40":
+        H = 40
+    if case == "max_width":
+        W, Tq = 2048, 3
+    if case == "many_queries":
+        Tq, W = 600, 192
+    if case == "dense_2k_rows":      # the 2K workload's causal rows, sampled queries
+        N, W = 2048, 2048
+        rows = np.array([0, 1, 2, 3, 100, 511, 1024, 2047])
+        Tq = len(rows)
+    q = rng.standard_normal((Tq, H, DQ)).astype(np.float32)
+    kv = rng.standard_normal((N, DQ)).astype(np.float32)
+    if case == "rising":
+        kv[N // 2:] *= 100.0
+    q, kv = f32_to_bf16_bits(q), f32_to_bf16_bits(kv)
+    idx = rng.integers(0, N, size=(Tq, W)).astype(np.int32)
+    if case == "dense_2k_rows":
+        idx = np.full((Tq, W), -1, np.int32)
+        for i, t in enumerate(rows):
+            idx[i, :t + 1] = np.arange(t + 1)
+    if case == "scattered_mask":
+        m = rng.random(idx.shape) < 0.4
+        idx[m] = rng.choice([-1, -5, N, N + 7, 2 ** 31 - 1], size=m.sum())
+    if case == "single":
+        idx[:] = -1
+        idx[np.arange(Tq), rng.integers(0, W, Tq)] = rng.integers(0, N, Tq)
+    if case == "duplicates":
+        idx[:, 100:] = idx[:, :W - 100]
+    if case == "rising":
+        idx[:, :64] = rng.integers(0, N // 2, size=(Tq, 64))
+        idx[:, 64:] = rng.integers(N // 2, N, size=(Tq, W - 64))
+    if case in ("max_width", "many_queries"):
+        idx[1::2][rng.random((len(idx[1::2]), W)) < 0.3] = -1
+        idx[0::7] = -1
+    _log("mla rope tail", case, (Tq, H, DQ), W)
+    scale = 1 / np.sqrt(DQ)
+    g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), scale)
+    assert tuple(g_out.shape) == (Tq, H, 512)
+    ref_out, ref_lse, ref_abs = oracle_mod.sparse_mla_dv(q, kv, idx, scale, 512, with_abs=True)
+    scaled = case == "rising"
+    info = check_out(host_bf16_f32(g_out), ref_out, case, ref_abs, scaled=scaled)
+    info["lse"] = check_lse(host(g_lse), ref_lse, case, scaled=scaled)
+    # the tail matters: dropping it (attention over the first 512 key columns) differs
+    if case == "dense_2k_rows":
+        no_tail, _ = oracle_mod.sparse_mla_dv(np.ascontiguousarray(q[:, :, :512]),
+                                              np.ascontiguousarray(kv[:, :512]), idx, scale, 512)
+        assert np.abs(no_tail - ref_out).max() > 10 * OUT_MAX
+    _log("  ", info)
