@@ -187,7 +187,7 @@ def main():
     nv = torch.empty(s.Tq, dtype=torch.int32, device=dev)
     out = torch.empty((s.Tq, s.H, s.D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((s.Tq, s.H), dtype=torch.float32, device=dev)
-    ws_bytes = K.kp_indexer_workspace_bytes(s.Tq, cap, s.H_I, s.D_I)
+    ws_bytes = K.kp_indexer_workspace_bytes(s.Tq, cap, s.H_I, s.D_I, s.topk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = P(stream.cuda_stream)

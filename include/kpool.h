@@ -29,6 +29,9 @@
  *   [P2-MLA] same page, "cuDNN sparse MLA parity and performance" (64 query
  *            heads, 512-wide latent, index_topk 2048, index_kpool 4: 2051 raw
  *            slots before alignment).
+ *   [P4-PW]  prime-rl PR "GLM-5.3-Flash text model", Patches and workarounds
+ *            (serving keeps hybrid KV blocks of index_kpool x 32 tokens, and
+ *            the indexer's paged-MQA kernel reads 32-pool pages).
  *
  * Conventions for every entry point:
  *   - Pointers named as device data are device pointers (hipMalloc or torch
@@ -161,8 +164,14 @@ kp_status kpool_build_from(const int32_t* cu_seqlens, int32_t num_docs, int32_t 
 kp_status indexer_rotate_quant(const uint16_t* q_idx, int32_t num_q, int32_t h_idx, int32_t d_idx,
                                uint8_t* codes, float* scales, hipStream_t stream);
 
-/* Bytes of workspace indexer_score_topk needs for these sizes. */
-size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx);
+/*
+ * Bytes of workspace indexer_score_topk needs for these sizes: the rotated
+ * queries, then either the score rows (num_q x max_pools fp32) or, on the
+ * fused path (max_pools >= 32768 and topk_pools <= 8192), 128 KiB of candidate
+ * list per query. 0 when num_q <= 0.
+ */
+size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx,
+                                  int32_t topk_pools);
 
 /*
  * indexer_score_topk -- FP8 indexer scoring and top-k index rows [P4-S3,
@@ -194,6 +203,17 @@ size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_id
  *   scores          device fp32 [num_q, max_pools]   (out, NULLABLE) I[i,p] for visible
  *                   pools, -inf elsewhere
  *   workspace       device memory of kp_indexer_workspace_bytes(...) bytes, 256-byte aligned
+ *
+ * Rows of many pools (decode over a long context): when scores == NULL,
+ * max_pools >= 32768 and topk_pools <= 8192, no score tensor is formed. Per
+ * query, a threshold is taken from the scores of every s-th pool (s >= 64);
+ * the scoring pass keeps only the (score, pool) pairs at or above it, at most
+ * 16384 per query, and the top-k is selected among them. The kept pools are
+ * the first k in the order "higher score first, then lower pool first", so
+ * whenever between k and 16384 pools clear the threshold they are all among
+ * the candidates; a row where that fails (adversarial score patterns only) is
+ * selected exactly by rescoring its pools. Either way the index rows are the
+ * ones the score-tensor path writes.
  */
 kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
                              const int32_t* cu_pools, int32_t max_pools,
@@ -214,7 +234,7 @@ kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_
  * library's load until the process ends; the call itself allocates nothing.
  * Sizes whose workspace (kp_indexer_workspace_bytes) exceeds that return
  * KP_ERR_UNSUPPORTED before anything is launched: the 64 decode queries of a
- * 1,048,576-token context fit (64.3 MiB). Every call on one GPU shares that
+ * 1,048,576-token context fit (8.3 MiB on the fused path). Every call on one GPU shares that
  * GPU's buffer, which keeps the last call's contents (no byte of it needs to
  * start at zero): calls that overlap on one GPU (on different streams, or
  * from different host threads) race and give undefined results; calls in one
@@ -230,6 +250,75 @@ kp_status indexer_score_topk_noalloc(const int32_t* cu_seqlens, int32_t num_docs
                                      int32_t topk_pools, int32_t row_width,
                                      int32_t* indices, int32_t* num_valid, float* scores,
                                      hipStream_t stream);
+
+/*
+ * Paged pooled-key cache [P4-PW]: physical pages of 32 * kpool token slots
+ * that also hold the 32 pools those tokens form (kpool 4: 128 tokens and 32
+ * pools per page). Document d (tokens cu_seqlens[d] .. cu_seqlens[d+1]-1, its
+ * length len_d) owns the pages page_table[d * max_pages + q], q = 0 ..
+ * max_pages - 1: its token l lives in slot page_table[d*max_pages + l / (32
+ * kpool)] * 32 kpool + l % (32 kpool) of every token-row array, and its pool j
+ * (tokens kpool*j .. kpool*j + kpool - 1, as in kpool_build) in row
+ * page_table[d*max_pages + j / 32] * 32 + j % 32 of every pool-row array. The
+ * packed numbering of cu_seqlens only describes lengths and query positions;
+ * nothing is stored in it. Pages need not be contiguous, in order, or
+ * distinct between documents' unused tail entries. A page-table entry outside
+ * [0, num_pages), or a token or pool past a document's max_pages pages, is a
+ * missing page: nothing there is read or written, and index-row entries that
+ * fall in it are -1.
+ */
+
+/*
+ * kpool_update_paged -- (re)compute the pooled keys of each document's pools
+ * whose last token is among its last `last_tokens` tokens [P4-S3, P4-PW]:
+ * decode appends tokens to the cache (their k_idx and gate rows written into
+ * their slots by the caller) and calls this with last_tokens = the number of
+ * tokens appended per document (the largest, when documents grew by
+ * different amounts: recomputing a pool rewrites the same bytes). Keys as in
+ * kpool_build, bit for bit.
+ *
+ *   page_table      device int32 [num_docs, max_pages]
+ *   num_pages       physical pages in the cache; num_pages * 32 * kpool < 2^31
+ *   k_idx_pages, gate_pages  device bf16 [num_pages * 32 * kpool, d_idx] (token rows)
+ *   ape             device fp32 [kpool, d_idx]
+ *   k8_pages        device uint8 [num_pages * 32, d_idx]   (out, pool rows)
+ *   sk_pages        device fp32  [num_pages * 32]          (out, pool rows)
+ *   last_tokens     >= 0 (0: nothing to do)
+ */
+kp_status kpool_update_paged(const int32_t* cu_seqlens, int32_t num_docs,
+                             const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                             const uint16_t* k_idx_pages, const uint16_t* gate_pages, const float* ape,
+                             int32_t d_idx, int32_t kpool, int32_t last_tokens,
+                             uint8_t* k8_pages, float* sk_pages, hipStream_t stream);
+
+/* Bytes of workspace indexer_score_topk_paged needs for these sizes. */
+size_t kp_indexer_paged_workspace_bytes(int32_t num_q, int32_t num_docs, int32_t h_idx, int32_t d_idx);
+
+/*
+ * indexer_score_topk_paged -- indexer_score_topk over a paged pooled-key cache
+ * [P4-S3, P4-PW], always on the fused path (no score tensor; topk_pools <=
+ * 8192). The selection is the one indexer_score_topk makes over the same keys
+ * in packed order; the index row entries are the page slots of the kept
+ * tokens (and of the query's own incomplete pool), so sparse_mla_fwd runs on a
+ * latent in the same pages (kv of num_pages * 32 * kpool rows).
+ *
+ *   num_tokens      cu_seqlens[num_docs]
+ *   k8_pages, sk_pages  as written by kpool_update_paged
+ *   row_path        device int32 [num_q] (out, NULLABLE): 0 when the row was
+ *                   selected among its candidates, 1 when it was rescored
+ *   workspace       kp_indexer_paged_workspace_bytes(num_q, num_docs, h_idx, d_idx)
+ *                   bytes, 256-byte aligned
+ *   (other arguments as in indexer_score_topk)
+ */
+kp_status indexer_score_topk_paged(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                   const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                                   const uint8_t* k8_pages, const float* sk_pages,
+                                   const int32_t* q_pos, int32_t num_q,
+                                   const uint16_t* q_idx, const float* w_idx,
+                                   int32_t h_idx, int32_t d_idx, int32_t kpool,
+                                   int32_t topk_pools, int32_t row_width,
+                                   int32_t* indices, int32_t* num_valid, int32_t* row_path,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * indexer_topk_from_scores -- the selection step alone, on a given score

@@ -29,11 +29,15 @@ SIGNATURES = [
     ("kpool_build", _I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
     ("kpool_build_from", _I, [_P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     ("indexer_rotate_quant", _I, [_P, _I, _I, _I, _P, _P, _P]),
-    ("kp_indexer_workspace_bytes", _Z, [_I, _I, _I, _I]),
+    ("kp_indexer_workspace_bytes", _Z, [_I, _I, _I, _I, _I]),
     ("indexer_score_topk", _I, [_P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                 _P, _P, _P, _P, _Z, _P]),
     ("indexer_score_topk_noalloc", _I, [_P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                         _P, _P, _P, _P]),
+    ("kpool_update_paged", _I, [_P, _I, _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
+    ("kp_indexer_paged_workspace_bytes", _Z, [_I, _I, _I, _I]),
+    ("indexer_score_topk_paged", _I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                      _P, _P, _P, _P, _Z, _P]),
     ("indexer_topk_from_scores", _I, [_P, _I, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
     ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     ("kp_mla_bwd_workspace_bytes", _Z, [_I, _I]),
@@ -123,8 +127,12 @@ def kp_version() -> int:
     return int(lib().kp_version())
 
 
-def kp_indexer_workspace_bytes(num_q: int, max_pools: int, h_idx: int, d_idx: int) -> int:
-    return int(lib().kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx))
+def kp_indexer_workspace_bytes(num_q: int, max_pools: int, h_idx: int, d_idx: int, topk_pools: int) -> int:
+    return int(lib().kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx, topk_pools))
+
+
+def kp_indexer_paged_workspace_bytes(num_q: int, num_docs: int, h_idx: int, d_idx: int) -> int:
+    return int(lib().kp_indexer_paged_workspace_bytes(num_q, num_docs, h_idx, d_idx))
 
 
 # -------------------------------------------------------------- entry points --
@@ -217,7 +225,7 @@ def indexer_score_topk(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, pooled_
     indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
     num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
     scores = torch.empty((Tq, max_pools), dtype=torch.float32, device=dev) if return_scores else None
-    need = kp_indexer_workspace_bytes(Tq, max_pools, h, d)
+    need = kp_indexer_workspace_bytes(Tq, max_pools, h, d, topk_pools)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib().indexer_score_topk(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, num_tokens, _ptr(cu_pools),
@@ -269,6 +277,73 @@ def indexer_score_topk_noalloc(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor,
                                             _ptr(q_idx), _ptr(w_idx), h, d, kpool, topk_pools, W, _ptr(indices),
                                             _ptr(num_valid), _ptr(scores), _stream(dev)))
     return indices, num_valid, scores
+
+
+def kpool_update_paged(cu_seqlens: torch.Tensor, page_table: torch.Tensor, k_idx_pages: torch.Tensor,
+                       gate_pages: torch.Tensor, ape: torch.Tensor, k8_pages: torch.Tensor, sk_pages: torch.Tensor,
+                       last_tokens: int, kpool: int = 4) -> None:
+    """Pool, rotate and quantise into a paged cache the pools whose last token is
+    among each document's last ``last_tokens`` tokens (writes k8_pages, sk_pages)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    B = cu_seqlens.shape[0] - 1
+    _need(page_table, "page_table", torch.int32, (B, None))
+    max_pages = page_table.shape[1]
+    _need(k8_pages, "k8_pages", torch.uint8, (None, None))
+    num_pages = k8_pages.shape[0] // 32
+    d = k8_pages.shape[1]
+    if k8_pages.shape[0] != 32 * num_pages:
+        raise ValueError(f"k8_pages must have a multiple of 32 rows, got {k8_pages.shape[0]}")
+    _need(sk_pages, "sk_pages", torch.float32, (32 * num_pages,))
+    _need(k_idx_pages, "k_idx_pages", torch.bfloat16, (32 * kpool * num_pages, d))
+    _need(gate_pages, "gate_pages", torch.bfloat16, (32 * kpool * num_pages, d))
+    _need(ape, "ape", torch.float32, (kpool, d))
+    dev = _on(("cu_seqlens", cu_seqlens), ("page_table", page_table), ("k_idx_pages", k_idx_pages),
+              ("gate_pages", gate_pages), ("ape", ape), ("k8_pages", k8_pages), ("sk_pages", sk_pages))
+    _check(lib().kpool_update_paged(_ptr(cu_seqlens), B, _ptr(page_table), max_pages, num_pages, _ptr(k_idx_pages),
+                                    _ptr(gate_pages), _ptr(ape), d, kpool, last_tokens, _ptr(k8_pages),
+                                    _ptr(sk_pages), _stream(dev)))
+
+
+def indexer_score_topk_paged(cu_seqlens: torch.Tensor, page_table: torch.Tensor, k8_pages: torch.Tensor,
+                             sk_pages: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, num_tokens: int,
+                             kpool: int = 4, topk_pools: int = 512, row_width: Optional[int] = None,
+                             q_pos: Optional[torch.Tensor] = None, return_row_path: bool = False,
+                             workspace: Optional[torch.Tensor] = None):
+    """Fused FP8 scoring and top-k over a paged pooled-key cache. Index rows hold
+    page slots. Returns (indices int32 [Tq,W], num_valid int32 [Tq], row_path
+    int32 [Tq] or None)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (None,))
+    B = cu_seqlens.shape[0] - 1
+    _need(page_table, "page_table", torch.int32, (B, None))
+    max_pages = page_table.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16, (None, None, None))
+    Tq, h, d = q_idx.shape
+    _need(k8_pages, "k8_pages", torch.uint8, (None, d))
+    num_pages = k8_pages.shape[0] // 32
+    if k8_pages.shape[0] != 32 * num_pages:
+        raise ValueError(f"k8_pages must have a multiple of 32 rows, got {k8_pages.shape[0]}")
+    _need(sk_pages, "sk_pages", torch.float32, (32 * num_pages,))
+    _need(w_idx, "w_idx", torch.float32, (Tq, h))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (Tq,))
+    elif Tq != num_tokens:
+        raise ValueError(f"without q_pos every token is a query: q_idx must have {num_tokens} rows, got {Tq}")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, (None,))
+    dev = _on(("cu_seqlens", cu_seqlens), ("page_table", page_table), ("k8_pages", k8_pages),
+              ("sk_pages", sk_pages), ("q_idx", q_idx), ("w_idx", w_idx), ("q_pos", q_pos), ("workspace", workspace))
+    W = row_width if row_width is not None else kp_row_width(kpool, topk_pools)
+    indices = torch.empty((Tq, W), dtype=torch.int32, device=dev)
+    num_valid = torch.empty(Tq, dtype=torch.int32, device=dev)
+    row_path = torch.empty(Tq, dtype=torch.int32, device=dev) if return_row_path else None
+    need = kp_indexer_paged_workspace_bytes(Tq, B, h, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().indexer_score_topk_paged(_ptr(cu_seqlens), B, num_tokens, _ptr(page_table), max_pages, num_pages,
+                                          _ptr(k8_pages), _ptr(sk_pages), _ptr(q_pos), Tq, _ptr(q_idx), _ptr(w_idx),
+                                          h, d, kpool, topk_pools, W, _ptr(indices), _ptr(num_valid),
+                                          _ptr(row_path), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return indices, num_valid, row_path
 
 
 def indexer_topk_from_scores(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, scores: torch.Tensor,

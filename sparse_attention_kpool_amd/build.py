@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "kpool")
 LIB = os.path.join(PKG, "libkpool.so")
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "topk.hip", "fused_topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Every HIP source is compiled for gfx950 only, with packed-fp32 instruction

@@ -67,7 +67,7 @@ extern "C" {
 
 const char* kp_last_error(void) { return g_err.c_str(); }
 
-int32_t kp_version(void) { return 100; }
+int32_t kp_version(void) { return 200; }
 
 int32_t kp_row_width(int32_t kpool, int32_t topk_pools) {
     if (kpool < 1 || topk_pools < 0) return -1;
@@ -129,12 +129,32 @@ kp_status indexer_rotate_quant(const uint16_t* q_idx, int32_t num_q, int32_t h_i
     return ok();
 }
 
-size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx) {
-    if (num_q <= 0 || max_pools < 0 || h_idx < 1 || d_idx < 1) return 0;
+// Rows this long take the fused scoring + top-k when no scores are asked for:
+// its candidate lists (FT_CAP per query) are then no larger than the score rows.
+static bool fused_rows(int32_t max_pools, int32_t topk_pools) {
+    return max_pools >= 2 * kp::FT_CAP && topk_pools <= kp::FT_CAP / 2;
+}
+
+// Bytes of the fused path's state after q8 and sq: thresholds, counts, candidates.
+static size_t fused_state_bytes(int32_t num_q) {
+    return align256((size_t)num_q * 2 * sizeof(uint32_t)) + align256((size_t)num_q * sizeof(int32_t)) +
+           align256((size_t)num_q * kp::FT_CAP * sizeof(uint2));
+}
+
+size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx,
+                                  int32_t topk_pools) {
+    if (num_q <= 0 || max_pools < 0 || h_idx < 1 || d_idx < 1 || topk_pools < 0) return 0;
     size_t q8 = align256((size_t)num_q * h_idx * d_idx);
     size_t sq = align256((size_t)num_q * h_idx * sizeof(float));
-    size_t sc = align256((size_t)num_q * (size_t)max_pools * sizeof(float));
-    return q8 + sq + sc;
+    size_t rest = fused_rows(max_pools, topk_pools) ? fused_state_bytes(num_q)
+                                                    : align256((size_t)num_q * (size_t)max_pools * sizeof(float));
+    return q8 + sq + rest;
+}
+
+size_t kp_indexer_paged_workspace_bytes(int32_t num_q, int32_t num_docs, int32_t h_idx, int32_t d_idx) {
+    if (num_q <= 0 || num_docs < 0 || h_idx < 1 || d_idx < 1) return 0;
+    return align256((size_t)(num_docs + 1) * sizeof(int32_t)) + align256((size_t)num_q * h_idx * d_idx) +
+           align256((size_t)num_q * h_idx * sizeof(float)) + fused_state_bytes(num_q);
 }
 
 static kp_status check_topk_args(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
@@ -179,7 +199,8 @@ static kp_status check_score_topk_args(const int32_t* cu_seqlens, int32_t num_do
 
 // The launches of indexer_score_topk on a checked workspace of at least
 // kp_indexer_workspace_bytes bytes (none of it needs clearing: every byte a
-// kernel reads was written by an earlier kernel of the same call).
+// kernel reads was written by an earlier kernel of the same call). Rows of
+// many pools take the fused path (no score tensor) unless scores are asked for.
 static kp_status score_topk_launch(const int32_t* cu_seqlens, int32_t num_docs, const int32_t* cu_pools,
                                    int32_t max_pools, const uint8_t* pooled_k_fp8, const float* pooled_k_scale,
                                    const int32_t* q_pos, int32_t num_q, const uint16_t* q_idx, const float* w_idx,
@@ -188,12 +209,22 @@ static kp_status score_topk_launch(const int32_t* cu_seqlens, int32_t num_docs, 
                                    uint8_t* ws, hipStream_t stream) {
     uint8_t* q8 = ws;
     float* sq = reinterpret_cast<float*>(ws + align256((size_t)num_q * h_idx * d_idx));
-    float* sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4));
-    if (scores) sc = scores;
+    uint8_t* rest = reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4);
+    float* sc = scores ? scores : reinterpret_cast<float*>(rest);
 
     hipError_t e = kp::launch_rotate_quant(q_idx, (long long)num_q * h_idx, d_idx, hadamard_norm(d_idx), q8, sq,
                                            stream);
     if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    if (!scores && fused_rows(max_pools, topk_pools)) {
+        uint32_t* tau = reinterpret_cast<uint32_t*>(rest);
+        int32_t* count = reinterpret_cast<int32_t*>(rest + align256((size_t)num_q * 8));
+        uint2* cand = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(count) + align256((size_t)num_q * 4));
+        e = kp::launch_fused_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w_idx, h_idx, d_idx,
+                                  pooled_k_fp8, pooled_k_scale, max_pools, nullptr, 0, 0, topk_pools, row_width,
+                                  indices, num_valid, nullptr, tau, count, cand, stream);
+        if (e != hipSuccess) return hip_fail(e, "fused score + top-k launch");
+        return KP_OK;
+    }
     if (scores) {
         e = kp::launch_fill_f32(scores, (size_t)num_q * max_pools, -INFINITY, stream);
         if (e != hipSuccess) return hip_fail(e, "score fill launch");
@@ -222,7 +253,7 @@ kp_status indexer_score_topk(const int32_t* cu_seqlens, int32_t num_docs, int32_
                                          topk_pools, row_width, indices);
     if (st != KP_OK) return st;
     if (num_q == 0) return ok();
-    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx);
+    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx, topk_pools);
     if (!workspace || workspace_bytes < need)
         return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -283,7 +314,7 @@ kp_status indexer_score_topk_noalloc(const int32_t* cu_seqlens, int32_t num_docs
                                          topk_pools, row_width, indices);
     if (st != KP_OK) return st;
     if (num_q == 0) return ok();
-    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx);
+    const size_t need = kp_indexer_workspace_bytes(num_q, max_pools, h_idx, d_idx, topk_pools);
     if (need > (size_t)KP_NOALLOC_SCRATCH_BYTES)
         return fail(KP_ERR_UNSUPPORTED,
                     "indexer_score_topk_noalloc: these sizes need %zu bytes of workspace, above the library's "
@@ -297,6 +328,86 @@ kp_status indexer_score_topk_noalloc(const int32_t* cu_seqlens, int32_t num_docs
     return score_topk_launch(cu_seqlens, num_docs, cu_pools, max_pools, pooled_k_fp8, pooled_k_scale, q_pos,
                              num_q, q_idx, w_idx, h_idx, d_idx, kpool, topk_pools, row_width, indices, num_valid,
                              scores, ws, stream);
+}
+
+kp_status kpool_update_paged(const int32_t* cu_seqlens, int32_t num_docs,
+                             const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                             const uint16_t* k_idx_pages, const uint16_t* gate_pages, const float* ape,
+                             int32_t d_idx, int32_t kpool, int32_t last_tokens,
+                             uint8_t* k8_pages, float* sk_pages, hipStream_t stream) {
+    g_err.clear();
+    if (num_docs < 0 || max_pages < 0 || num_pages < 0 || last_tokens < 0)
+        return fail(KP_ERR_INVALID_ARG, "negative size");
+    if (kpool < 1 || kpool > 16) return fail(KP_ERR_UNSUPPORTED, "kpool must be in 1..16 (got %d)", kpool);
+    if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+    if ((long long)num_pages * 32 * kpool > 0x7FFFFFFFLL || (long long)num_docs * max_pages > 0x7FFFFFFFLL)
+        return fail(KP_ERR_UNSUPPORTED, "page cache too large for 32-bit slot numbers");
+    if (num_docs == 0 || last_tokens == 0 || max_pages == 0 || num_pages == 0) return ok();
+    if (!cu_seqlens || !page_table || !k_idx_pages || !gate_pages || !ape || !k8_pages || !sk_pages)
+        return fail(KP_ERR_INVALID_ARG, "cu_seqlens, page_table, k_idx_pages, gate_pages, ape, k8_pages and "
+                                        "sk_pages are required");
+    kp_status st = device_check();
+    if (st != KP_OK) return st;
+    hipError_t e = kp::launch_pool_paged(cu_seqlens, num_docs, page_table, max_pages, num_pages, k_idx_pages,
+                                         gate_pages, ape, d_idx, kpool, hadamard_norm(d_idx), k8_pages, sk_pages,
+                                         last_tokens, stream);
+    if (e != hipSuccess) return hip_fail(e, "kpool_update_paged launch");
+    return ok();
+}
+
+kp_status indexer_score_topk_paged(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,
+                                   const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                                   const uint8_t* k8_pages, const float* sk_pages,
+                                   const int32_t* q_pos, int32_t num_q,
+                                   const uint16_t* q_idx, const float* w_idx,
+                                   int32_t h_idx, int32_t d_idx, int32_t kpool,
+                                   int32_t topk_pools, int32_t row_width,
+                                   int32_t* indices, int32_t* num_valid, int32_t* row_path,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (num_docs < 0 || num_tokens < 0 || num_q < 0 || max_pages < 0 || num_pages < 0)
+        return fail(KP_ERR_INVALID_ARG, "negative size");
+    if (kpool < 1 || kpool > 16) return fail(KP_ERR_UNSUPPORTED, "kpool must be in 1..16 (got %d)", kpool);
+    if (topk_pools < 0) return fail(KP_ERR_INVALID_ARG, "topk_pools must be >= 0");
+    if (topk_pools > kp::FT_CAP / 2)
+        return fail(KP_ERR_UNSUPPORTED, "topk_pools must be at most %d on the paged path (got %d)", kp::FT_CAP / 2,
+                    topk_pools);
+    const long long need_w = (long long)kpool * topk_pools + kpool - 1;
+    if (row_width % 128 != 0 || row_width < need_w || row_width < 128)
+        return fail(KP_ERR_INVALID_ARG, "row_width %d must be a multiple of 128 and >= %lld", row_width, need_w);
+    if (h_idx < 1 || h_idx > 64) return fail(KP_ERR_UNSUPPORTED, "h_idx must be in 1..64 (got %d)", h_idx);
+    if (!pow2_idx(d_idx)) return fail(KP_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+    if ((long long)num_pages * 32 * kpool > 0x7FFFFFFFLL || (long long)num_docs * max_pages > 0x7FFFFFFFLL)
+        return fail(KP_ERR_UNSUPPORTED, "page cache too large for 32-bit slot numbers");
+    if (num_q == 0) return ok();
+    if (num_docs == 0 || num_tokens == 0) return fail(KP_ERR_INVALID_ARG, "queries need a non-empty row");
+    if (!q_pos && num_q != num_tokens) return fail(KP_ERR_INVALID_ARG, "q_pos == NULL requires num_q == num_tokens");
+    if (!cu_seqlens || !page_table || !k8_pages || !sk_pages || !q_idx || !w_idx || !indices)
+        return fail(KP_ERR_INVALID_ARG, "cu_seqlens, page_table, k8_pages, sk_pages, q_idx, w_idx and indices are "
+                                        "required");
+    const size_t need = kp_indexer_paged_workspace_bytes(num_q, num_docs, h_idx, d_idx);
+    if (!workspace || workspace_bytes < need)
+        return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    kp_status st = device_check();
+    if (st != KP_OK) return st;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* cu_pools = reinterpret_cast<int32_t*>(ws);
+    uint8_t* q8 = ws + align256((size_t)(num_docs + 1) * sizeof(int32_t));
+    float* sq = reinterpret_cast<float*>(q8 + align256((size_t)num_q * h_idx * d_idx));
+    uint8_t* rest = reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4);
+    uint32_t* tau = reinterpret_cast<uint32_t*>(rest);
+    int32_t* count = reinterpret_cast<int32_t*>(rest + align256((size_t)num_q * 8));
+    uint2* cand = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(count) + align256((size_t)num_q * 4));
+    hipError_t e = kp::launch_layout(cu_seqlens, num_docs, kpool, cu_pools, stream);
+    if (e != hipSuccess) return hip_fail(e, "layout launch");
+    e = kp::launch_rotate_quant(q_idx, (long long)num_q * h_idx, d_idx, hadamard_norm(d_idx), q8, sq, stream);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    e = kp::launch_fused_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w_idx, h_idx, d_idx,
+                              k8_pages, sk_pages, num_tokens / kpool, page_table, max_pages, num_pages, topk_pools,
+                              row_width, indices, num_valid, row_path, tau, count, cand, stream);
+    if (e != hipSuccess) return hip_fail(e, "fused score + top-k launch");
+    return ok();
 }
 
 kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, int32_t num_tokens,

@@ -1,0 +1,416 @@
+// Fused FP8 indexer scoring and top-k for rows of many pools (decode over a
+// long context): the [queries x pools] score tensor is never written.
+//
+// The selection is the one of topk.hip (prime-rl PR "GLM-5.3-Flash text
+// model", Summary, third bullet: the top-k visible pools by indexer score,
+// equal scores keeping the lower pool, listed ascending, then the query's own
+// incomplete pool); only the route to it differs. Order pools by (score key
+// descending, pool ascending): a total order in which the kept pools are
+// exactly the first k. Any threshold (key, pool) whose count of pools at or
+// above it lies in [k, cap] therefore holds every kept pool among those
+// candidates, and an exact selection over the candidates gives the answer.
+// Three launches:
+//
+//   1. fused_thresh_kernel, one workgroup per query: rows of at most `cap`
+//      visible pools take every pool as a candidate; longer rows score every
+//      s-th pool (s >= 64, at most 16384 samples) and take as threshold the
+//      sample of rank r = T*m/n in that order (m samples, n pools, T the
+//      target count max(2k, cap/2)), so about T pools clear it when the
+//      samples are representative. Only its count decides correctness.
+//   2. score_kernel in its emitting form (score.hip) scores every visible
+//      pair and appends the pairs at or above the threshold, as (key, pool),
+//      to the query's candidate list, counting all of them.
+//   3. fused_select_kernel, one workgroup per query: when the count lies in
+//      [k, cap], a radix select over the candidates in LDS (ties on the key
+//      resolved by a second select over the pools), then a bitonic sort of
+//      the k kept pools; otherwise (adversarial rows only) the workgroup
+//      rescores every visible pool itself for each digit of an exact radix
+//      select and writes the kept pools in one ordered pass.
+//
+// Scores here are computed as score_kernel computes them, bit for bit: the
+// same MFMA dots (16 heads x 16 pools per v_mfma_f32_16x16x128_f8f6f4, the
+// heads on the M dimension because one query is scored), then, per pool,
+// acc = fma(w*sq of head h, ReLU(dot_h), acc) over h in order from acc = 0,
+// and acc * sk; the running sum hops across the four 16-lane groups that hold
+// the heads in turn.
+//
+// Pooled keys are addressed by global pool number, or through a page table of
+// 32-pool pages; index rows then hold the page slots of the kept tokens.
+#include "kp_device.h"
+#include "kp_launch.h"
+#include "kp_select.h"
+
+namespace kp {
+
+constexpr int FT_SAMPLE_MAX = 16384;   // sampled pools per query
+constexpr int FT_STRIDE_MIN = 64;      // sampling stride, at least
+constexpr int FT_TH_THREADS = 512;
+constexpr int FT_SEL_THREADS = 1024;
+constexpr int FT_SEL_WAVES = FT_SEL_THREADS / 64;
+
+// Pooled-key rows, by global pool number or through 32-pool pages.
+struct KeyRows {
+    const uint8_t* k8;
+    const float* sk;
+    const int32_t* table;   // nullptr: row = pool number
+    int max_pages;
+    int num_pages;          // page numbers outside [0, num_pages): no page
+};
+
+// Row of pool p of the document whose first pool is plo and whose page-table
+// row starts at tab (-1: its page is missing or past the table row).
+__device__ __forceinline__ long long key_row(const KeyRows& kr, int p, int plo, long long tab) {
+    if (!kr.table) return p;
+    const int l = p - plo;
+    if ((l >> 5) >= kr.max_pages) return -1;
+    const int pn = kr.table[tab + (l >> 5)];
+    return (unsigned)pn < (unsigned)kr.num_pages ? (long long)pn * 32 + (l & 31) : -1;
+}
+
+// One query's operands with its heads as the MFMA's rows: a[hg] holds, in
+// lane (n, g), bytes 32g .. 32g+31 of the codes of head 16*hg + n (zero past
+// d_idx and past h_idx); wv[hg][e] = w*sq of head 16*hg + 4g + e.
+struct HmQuery {
+    i32x8 a[4];
+    float wv[4][4];
+};
+
+__device__ __forceinline__ void hm_load_query(HmQuery& hq, const uint8_t* __restrict__ q8,
+                                              const float* __restrict__ sq, const float* __restrict__ w, int i,
+                                              int h_idx, int d_idx) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int dchunks = d_idx >> 4;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+        const int head = 16 * hg + n;
+        uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
+        if (head < h_idx) {
+            const uint8_t* src = q8 + ((size_t)i * h_idx + head) * d_idx + 32 * g;
+            if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src);
+            if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 16);
+        }
+        hq.a[hg] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int h = 16 * hg + 4 * g + e;
+            const size_t o = (size_t)i * h_idx + h;
+            hq.wv[hg][e] = h < h_idx ? w[o] * sq[o] : 0.0f;
+        }
+    }
+}
+
+// Key of pool n of a 16-pool tile for the query of hq: lane (n, g) names the
+// pool's key row (row < 0: no pool, key 0) and every lane of column n gets the
+// key. Called by whole waves.
+__device__ __forceinline__ uint32_t hm_tile_key(const HmQuery& hq, int h_idx, int d_idx, const KeyRows& kr,
+                                                long long row) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int dchunks = d_idx >> 4;
+    uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
+    float s = 0.0f;
+    if (row >= 0) {
+        const uint8_t* src = kr.k8 + (size_t)row * d_idx + 32 * g;
+        if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src);
+        if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 16);
+        s = kr.sk[row];
+    }
+    const i32x8 b = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+    f32x4 d[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg)
+        d[hg] = 16 * hg < h_idx ? mfma_fp8_16x16x128(hq.a[hg], b, f32x4{0.f, 0.f, 0.f, 0.f}) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // heads 16hg + 4gp .. +3 sit in lane group gp: each group folds its four
+    // into the running sum, and the sum of group gp goes on to every lane
+    float acc = 0.0f;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp) {
+            if (16 * hg + 4 * gp < h_idx) {
+                float t = acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * hg + 4 * g + e < h_idx) t = __builtin_fmaf(hq.wv[hg][e], relu_f32(d[hg][e]), t);
+                acc = __shfl(t, n + 16 * gp, 64);
+            }
+        }
+    }
+    return row >= 0 ? score_key(acc * s) : 0u;
+}
+
+// Key of the pool of lane (16g + n) among 64 consecutive entries (4 tiles);
+// row_of(j) gives lane (n, *)'s key row for tile j.
+template <typename RowOf>
+__device__ __forceinline__ uint32_t hm_block_key(const HmQuery& hq, int h_idx, int d_idx, const KeyRows& kr,
+                                                 RowOf row_of) {
+    const int g = (threadIdx.x & 63) >> 4;
+    uint32_t mine = 0u;
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t k = hm_tile_key(hq, h_idx, d_idx, kr, row_of(j));
+        if (g == j) mine = k;
+    }
+    return mine;
+}
+
+// ------------------------------------------------------------ threshold -----
+template <bool PAGED>
+__global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const uint8_t* __restrict__ q8, const float* __restrict__ sq,
+    const float* __restrict__ w, int h_idx, int d_idx, KeyRows kr, int topk, int cap,
+    uint32_t* __restrict__ tau, int32_t* __restrict__ count) {
+    constexpr int NTH = FT_TH_THREADS, NW = NTH / 64;
+    __shared__ __align__(16) uint32_t keys[FT_SAMPLE_MAX];
+    __shared__ int hist[2][RS_BINS];
+    __shared__ int wave_buf[NW];
+    __shared__ int sel[3];
+    __shared__ int found;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15;
+    const int i = blockIdx.x;
+    const int t = q_pos ? q_pos[i] : i;
+    const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
+    const int n = qp.n_vis;
+    const int k = n < topk ? n : topk;
+    if (k == 0 || n <= cap) {
+        // nothing to keep: a threshold above every (key, pool); short row: every pool
+        if (tid == 0) {
+            tau[2 * i] = k == 0 ? 0xFFFFFFFFu : 0u;
+            tau[2 * i + 1] = k == 0 ? 0xFFFFFFFFu : 0x7FFFFFFFu;
+            count[i] = 0;
+        }
+        return;
+    }
+    const int ss = max(FT_STRIDE_MIN, (n + FT_SAMPLE_MAX - 1) / FT_SAMPLE_MAX);
+    const int m = (n + ss - 1) / ss;   // samples: pools pool_lo + ss*j, j < m
+    const long long tab = PAGED ? (long long)qp.doc * kr.max_pages : 0;
+    HmQuery hq;
+    hm_load_query(hq, q8, sq, w, i, h_idx, d_idx);
+    for (int b0 = wave * 64; b0 < m; b0 += NW * 64) {
+        const uint32_t key = hm_block_key(hq, h_idx, d_idx, kr, [&](int j) -> long long {
+            const int s = b0 + 16 * j + n16;
+            return s < m ? key_row(kr, qp.pool_lo + ss * s, qp.pool_lo, tab) : -1;
+        });
+        if (b0 + lane < m) keys[b0 + lane] = key;
+    }
+    __syncthreads();
+
+    const long long target = max(2 * k, cap / 2);
+    const int r = (int)max(1LL, min((long long)m, target * m / n));
+    uint32_t th;
+    int teq;
+    radix_select<NTH>([&](auto f) {
+        for (int j = tid; j < m; j += NTH) f(keys[j]);
+    }, r, hist, sel, &th, &teq);
+    uint32_t tp = 0x7FFFFFFFu;
+    if (teq != RS_ALL_EQ) {
+        // the teq-th sample with key th, in pool order (samples are in pool order)
+        const int chunk = (m + NTH - 1) / NTH;
+        const int j0 = min(m, tid * chunk), j1 = min(m, j0 + chunk);
+        int c = 0;
+        for (int j = j0; j < j1; ++j) c += keys[j] == th;
+        int tot;
+        const int before = block_excl_scan<NTH>(c, wave_buf, &tot);
+        if (before < teq && before + c >= teq) {
+            int need = teq - before;
+            for (int j = j0; j < j1; ++j)
+                if (keys[j] == th && --need == 0) found = j;
+        }
+        __syncthreads();
+        tp = (uint32_t)(qp.pool_lo + ss * found);
+    }
+    if (tid == 0) {
+        tau[2 * i] = th;
+        tau[2 * i + 1] = tp;
+        count[i] = 0;
+    }
+}
+
+// -------------------------------------------------------------- select ------
+template <bool PAGED>
+__global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const uint8_t* __restrict__ q8, const float* __restrict__ sq,
+    const float* __restrict__ w, int h_idx, int d_idx, KeyRows kr, int topk, int cap,
+    const int32_t* __restrict__ count, const uint2* __restrict__ cand, int row_width,
+    int32_t* __restrict__ indices, int32_t* __restrict__ num_valid, int32_t* __restrict__ row_path) {
+    constexpr int NTH = FT_SEL_THREADS, NW = FT_SEL_WAVES;
+    constexpr int PER = FT_CAP / NTH;   // candidates per thread, at most
+    __shared__ __align__(16) uint32_t ckey[FT_CAP];   // candidate keys, then the kept pools
+    __shared__ __align__(16) int cpool[FT_CAP];
+    __shared__ int hist[2][RS_BINS];
+    __shared__ int wave_buf[NW];
+    __shared__ int sel[3];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15;
+    const int i = blockIdx.x;
+    const int t = q_pos ? q_pos[i] : i;
+    const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
+    const int n = qp.n_vis, lo = qp.pool_lo, hi = qp.pool_lo + qp.n_vis;
+    const int k = n < topk ? n : topk;
+    const int doc_start = cu[qp.doc];
+    const int page_tok = 32 * kpool;
+    const long long tab = PAGED ? (long long)qp.doc * kr.max_pages : 0;
+    int32_t* row = indices + (size_t)i * row_width;
+
+    // slot of the document's token l (l counted from its first token; -1 when
+    // its page is missing)
+    auto slot = [&](int l) -> int {
+        if (!PAGED) return doc_start + l;
+        if (l / page_tok >= kr.max_pages) return -1;
+        const int pn = kr.table[tab + l / page_tok];
+        return (unsigned)pn < (unsigned)kr.num_pages ? pn * page_tok + l % page_tok : -1;
+    };
+    // the kpool tokens of pool p at rank pos of the row (a pool's tokens share a page)
+    auto put_pool = [&](int pos, int p) {
+        const int s0 = slot(kpool * (p - lo));
+        const int st = s0 < 0 ? 0 : 1;
+        if (kpool == 4) {
+            *reinterpret_cast<int4*>(row + 4 * pos) = make_int4(s0, s0 + st, s0 + 2 * st, s0 + 3 * st);
+        } else {
+            for (int r = 0; r < kpool; ++r) row[pos * kpool + r] = s0 + r * st;
+        }
+    };
+
+    const int cnt = count[i];
+    const bool fits = k > 0 && cnt >= k && cnt <= cap;
+    if (fits) {
+        for (int j = tid; j < cnt; j += NTH) {
+            const uint2 c = cand[(size_t)i * cap + j];
+            ckey[j] = c.x;
+            cpool[j] = (int)c.y;
+        }
+        __syncthreads();
+        uint32_t th = 0u, th2 = 0u;
+        int teq = RS_ALL_EQ;
+        if (k < cnt) {
+            radix_select<NTH>([&](auto f) {
+                for (int j = tid; j < cnt; j += NTH) f(ckey[j]);
+            }, k, hist, sel, &th, &teq);
+            if (teq != RS_ALL_EQ) {
+                // keys equal to th: keep the teq lowest pools (largest ~pool);
+                // pools are distinct, so this select is exact
+                int teq2;
+                radix_select<NTH>([&](auto f) {
+                    for (int j = tid; j < cnt; j += NTH)
+                        if (ckey[j] == th) f(~(uint32_t)cpool[j]);
+                }, teq, hist, sel, &th2, &teq2);
+            }
+        }
+        // kept flags of this thread's candidates j = tid + NTH*s, then their ranks
+        uint32_t keep = 0u;
+        int nk = 0;
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int j = tid + NTH * s;
+            if (j < cnt) {
+                const uint32_t v = ckey[j];
+                const bool kp = teq == RS_ALL_EQ ? v >= th : (v > th || (v == th && ~(uint32_t)cpool[j] >= th2));
+                keep |= (uint32_t)kp << s;
+                nk += kp;
+            }
+        }
+        int tot;
+        int pos = block_excl_scan<NTH>(nk, wave_buf, &tot);   // (its barriers end every read of ckey)
+        int* list = reinterpret_cast<int*>(ckey);
+#pragma unroll
+        for (int s = 0; s < PER; ++s)
+            if (keep >> s & 1u) list[pos++] = cpool[tid + NTH * s];
+        // ascending pools: bitonic sort of the k kept (tot == k), padded to a power of two
+        int P = 1;
+        while (P < tot) P <<= 1;
+        for (int p = tot + tid; p < P; p += NTH) list[p] = 0x7FFFFFFF;
+        __syncthreads();
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int p = tid; p < P / 2; p += NTH) {
+                    const int a_i = 2 * stride * (p / stride) + (p % stride), b_i = a_i + stride;
+                    const bool up = (a_i & size) == 0;
+                    const int a = list[a_i], b = list[b_i];
+                    if ((a > b) == up) {
+                        list[a_i] = b;
+                        list[b_i] = a;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int p = tid; p < min(tot, k); p += NTH) put_pool(p, list[p]);   // (tot == k)
+    } else if (k > 0) {
+        // exact selection by rescoring every visible pool for each digit
+        HmQuery hq;
+        hm_load_query(hq, q8, sq, w, i, h_idx, d_idx);
+        auto block_key = [&](int base) -> uint32_t {   // key of pool base + lane (0 past hi)
+            return hm_block_key(hq, h_idx, d_idx, kr, [&](int j) -> long long {
+                const int p = base + 16 * j + n16;
+                return p < hi ? key_row(kr, p, lo, tab) : -1;
+            });
+        };
+        uint32_t th;
+        int teq;
+        radix_select<NTH>([&](auto f) {
+            for (int base = lo + wave * 64; base < hi; base += NW * 64) {
+                const uint32_t key = block_key(base);
+                if (base + lane < hi) f(key);
+            }
+        }, k, hist, sel, &th, &teq);
+        // one ordered pass: every pool above th, and the first teq equal to th
+        int eq_run = 0, pos_run = 0;
+        for (int base = lo; base < hi; base += NW * 64) {
+            const int p = base + wave * 64 + lane;
+            const uint32_t key = block_key(base + wave * 64);
+            const bool valid = p < hi;
+            const bool eq = valid && teq != RS_ALL_EQ && key == th;
+            const bool gt = valid && (teq == RS_ALL_EQ ? key >= th : key > th);
+            int tot_eq, tot_keep;
+            const int eqb = eq_run + block_excl_scan<NTH>(eq, wave_buf, &tot_eq);
+            const bool kp = gt || (eq && eqb < teq);
+            const int pos = pos_run + block_excl_scan<NTH>(kp, wave_buf, &tot_keep);
+            if (kp && pos < k) put_pool(pos, p);   // (exactly k are kept)
+            eq_run += tot_eq;
+            pos_run += tot_keep;
+        }
+    }
+    // own incomplete pool, then padding
+    const int base = k * kpool;
+    const int n_tail = t - qp.tail_start + 1;
+    for (int r = tid; r < row_width - base; r += NTH)
+        row[base + r] = r < n_tail ? slot(kpool * n + r) : -1;
+    if (tid == 0) {
+        if (num_valid) num_valid[i] = base + n_tail;
+        if (row_path) row_path[i] = fits || k == 0 ? 0 : 1;
+    }
+}
+
+hipError_t launch_fused_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                             const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq, const float* w,
+                             int h_idx, int d_idx, const uint8_t* k8, const float* sk, int max_pools,
+                             const int32_t* page_table, int max_pages, int num_pages, int topk, int row_width,
+                             int32_t* indices, int32_t* num_valid, int32_t* row_path, uint32_t* tau, int32_t* count,
+                             uint2* cand, hipStream_t stream) {
+    if (num_q == 0) return hipSuccess;
+    const KeyRows kr{k8, sk, page_table, max_pages, num_pages};
+    if (page_table)
+        fused_thresh_kernel<true><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w,
+                                                                      h_idx, d_idx, kr, topk, FT_CAP, tau, count);
+    else
+        fused_thresh_kernel<false><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq,
+                                                                       w, h_idx, d_idx, kr, topk, FT_CAP, tau, count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_score_emit(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx, k8, sk, max_pools,
+                          page_table, max_pages, num_pages, tau, count, cand, FT_CAP, stream);
+    if (e != hipSuccess) return e;
+    if (page_table)
+        fused_select_kernel<true><<<num_q, FT_SEL_THREADS, 0, stream>>>(
+            cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w, h_idx, d_idx, kr, topk, FT_CAP, count, cand, row_width,
+            indices, num_valid, row_path);
+    else
+        fused_select_kernel<false><<<num_q, FT_SEL_THREADS, 0, stream>>>(
+            cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w, h_idx, d_idx, kr, topk, FT_CAP, count, cand, row_width,
+            indices, num_valid, row_path);
+    return hipGetLastError();
+}
+
+}  // namespace kp

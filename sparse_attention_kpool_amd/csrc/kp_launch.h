@@ -14,6 +14,16 @@ hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, c
                               float norm, int32_t* cu_pools, int32_t* pool_start, uint8_t* k8,
                               float* ks, float* kf32, int token_lo, hipStream_t stream);
 
+// Pool layout alone (cu_pools from the document lengths).
+hipError_t launch_layout(const int32_t* cu, int num_docs, int kpool, int32_t* cu_pools, hipStream_t stream);
+
+// Rotated FP8 pooled keys of the pools whose last token is among each
+// document's last `last_tokens` tokens, in a paged cache (token rows in pages of
+// 32*kpool slots, pool rows in pages of 32, both through the page table).
+hipError_t launch_pool_paged(const int32_t* cu, int num_docs, const int32_t* table, int max_pages, int num_pages,
+                             const uint16_t* k_idx, const uint16_t* gate, const float* ape, int d_idx, int kpool,
+                             float norm, uint8_t* k8, float* ks, int last_tokens, hipStream_t stream);
+
 // Rotated FP8 indexer queries: rows = num_q * h_idx vectors of d_idx channels.
 hipError_t launch_rotate_quant(const uint16_t* q_idx, long long rows, int d_idx, float norm,
                                uint8_t* codes, float* scales, hipStream_t stream);
@@ -26,6 +36,27 @@ hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools
                         const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
                         const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
                         int max_pools, float* scores, hipStream_t stream);
+
+// Scoring that appends (key, pool) candidates at or above a per-query
+// threshold instead of storing scores (page_table == nullptr: key row = pool).
+hipError_t launch_score_emit(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                             const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
+                             const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
+                             int max_pools, const int32_t* page_table, int max_pages, int num_pages,
+                             const uint32_t* tau, int32_t* count, uint2* cand, int cap, hipStream_t stream);
+
+// Candidates kept per query by the fused scoring + top-k.
+constexpr int FT_CAP = 16384;
+
+// Fused scoring + top-k (no score tensor): threshold, emission, selection.
+// Workspace: tau [num_q][2] u32, count [num_q] i32, cand [num_q][FT_CAP] uint2.
+// topk <= FT_CAP / 2. With a page table, index rows hold page slots.
+hipError_t launch_fused_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                             const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq, const float* w,
+                             int h_idx, int d_idx, const uint8_t* k8, const float* sk, int max_pools,
+                             const int32_t* page_table, int max_pages, int num_pages, int topk, int row_width,
+                             int32_t* indices, int32_t* num_valid, int32_t* row_path, uint32_t* tau, int32_t* count,
+                             uint2* cand, hipStream_t stream);
 
 // Top-k index rows from a score tensor (visible entries only are read).
 hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,

@@ -1,0 +1,121 @@
+// Selection helpers shared by the top-k kernels: the order-preserving score
+// key, wave and block scans, and a most-significant-digit-first radix select.
+#pragma once
+
+#include "kp_device.h"
+
+namespace kp {
+
+// Order-preserving 32-bit key of a score: a larger score has a larger key;
+// -0 is folded onto +0 and NaN sorts below -inf (key 0).
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;                       // -0 == +0
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0u;  // NaN: lowest
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast 15 and 31 carry the
+// row totals into the rows above.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// Exclusive scan of one int per thread over a block of NTH threads; returns
+// the prefix and writes the total to *total.
+template <int NTH>
+__device__ __forceinline__ int block_excl_scan(int v, int* wave_buf, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int x = wave_incl_scan(v);
+    if (lane == 63) wave_buf[wave] = x;
+    __syncthreads();
+    int add = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NTH / 64; ++w) {
+        int t = wave_buf[w];
+        if (w < wave) add += t;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return add + x - v;
+}
+
+constexpr int RS_BINS = 2048;             // histogram bins of the widest digit
+constexpr int RS_ALL_EQ = 0x7FFFFFFF;     // the boundary bin is kept whole
+
+// k-th largest key by a most-significant-digit-first radix select over
+// digits of 11, 11 and 10 bits, histograms in LDS. visit(f) calls f(key) for
+// every key of this thread's share (the shares of the NTH threads together
+// are the keys taking part; a pass may visit them in any order, the same set
+// each time). Requires 0 < k <= number of keys. On return *thresh is the key K
+// of the k-th largest and *take_eq the number of keys equal to K that are
+// kept (which ones is the caller's tie rule), or, when a digit's boundary bin
+// is kept whole, *thresh is that bin's prefix (lower bits zero), *take_eq =
+// RS_ALL_EQ, and exactly k keys are >= *thresh. Called by all NTH threads of
+// the block; hist is [2][RS_BINS], sel holds 3 ints.
+template <int NTH, typename Visit>
+__device__ __forceinline__ void radix_select(Visit visit, int k, int (*hist)[RS_BINS], int* sel,
+                                             uint32_t* thresh, int* take_eq) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int b = tid; b < RS_BINS; b += NTH) hist[0][b] = 0;
+    __syncthreads();
+    int remaining = k;
+    uint32_t prefix = 0u, pmask = 0u;
+    int teq = -1;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int width = pass < 2 ? 11 : 10;
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = 1 << width;
+        int* h = hist[pass & 1];
+        visit([&](uint32_t v) {
+            if ((v & pmask) == prefix) atomicAdd(&h[(v >> shift) & (uint32_t)(nb - 1)], 1);
+        });
+        for (int b = tid; b < RS_BINS; b += NTH) hist[(pass + 1) & 1][b] = 0;
+        __syncthreads();
+        if (wave == 0) {
+            // lane l owns bins [nb - per*(l+1), nb - per*l): a scan over lanes
+            // counts the keys in the bins above each lane's
+            const int per = nb >> 6;
+            const int base = nb - per * (lane + 1);
+            int own = 0;
+            for (int m = 0; m < per; ++m) own += h[base + m];
+            const int incl = wave_incl_scan(own);
+            const int before = incl - own;
+            if (before < remaining && incl >= remaining) {
+                int acc = before;
+                for (int m = per - 1; m >= 0; --m) {
+                    const int c = h[base + m];
+                    if (acc < remaining && acc + c >= remaining) {
+                        sel[0] = base + m;
+                        sel[1] = acc;
+                        sel[2] = c;
+                    }
+                    acc += c;
+                }
+            }
+        }
+        __syncthreads();
+        // (sel is rewritten only after the next digit's histogram barrier)
+        const int sel_digit = sel[0], sel_above = sel[1], sel_cnt = sel[2];
+        remaining -= sel_above;
+        prefix |= (uint32_t)sel_digit << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        if (sel_cnt == remaining) {
+            teq = RS_ALL_EQ;
+            break;
+        }
+    }
+    *thresh = prefix;
+    *take_eq = teq < 0 ? remaining : teq;
+}
+
+}  // namespace kp

@@ -88,6 +88,68 @@ __device__ __forceinline__ uint32_t quant4(const float (&x)[4], float* scale_out
 }
 
 // ------------------------------------------------------------ keys ----------
+// Channels 4j .. 4j+3 of the pooled key (before rotation) of the kpool tokens
+// whose k_idx and gate rows are tok_row(0) .. tok_row(kpool-1): per channel, a
+// softmax over the pool's tokens of gate + ape, then the weighted sum of k_idx.
+template <int L, int KP, typename TokRow>
+__device__ __forceinline__ void pool_vector(float (&x)[4], const uint16_t* __restrict__ k_idx,
+                                            const uint16_t* __restrict__ gate, const float* __restrict__ ape,
+                                            int kpool, int j, TokRow tok_row) {
+    constexpr int N = 4 * L;
+    if (KP > 0) {
+        // max-subtracted softmax over a fixed pool size, values held in registers
+        float a[KP > 0 ? KP : 1][4], kv[KP > 0 ? KP : 1][4];
+        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            const size_t r = tok_row(i);
+            uint2 g = reinterpret_cast<const uint2*>(gate + r * N)[j];
+            uint2 k = reinterpret_cast<const uint2*>(k_idx + r * N)[j];
+            float4 e = reinterpret_cast<const float4*>(ape + (size_t)i * N)[j];
+            a[i][0] = bf16_lo(g.x) + e.x; a[i][1] = bf16_hi(g.x) + e.y;
+            a[i][2] = bf16_lo(g.y) + e.z; a[i][3] = bf16_hi(g.y) + e.w;
+            kv[i][0] = bf16_lo(k.x); kv[i][1] = bf16_hi(k.x);
+            kv[i][2] = bf16_lo(k.y); kv[i][3] = bf16_hi(k.y);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m[c] = fmaxf(m[c], a[i][c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float den = 0.0f, num = 0.0f;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) {
+                float e = expf(a[i][c] - m[c]);
+                den += e;
+                num += e * kv[i][c];
+            }
+            x[c] = num / den;
+        }
+    } else {
+        // any pool size: running max with rescaled partial sums
+        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        float den[4] = {0.f, 0.f, 0.f, 0.f}, num[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kpool; ++i) {
+            const size_t r = tok_row(i);
+            uint2 g = reinterpret_cast<const uint2*>(gate + r * N)[j];
+            uint2 k = reinterpret_cast<const uint2*>(k_idx + r * N)[j];
+            float4 e = reinterpret_cast<const float4*>(ape + (size_t)i * N)[j];
+            float av[4] = {bf16_lo(g.x) + e.x, bf16_hi(g.x) + e.y, bf16_lo(g.y) + e.z, bf16_hi(g.y) + e.w};
+            float kk[4] = {bf16_lo(k.x), bf16_hi(k.x), bf16_lo(k.y), bf16_hi(k.y)};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float mn = fmaxf(m[c], av[c]);
+                float r2 = expf(m[c] - mn);   // 0 on the first token
+                float w = expf(av[c] - mn);
+                den[c] = den[c] * r2 + w;
+                num[c] = num[c] * r2 + w * kk[c];
+                m[c] = mn;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = num[c] / den[c];
+    }
+}
+
 // One pool per L lanes. Capacity rows (num_tokens / kpool) past the last pool
 // get pool_start -1, zero codes and a zero scale.
 template <int L, int KP>
@@ -114,64 +176,58 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
     const int s = cu[d] + kpool * (p - cu_pools[d]);
     if (s + kpool - 1 < token_lo) return;   // a pool of the caller's cache
 
-    // per-channel softmax over the kpool tokens of the pool, then the weighted sum
     float x[4];
-    if (KP > 0) {
-        // max-subtracted softmax over a fixed pool size, values held in registers
-        float a[KP > 0 ? KP : 1][4], kv[KP > 0 ? KP : 1][4];
-        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-        for (int i = 0; i < KP; ++i) {
-            uint2 g = reinterpret_cast<const uint2*>(gate + (size_t)(s + i) * N)[j];
-            uint2 k = reinterpret_cast<const uint2*>(k_idx + (size_t)(s + i) * N)[j];
-            float4 e = reinterpret_cast<const float4*>(ape + (size_t)i * N)[j];
-            a[i][0] = bf16_lo(g.x) + e.x; a[i][1] = bf16_hi(g.x) + e.y;
-            a[i][2] = bf16_lo(g.y) + e.z; a[i][3] = bf16_hi(g.y) + e.w;
-            kv[i][0] = bf16_lo(k.x); kv[i][1] = bf16_hi(k.x);
-            kv[i][2] = bf16_lo(k.y); kv[i][3] = bf16_hi(k.y);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) m[c] = fmaxf(m[c], a[i][c]);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float den = 0.0f, num = 0.0f;
-#pragma unroll
-            for (int i = 0; i < KP; ++i) {
-                float e = expf(a[i][c] - m[c]);
-                den += e;
-                num += e * kv[i][c];
-            }
-            x[c] = num / den;
-        }
-    } else {
-        // any pool size: running max with rescaled partial sums
-        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        float den[4] = {0.f, 0.f, 0.f, 0.f}, num[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < kpool; ++i) {
-            uint2 g = reinterpret_cast<const uint2*>(gate + (size_t)(s + i) * N)[j];
-            uint2 k = reinterpret_cast<const uint2*>(k_idx + (size_t)(s + i) * N)[j];
-            float4 e = reinterpret_cast<const float4*>(ape + (size_t)i * N)[j];
-            float av[4] = {bf16_lo(g.x) + e.x, bf16_hi(g.x) + e.y, bf16_lo(g.y) + e.z, bf16_hi(g.y) + e.w};
-            float kk[4] = {bf16_lo(k.x), bf16_hi(k.x), bf16_lo(k.y), bf16_hi(k.y)};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float mn = fmaxf(m[c], av[c]);
-                float r = expf(m[c] - mn);   // 0 on the first token
-                float w = expf(av[c] - mn);
-                den[c] = den[c] * r + w;
-                num[c] = num[c] * r + w * kk[c];
-                m[c] = mn;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = num[c] / den[c];
-    }
+    pool_vector<L, KP>(x, k_idx, gate, ape, kpool, j, [&](int i) { return (size_t)(s + i); });
     if (kf32) reinterpret_cast<float4*>(kf32 + (size_t)p * N)[j] = make_float4(x[0], x[1], x[2], x[3]);
     fwht4<L>(x, lane, norm);
     float sc;
     uint32_t codes = quant4<L>(x, &sc);
     reinterpret_cast<uint32_t*>(k8 + (size_t)p * N)[j] = codes;
     if (j == 0) { ks[p] = sc; pool_start[p] = s; }
+}
+
+// Paged cache: document d's tokens live in pages of 32*kpool token slots and
+// its pools in pages of 32 pool rows, page q of d at table[d*max_pages + q]
+// (token l of d in slot table[..][l / (32 kpool)] * 32 kpool + l % (32 kpool),
+// pool j in row table[..][j / 32] * 32 + j % 32). Grid: per_doc pool slots per
+// document, one pool per L lanes; slot u of d is pool j_first(d) + u, the pools
+// whose last token is among d's last `last_tokens` tokens. A page number
+// outside [0, num_pages), or a pool past the document's max_pages pages, is
+// left unwritten.
+template <int L, int KP>
+__global__ __launch_bounds__(256) void pool_keys_paged_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ table, int max_pages,
+    int num_pages, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ gate,
+    const float* __restrict__ ape, int kpool, float norm, uint8_t* __restrict__ k8, float* __restrict__ ks,
+    int last_tokens, int per_doc) {
+    constexpr int N = 4 * L;
+    const int lane = threadIdx.x & 63;
+    const int j = lane % L;
+    const long long u = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / L;
+    if (u >= (long long)num_docs * per_doc) return;
+    const int d = (int)(u / per_doc);
+    const int len = cu[d + 1] - cu[d];
+    const int first_tok = len - last_tokens;                  // pools ending at or after it
+    const int lo = first_tok <= kpool - 1 ? 0 : (first_tok - (kpool - 1) + kpool - 1) / kpool;
+    const int pj = lo + (int)(u % per_doc);
+    if (pj >= len / kpool) return;
+    const int page_tok = 32 * kpool;
+    const int* trow = table + (size_t)d * max_pages;
+    const int s = kpool * pj;                                  // the pool's first token (of d)
+    if (s / page_tok >= max_pages || (pj >> 5) >= max_pages) return;   // past the document's table row
+    const int tpage = trow[s / page_tok];                      // (the pool's tokens share a page)
+    const int ppage = trow[pj >> 5];
+    if (tpage < 0 || tpage >= num_pages || ppage < 0 || ppage >= num_pages) return;
+    const size_t tok0 = (size_t)tpage * page_tok + s % page_tok;
+
+    float x[4];
+    pool_vector<L, KP>(x, k_idx, gate, ape, kpool, j, [&](int i) { return tok0 + i; });
+    fwht4<L>(x, lane, norm);
+    float sc;
+    uint32_t codes = quant4<L>(x, &sc);
+    const size_t prow = (size_t)ppage * 32 + (pj & 31);
+    reinterpret_cast<uint32_t*>(k8 + prow * N)[j] = codes;
+    if (j == 0) ks[prow] = sc;
 }
 
 // ---------------------------------------------------------- queries ---------
@@ -263,6 +319,40 @@ hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, c
     else
         launch_pool_keys<0>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
                             norm, pool_start, k8, ks, kf32, p_base, token_lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_paged(const int32_t* cu, int num_docs, const int32_t* table, int max_pages, int num_pages,
+                             const uint16_t* k_idx, const uint16_t* gate, const float* ape, int d_idx, int kpool,
+                             float norm, uint8_t* k8, float* ks, int last_tokens, hipStream_t stream) {
+    if (num_docs == 0 || last_tokens == 0) return hipSuccess;
+    // a document's last `last_tokens` tokens close at most last_tokens / kpool + 1 pools
+    const int per_doc = last_tokens / kpool + 1;
+    const int L = d_idx / 4;
+    const long long threads = (long long)num_docs * per_doc * L;
+    const long long blocks = (threads + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+#define KP_PAGED_ARGS cu, num_docs, table, max_pages, num_pages, k_idx, gate, ape, kpool, norm, k8, ks, last_tokens, per_doc
+    const unsigned b = (unsigned)blocks;
+    if (kpool == 4) {
+        switch (d_idx) {
+            case 32: pool_keys_paged_kernel<8, 4><<<b, 256, 0, stream>>>(KP_PAGED_ARGS); break;
+            case 64: pool_keys_paged_kernel<16, 4><<<b, 256, 0, stream>>>(KP_PAGED_ARGS); break;
+            default: pool_keys_paged_kernel<32, 4><<<b, 256, 0, stream>>>(KP_PAGED_ARGS); break;
+        }
+    } else {
+        switch (d_idx) {
+            case 32: pool_keys_paged_kernel<8, 0><<<b, 256, 0, stream>>>(KP_PAGED_ARGS); break;
+            case 64: pool_keys_paged_kernel<16, 0><<<b, 256, 0, stream>>>(KP_PAGED_ARGS); break;
+            default: pool_keys_paged_kernel<32, 0><<<b, 256, 0, stream>>>(KP_PAGED_ARGS); break;
+        }
+    }
+#undef KP_PAGED_ARGS
+    return hipGetLastError();
+}
+
+hipError_t launch_layout(const int32_t* cu, int num_docs, int kpool, int32_t* cu_pools, hipStream_t stream) {
+    layout_scan_kernel<<<1, 1024, 0, stream>>>(cu, num_docs, kpool, cu_pools);
     return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@
 // longest causal rows start early.
 #include "kp_device.h"
 #include "kp_launch.h"
+#include "kp_select.h"
 
 namespace kp {
 
@@ -51,10 +52,6 @@ hipError_t launch_fill_f32(float* dst, size_t n, float value, hipStream_t stream
 // LDS layout of the query tile: [head][query][128 bytes]; the 16-byte chunk c
 // of query row q is stored at chunk c ^ ((q >> 1) & 7), so the 16 rows one
 // A-operand read touches fall in distinct banks.
-// max(x, 0) on the bit pattern: a set sign bit reads as a negative integer
-// (-0 included), so one integer max clears every negative value; positive
-// values pass unchanged. One instruction, and no quieting of the MFMA result.
-__device__ __forceinline__ float relu_f32(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // All heads of one 64-pool block of a wave: acc[j][e] += w*sq(query 4g+e, h) *
 // ReLU(<q8[query, h], k8[pool 16j+n]>) summed over h. The heads run as a
@@ -106,18 +103,47 @@ __device__ __forceinline__ void score_heads(const uint8_t* __restrict__ q_lds, c
     }
 }
 
+// Pooled keys in pages of 32 pools (a page holds the pools of kpool*32
+// tokens): pool p of document d (global number p, d's pools starting at
+// cu_pools[d]) is row table[d*max_pages + (p - cu_pools[d]) / 32] * 32 +
+// (p - cu_pools[d]) % 32 of k8 and sk (a page number outside [0, num_pages),
+// or a pool past d's max_pages pages: no row, its key reads as zero).
+// table == nullptr: row p.
+struct PageArgs {
+    const int32_t* table;
+    int max_pages;
+    int num_pages;
+};
+
+// Candidate emission of the fused scoring + top-k: query i keeps every
+// visible pool whose (key, pool) is at least (tau[2i], tau[2i+1]) in the
+// order "larger key first, then lower pool first"; count[i] counts them all
+// and the first `cap` go to cand[i*cap ...] as (key, pool) in any order.
+struct EmitArgs {
+    const uint32_t* tau;
+    int32_t* count;
+    uint2* cand;
+    int cap;
+};
+
 // (at least four waves per SIMD: 128 registers)
+template <bool EMIT, bool PAGED>
 __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, int num_q, const uint8_t* __restrict__ q8,
     const float* __restrict__ sq, const float* __restrict__ w, int h_idx, int d_idx,
     const uint8_t* __restrict__ k8, const float* __restrict__ sk, int max_pools,
-    float* __restrict__ scores, int nsplit) {
+    float* __restrict__ scores, int nsplit, EmitArgs em, PageArgs pg) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* q_lds = smem;                                                 // [h_idx][QT][128]
     float* wq_lds = reinterpret_cast<float*>(smem + (size_t)h_idx * SC_QT * 128);  // [h_idx][QT]
     __shared__ int lo_s[SC_QT], hi_s[SC_QT];
     __shared__ int plo_s, phi_s;
+    // emission: thresholds, per-chunk candidate counts and write cursors
+    __shared__ uint32_t tk_s[SC_QT];
+    __shared__ int tp_s[SC_QT], lcnt_s[SC_QT], lcur_s[SC_QT];
+    // paged keys: the distinct documents of the tile (pool range, table row)
+    __shared__ int ndoc_s, dlo_s[SC_QT], dhi_s[SC_QT], dtab_s[SC_QT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -129,16 +155,23 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
     const int q0 = qtile * SC_QT;
 
     if (tid < SC_QT) {
-        int lo = 0, hi = 0;
+        int lo = 0, hi = 0, doc = -1;
         int i = q0 + tid;
         if (i < num_q) {
             int t = q_pos ? q_pos[i] : i;
             QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
             lo = qp.pool_lo;
             hi = qp.pool_lo + qp.n_vis;
+            doc = qp.doc;
+            if (EMIT) {
+                tk_s[tid] = em.tau[2 * i];
+                tp_s[tid] = (int)em.tau[2 * i + 1];
+            }
         }
         lo_s[tid] = lo;
         hi_s[tid] = hi;
+        if (EMIT) lcnt_s[tid] = 0;
+        if (PAGED) dtab_s[tid] = doc;   // (documents, deduplicated below)
     }
     __syncthreads();
     if (tid == 0) {   // the pools any query of the tile sees lie in [plo, phi)
@@ -150,6 +183,26 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
             }
         plo_s = plo;
         phi_s = phi;
+        if (PAGED) {
+            // per distinct document: its first pool, the end of what the tile's
+            // queries see of it, and its row of the page table
+            int nd = 0;
+            for (int q = 0; q < SC_QT; ++q) {
+                if (lo_s[q] >= hi_s[q]) continue;
+                int f = -1;
+                for (int e = 0; e < nd; ++e)
+                    if (dlo_s[e] == lo_s[q]) f = e;
+                if (f < 0) {
+                    f = nd++;
+                    dlo_s[f] = lo_s[q];
+                    dhi_s[f] = hi_s[q];
+                    dtab_s[f] = dtab_s[q] * pg.max_pages;
+                } else {
+                    dhi_s[f] = max(dhi_s[f], hi_s[q]);
+                }
+            }
+            ndoc_s = nd;
+        }
     }
     __syncthreads();
     const int plo = plo_s, phi = phi_s;
@@ -194,60 +247,107 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
 
     __syncthreads();
 
+    // (the chunk loop is uniform over the workgroup: emission synchronises it)
     for (int P0 = P_first; P0 < phi; P0 += SC_PC * nsplit) {
         const int Pw = P0 + wave * SC_PW;
         // skip the block if no query of the tile sees any of its pools
         bool seen = false;
         for (int q = 0; q < SC_QT; ++q) seen |= max(lo_s[q], Pw) < min(hi_s[q], Pw + SC_PW);
-        if (!seen) continue;
+        if (!EMIT && !seen) continue;
 
-        // this wave's pools: B operands (32 code bytes of column n per lane) and key scales
-        i32x8 b[SC_NJ];
-        float skj[SC_NJ];
-#pragma unroll
-        for (int j = 0; j < SC_NJ; ++j) {
-            int p = Pw + 16 * j + n;
-            uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
-            float s = 0.0f;
-            if (p < max_pools) {
-                const uint8_t* src = k8 + (size_t)p * d_idx;
-                if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src + 32 * g);
-                if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 32 * g + 16);
-                s = sk[p];
-            }
-            b[j] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                         (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-            skj[j] = s;
-        }
-
-        // (a block with only some tiles visible computes all four: the others'
-        // results are dropped at the store)
         f32x4 acc[SC_NJ];
-#pragma unroll
-        for (int j = 0; j < SC_NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        score_heads(q_lds, wq_lds, h_idx, b, acc);
-
-        // lane holds queries 4g + e of the tile for pool Pw + 16j + n
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int q = 4 * g + e;
-            if (q0 + q >= num_q) continue;
-            const int lo = lo_s[q], hi = hi_s[q];
-            float* orow = scores + (size_t)(q0 + q) * max_pools;
+        float skj[SC_NJ];
+        if (seen) {
+            // this wave's pools: B operands (32 code bytes of column n per lane) and key scales
+            i32x8 b[SC_NJ];
 #pragma unroll
             for (int j = 0; j < SC_NJ; ++j) {
-                const int p = Pw + 16 * j + n;
-                if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
+                int p = Pw + 16 * j + n;
+                uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
+                float s = 0.0f;
+                long long row = -1;
+                if (PAGED) {
+                    // a pool some query of the tile sees; others stay zero
+                    for (int e = 0; e < ndoc_s; ++e)
+                        if (p >= dlo_s[e] && p < dhi_s[e]) {
+                            const int l = p - dlo_s[e];
+                            const int pn = (l >> 5) < pg.max_pages ? pg.table[dtab_s[e] + (l >> 5)] : -1;
+                            if ((unsigned)pn < (unsigned)pg.num_pages) row = (long long)pn * 32 + (l & 31);
+                            break;
+                        }
+                } else if (p < max_pools) {
+                    row = p;
+                }
+                if (row >= 0) {
+                    const uint8_t* src = k8 + (size_t)row * d_idx;
+                    if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src + 32 * g);
+                    if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 32 * g + 16);
+                    s = sk[row];
+                }
+                b[j] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                             (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+                skj[j] = s;
+            }
+
+            // (a block with only some tiles visible computes all four: the others'
+            // results are dropped at the store)
+#pragma unroll
+            for (int j = 0; j < SC_NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            score_heads(q_lds, wq_lds, h_idx, b, acc);
+        }
+
+        if (!EMIT) {
+            // lane holds queries 4g + e of the tile for pool Pw + 16j + n
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = 4 * g + e;
+                if (q0 + q >= num_q) continue;
+                const int lo = lo_s[q], hi = hi_s[q];
+                float* orow = scores + (size_t)(q0 + q) * max_pools;
+#pragma unroll
+                for (int j = 0; j < SC_NJ; ++j) {
+                    const int p = Pw + 16 * j + n;
+                    if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
+                }
+            }
+        } else {
+            // candidates of this block: bit 4j+e for query 4g+e and pool Pw+16j+n
+            uint32_t cm = 0u, key[SC_NJ][4];
+            if (seen) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q = 4 * g + e;
+                    const int lo = lo_s[q], hi = hi_s[q];
+                    const uint32_t tk = tk_s[q];
+                    const int tp = tp_s[q];
+#pragma unroll
+                    for (int j = 0; j < SC_NJ; ++j) {
+                        const int p = Pw + 16 * j + n;
+                        key[j][e] = score_key(acc[j][e] * skj[j]);
+                        const bool c = p >= lo && p < hi && (key[j][e] > tk || (key[j][e] == tk && p <= tp));
+                        cm |= (uint32_t)c << (4 * j + e);
+                    }
+                }
+            }
+            // count per query, reserve one range of each query's list, then write
+            for (uint32_t m = cm; m; m &= m - 1) atomicAdd(&lcnt_s[4 * g + (__builtin_ctz(m) & 3)], 1);
+            __syncthreads();
+            if (tid < SC_QT) {
+                const int c = lcnt_s[tid];
+                lcur_s[tid] = c ? atomicAdd(&em.count[q0 + tid], c) : 0;
+                lcnt_s[tid] = 0;
+            }
+            __syncthreads();
+            for (uint32_t m = cm; m; m &= m - 1) {
+                const int b = __builtin_ctz(m), j = b >> 2, e = b & 3, q = 4 * g + e;
+                const int pos = atomicAdd(&lcur_s[q], 1);
+                if (pos < em.cap) em.cand[(size_t)(q0 + q) * em.cap + pos] = make_uint2(key[j][e], Pw + 16 * j + n);
             }
         }
     }
 }
 
-hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
-                        const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
-                        const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
-                        int max_pools, float* scores, hipStream_t stream) {
-    if (num_q == 0 || max_pools == 0) return hipSuccess;
+static int score_split(int num_q, int max_pools) {
     // split the pools of a query tile over several workgroups when the tiles
     // alone give fewer than 512 workgroups: two per compute unit (four waves per
     // SIMD) on the 256 CUs, so one round of workgroups fills the GPU and each
@@ -258,15 +358,50 @@ hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools
     int nsplit = (512 + nqt - 1) / nqt;
     if (nsplit > nchunks) nsplit = nchunks;
     if (nsplit < 1) nsplit = 1;
+    return nsplit;
+}
+
+template <bool EMIT, bool PAGED>
+static hipError_t launch_score_t(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                                 const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
+                                 const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
+                                 int max_pools, float* scores, EmitArgs em, PageArgs pg, hipStream_t stream) {
+    if (num_q == 0 || max_pools == 0) return hipSuccess;
+    const int nqt = (num_q + SC_QT - 1) / SC_QT;
+    const int nsplit = score_split(num_q, max_pools);
     const long long nblk = (long long)nqt * nsplit;
     if (nblk > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nblk);
     const size_t lds = (size_t)h_idx * SC_QT * (128 + 4);
-    hipError_t e = hipFuncSetAttribute((const void*)score_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)score_kernel<EMIT, PAGED>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    score_kernel<<<grid, SC_THREADS, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx,
-                                             k8, sk, max_pools, scores, nsplit);
+    score_kernel<EMIT, PAGED><<<grid, SC_THREADS, lds, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8,
+                                                                  sq, w, h_idx, d_idx, k8, sk, max_pools, scores,
+                                                                  nsplit, em, pg);
     return hipGetLastError();
+}
+
+hipError_t launch_score(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                        const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
+                        const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
+                        int max_pools, float* scores, hipStream_t stream) {
+    return launch_score_t<false, false>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx, k8,
+                                        sk, max_pools, scores, EmitArgs{}, PageArgs{nullptr, 0, 0}, stream);
+}
+
+hipError_t launch_score_emit(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
+                             const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq,
+                             const float* w, int h_idx, int d_idx, const uint8_t* k8, const float* sk,
+                             int max_pools, const int32_t* page_table, int max_pages, int num_pages,
+                             const uint32_t* tau, int32_t* count, uint2* cand, int cap, hipStream_t stream) {
+    const EmitArgs em{tau, count, cand, cap};
+    const PageArgs pg{page_table, max_pages, num_pages};
+    if (page_table)
+        return launch_score_t<true, true>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx,
+                                          k8, sk, max_pools, nullptr, em, pg, stream);
+    return launch_score_t<true, false>(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx, k8,
+                                       sk, max_pools, nullptr, em, pg, stream);
 }
 
 }  // namespace kp

@@ -18,52 +18,13 @@
 // short enough stay in LDS between passes; longer rows are re-read.
 #include "kp_device.h"
 #include "kp_launch.h"
+#include "kp_select.h"
 
 namespace kp {
 
 constexpr int TK_THREADS = 512;
 constexpr int TK_LDS_KEYS = 8192;    // keys cached in LDS (32 KB)
 constexpr int TK_BINS = 2048;        // histogram bins of the widest digit
-
-__device__ __forceinline__ uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;                       // -0 == +0
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0u;  // NaN: lowest
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
-// row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast 15 and 31 carry the
-// row totals into the rows above.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
-    return x;
-}
-
-// Exclusive scan of one int per thread over a block of NTH threads; returns
-// the prefix and writes the total to *total.
-template <int NTH = TK_THREADS>
-__device__ __forceinline__ int block_excl_scan(int v, int* wave_buf, int* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int x = wave_incl_scan(v);
-    if (lane == 63) wave_buf[wave] = x;
-    __syncthreads();
-    int add = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NTH / 64; ++w) {
-        int t = wave_buf[w];
-        if (w < wave) add += t;
-        tot += t;
-    }
-    __syncthreads();
-    *total = tot;
-    return add + x - v;
-}
 
 // Keys j .. j+3 of the row (j a multiple of 4); entries at or past n read as 0.
 // Cached rows read one 16-byte LDS vector; others read the scores.
@@ -175,7 +136,7 @@ __device__ __forceinline__ void topk_row(const uint32_t* keys_lds, int (*hist)[T
 #pragma unroll
             for (int e = 0; e < 4; ++e) n_eq += (j + e < j1 && kk[e] == thresh);
         }
-        eq_before = block_excl_scan(n_eq, wave_buf, &tot);
+        eq_before = block_excl_scan<TK_THREADS>(n_eq, wave_buf, &tot);
     }
     int n_sel = 0;
     if (!all) {
@@ -190,7 +151,7 @@ __device__ __forceinline__ void topk_row(const uint32_t* keys_lds, int (*hist)[T
     } else {
         n_sel = j1 - j0;
     }
-    const int sel_before = block_excl_scan(n_sel, wave_buf, &tot);
+    const int sel_before = block_excl_scan<TK_THREADS>(n_sel, wave_buf, &tot);
     int e_rank = eq_before, pos = sel_before;
     for (int j = j0; j < j1; j += 4) {
         uint32_t kk[4] = {0u, 0u, 0u, 0u};
@@ -640,7 +601,7 @@ __global__ __launch_bounds__(TM_THREADS) void topk_mw_count_kernel(
     }
     // (16 bits each: a chunk has at most TM_CHUNK keys)
     int tot;
-    block_excl_scan(gt | (eq << 16), wave_buf, &tot);
+    block_excl_scan<TM_THREADS>(gt | (eq << 16), wave_buf, &tot);
     if (threadIdx.x == 0) {
         r.cc[2 * blockIdx.y] = tot & 0xFFFF;
         r.cc[2 * blockIdx.y + 1] = tot >> 16;
@@ -684,12 +645,12 @@ __global__ __launch_bounds__(TM_THREADS) void topk_mw_write_kernel(
     int tot, n_eq = 0;
 #pragma unroll
     for (int q = 0; q < TM_RUN; ++q) n_eq += (j0 + q < c1 && kk[q] == thresh);
-    const int eq_before = eqb + block_excl_scan(n_eq, wave_buf, &tot);
+    const int eq_before = eqb + block_excl_scan<TM_THREADS>(n_eq, wave_buf, &tot);
     int e_rank = eq_before, n_sel = 0;
 #pragma unroll
     for (int q = 0; q < TM_RUN; ++q)
         if (j0 + q < c1) n_sel += kk[q] > thresh || (kk[q] == thresh && e_rank++ < take_eq);
-    int pos = pos0 + block_excl_scan(n_sel, wave_buf, &tot);
+    int pos = pos0 + block_excl_scan<TM_THREADS>(n_sel, wave_buf, &tot);
     e_rank = eq_before;
 #pragma unroll
     for (int q = 0; q < TM_RUN; ++q) {

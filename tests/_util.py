@@ -116,3 +116,60 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str = "", scaled: bool = F
     worst = float(d.max()) if d.size else 0.0
     assert worst <= LSE_TOL, f"{what}: lse error {worst:.3e}"
     return worst
+
+
+# Top-k selection made on GPU scores vs the oracle's selection on its own
+# (float64, rounded to fp32) scores. The GPU scores sit within 2.7e-4 of the
+# row scale of the oracle's (worst case measured on the workloads' rows, held
+# to SCORE_RTOL), so the two selections can differ only where two pools score
+# within twice that of each other at the k-th score: the swapped pools must
+# lie within SELECT_RTOL * scale of the oracle's k-th score (scale = the
+# larger of |k-th score| and the row's mean |score|). Rows with no other pool
+# inside that band must agree bit for bit.
+SELECT_RTOL = 2e-3
+
+
+def _pool_of(tok, cu, cp, kpool):
+    d = np.searchsorted(cu, tok, side="right") - 1
+    return cp[d] + (tok - cu[d]) // kpool
+
+
+def check_selection(g_idx, g_nv, ref_idx, ref_nv, ref_scores, cu, cp, kpool, q_pos, topk, what=""):
+    """GPU index rows against the oracle's: slot counts, tails and padding equal;
+    kept pools ascending, whole and visible; any pool kept by one side only is a
+    near-tie at the k-th score; rows without a near-tie are identical."""
+    cu = np.asarray(cu, np.int64)
+    cp = np.asarray(cp, np.int64)
+    assert np.array_equal(g_nv, ref_nv), f"{what}: slot counts differ"
+    exact, swaps, worst = 0, 0, 0.0
+    for i in range(g_idx.shape[0]):
+        t = int(q_pos[i])
+        d = int(np.searchsorted(cu, t, side="right") - 1)
+        n = (t - int(cu[d]) + 1) // kpool
+        lo = int(cp[d])
+        k = min(topk, n)
+        w = k * kpool
+        assert np.array_equal(g_idx[i, w:], ref_idx[i, w:]), f"{what}: row {i} tail or padding differs"
+        g = g_idx[i, :w].reshape(k, kpool).astype(np.int64)
+        assert np.all(g == g[:, :1] + np.arange(kpool)), f"{what}: row {i} pools not whole"
+        gp = _pool_of(g[:, 0], cu, cp, kpool)
+        assert np.all(np.diff(gp) > 0), f"{what}: row {i} pools not ascending"
+        assert k == 0 or (gp[0] >= lo and gp[-1] < lo + n), f"{what}: row {i} pool outside its visible range"
+        if np.array_equal(g_idx[i, :w], ref_idx[i, :w]):
+            exact += 1
+            continue
+        rp = _pool_of(ref_idx[i, :w:kpool].astype(np.int64), cu, cp, kpool)
+        a, b = np.setdiff1d(gp, rp), np.setdiff1d(rp, gp)
+        s = ref_scores[i, lo:lo + n].astype(np.float64)
+        sk = np.sort(s)[::-1][k - 1]
+        scale = max(abs(sk), float(np.abs(s).mean()))
+        band = SELECT_RTOL * scale
+        near = int(np.sum(np.abs(s - sk) <= band))
+        assert near > 1, f"{what}: row {i} differs with no near-tie at the k-th score"
+        for p in a:
+            assert sk - band <= s[p - lo] <= sk, f"{what}: row {i} keeps pool {p} ({s[p - lo]} vs k-th {sk})"
+        for p in b:
+            assert sk <= s[p - lo] <= sk + band, f"{what}: row {i} drops pool {p} ({s[p - lo]} vs k-th {sk})"
+        swaps += len(a)
+        worst = max(worst, float(np.abs(s[np.concatenate([a, b]) - lo] - sk).max()) / scale)
+    return {"rows": int(g_idx.shape[0]), "identical": exact, "swapped_pools": swaps, "worst_swap_rel": worst}

@@ -47,10 +47,21 @@ def test_row_width(L):
 
 
 def test_workspace_size(L):
-    ws = L.kp_indexer_workspace_bytes(32768, 8192, 32, 128)
+    ws = L.kp_indexer_workspace_bytes(32768, 8192, 32, 128, 512)
     assert ws >= 32768 * 32 * 128 + 32768 * 32 * 4 + 32768 * 8192 * 4
     assert ws % 256 == 0
-    assert L.kp_indexer_workspace_bytes(0, 8192, 32, 128) == 0
+    assert L.kp_indexer_workspace_bytes(0, 8192, 32, 128, 512) == 0
+    # rows of at least 32768 pools with top-k <= 8192: no score tensor, 128 KiB of
+    # candidates per query instead (the 1M-token decode: 64 MiB of scores -> 8 MiB)
+    q_part = 64 * 32 * 128 + 64 * 32 * 4
+    fused = L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128, 512)
+    assert q_part + 64 * 16384 * 8 <= fused < q_part + 64 * 16384 * 8 + 4096
+    assert L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128, 8193) >= 64 * (1 << 18) * 4   # top-k too large
+    assert L.kp_indexer_workspace_bytes(64, 32767, 32, 128, 512) >= 64 * 32767 * 4          # rows too short
+    # the paged path: the pool layout, the queries and the candidate lists
+    pw = L.kp_indexer_paged_workspace_bytes(64, 3, 32, 128)
+    assert pw % 256 == 0 and fused < pw <= fused + 256
+    assert L.kp_indexer_paged_workspace_bytes(0, 3, 32, 128) == 0
 
 
 def test_invalid_args_rejected_on_host(L):
@@ -114,6 +125,34 @@ def test_invalid_args_rejected_on_host(L):
     assert L.indexer_score_topk_noalloc(*nargs(4096, 10, None)) == 1          # q_pos NULL needs num_q == T
     assert L.indexer_score_topk_noalloc(*nargs(32768, 32768, None)) == 2      # 32K: 671 MB of workspace
     assert b"scratch" in L.kp_last_error()
-    assert L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128) <= 72 << 20     # 1M-token decode fits
+    assert L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128, 512) <= 72 << 20     # 1M-token decode fits
     assert L.indexer_rotate_quant(fake, 4, 2, 48, fake, fake, None) == 2
     assert L.indexer_topk_from_scores(fake, 1, 64, fake, 16, None, 64, None, 4, 4, 128, fake, None, None) == 1
+
+
+def test_paged_args_rejected_on_host(L):
+    """Argument checks of the paged cache's two entry points (no launch)."""
+    fake = C.c_void_p(0x1000)
+    # kpool_update_paged(cu, B, table, max_pages, num_pages, k_idx, gate, ape, d, kpool, last, k8, sk, stream)
+    up = lambda **kw: L.kpool_update_paged(*[kw.get(k, v) for k, v in (
+        ("cu", fake), ("B", 1), ("tab", fake), ("mp", 4), ("np", 8), ("ki", fake), ("ga", fake), ("ape", fake),
+        ("d", 128), ("kp", 4), ("last", 1), ("k8", fake), ("sk", fake), ("st", None))])
+    assert up(kp=0) == 2 and up(d=48) == 2
+    assert up(last=-1) == 1 and up(np=-1) == 1
+    assert up(last=0) == 0 and up(B=0) == 0                    # nothing to do
+    assert up(tab=None) == 1 and b"required" in L.kp_last_error()
+    assert up(np=1 << 26) == 2                                 # slots past 2^31
+    # indexer_score_topk_paged(cu, B, T, table, max_pages, num_pages, k8, sk, q_pos, nq, q, w, h, d, kpool, topk,
+    #                          W, idx, nv, row_path, ws, ws_bytes, stream)
+    sp = lambda **kw: L.indexer_score_topk_paged(*[kw.get(k, v) for k, v in (
+        ("cu", fake), ("B", 1), ("T", 4096), ("tab", fake), ("mp", 32), ("np", 32), ("k8", fake), ("sk", fake),
+        ("qpos", fake), ("nq", 4), ("q", fake), ("w", fake), ("h", 32), ("d", 128), ("kp", 4), ("topk", 512),
+        ("W", 2176), ("idx", fake), ("nv", None), ("rp", None), ("ws", fake), ("wsb", 1 << 30), ("st", None))])
+    assert sp(topk=8193, W=32896) == 2 and b"8192" in L.kp_last_error()
+    assert sp(W=2048) == 1 and sp(W=2200) == 1                   # narrower than 4*512+3 / not a multiple of 128
+    assert sp(h=65) == 2 and sp(d=96) == 2
+    assert sp(nq=0) == 0                                         # empty shard
+    assert sp(qpos=None) == 1                                    # q_pos NULL needs num_q == num_tokens
+    assert sp(tab=None) == 1 and sp(k8=None) == 1
+    assert sp(wsb=1024) == 1 and b"workspace" in L.kp_last_error()
+    assert sp(ws=C.c_void_p(0x1010)) == 1 and b"aligned" in L.kp_last_error()

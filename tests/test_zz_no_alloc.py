@@ -48,7 +48,7 @@ def test_noalloc_matches_workspace_variant(K):
     for name in ["decode1m", "packed4k", "tiny"]:
         s, cu, k_idx, gate, ape, q_idx, w, q_pos = _inputs(name)
         print("no-alloc indexer", name, "T", s.T, "queries", s.Tq,
-              "workspace bytes", K.kp_indexer_workspace_bytes(s.Tq, s.max_pools, s.H_I, s.D_I), flush=True)
+              "workspace bytes", K.kp_indexer_workspace_bytes(s.Tq, s.max_pools, s.H_I, s.D_I, s.topk), flush=True)
         cp, _, k8, ks, _ = K.kpool_build(cu, k_idx, gate, ape, s.kpool)
         for with_scores in (True, False):
             ref = K.indexer_score_topk(cu, cp, k8, ks, q_idx, w, s.T, s.kpool, s.topk, q_pos=q_pos,
