@@ -189,6 +189,8 @@ def main():
     lse = torch.empty((s.Tq, s.H), dtype=torch.float32, device=dev)
     ws_bytes = K.kp_indexer_workspace_bytes(s.Tq, cap, s.H_I, s.D_I, s.topk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    mla_ws_bytes = K.kp_mla_fwd_workspace_bytes(s.Tq, s.H, s.D, W)     # (0 unless the rows are split)
+    mla_ws = torch.empty(max(mla_ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = P(stream.cuda_stream)
     ptr = lambda t: None if t is None else P(t.data_ptr())
@@ -218,7 +220,7 @@ def main():
         if ev:
             ev[2].record(stream)
         call(L.sparse_mla_fwd(ptr(q), ptr(kv), ptr(idx), s.Tq, s.T, s.H, s.D, W, C.c_float(s.scale), ptr(out),
-                              ptr(lse), sp))
+                              ptr(lse), ptr(mla_ws) if mla_ws_bytes else None, mla_ws_bytes, sp))
         if ev:
             ev[3].record(stream)
 

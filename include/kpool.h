@@ -167,8 +167,8 @@ kp_status indexer_rotate_quant(const uint16_t* q_idx, int32_t num_q, int32_t h_i
 /*
  * Bytes of workspace indexer_score_topk needs for these sizes: the rotated
  * queries, then either the score rows (num_q x max_pools fp32) or, on the
- * fused path (max_pools >= 32768 and topk_pools <= 8192), 128 KiB of candidate
- * list per query. 0 when num_q <= 0.
+ * fused path (max_pools >= 32768 and topk_pools <= 8192), 128 KiB of
+ * candidate list per query. 0 when num_q <= 0.
  */
 size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx,
                                   int32_t topk_pools);
@@ -359,11 +359,21 @@ kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, 
  *            softmax_scale finite and > 0
  *   out      device bf16 [num_q, heads, d_v]        (out)
  *   lse      device fp32 [num_q, heads]             (out, NULLABLE)
+ *   workspace  device memory of kp_mla_fwd_workspace_bytes(num_q, heads,
+ *            d_latent, row_width) bytes, 256-byte aligned (NULLABLE). Launches
+ *            of fewer than 128 queries (decode) then split each index row into
+ *            up to 16 ranges of 64-row tiles, one workgroup each, whose
+ *            normalised fp32 partial outputs and lse are merged by a second
+ *            kernel: out = sum over ranges of exp(lse_r - lse) out_r, rounded to
+ *            bf16 once. Without a workspace (or when that size is 0) each query
+ *            is one workgroup. The two agree to the bf16 rounding of out.
  */
+size_t kp_mla_fwd_workspace_bytes(int32_t num_q, int32_t heads, int32_t d_latent, int32_t row_width);
 kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
                          int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_latent,
                          int32_t row_width, float softmax_scale,
-                         uint16_t* out, float* lse, hipStream_t stream);
+                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* Bytes of workspace sparse_mla_bwd needs for these sizes. */
 size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width);

@@ -39,7 +39,8 @@ SIGNATURES = [
     ("indexer_score_topk_paged", _I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                       _P, _P, _P, _P, _Z, _P]),
     ("indexer_topk_from_scores", _I, [_P, _I, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
-    ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    ("kp_mla_fwd_workspace_bytes", _Z, [_I, _I, _I, _I]),
+    ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _P]),
     ("kp_mla_bwd_workspace_bytes", _Z, [_I, _I]),
     ("sparse_mla_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _P]),
     ("kp_check_inputs", _I, [_P, _I, _I, _P, _I, _P]),
@@ -369,10 +370,16 @@ def indexer_topk_from_scores(cu_seqlens: torch.Tensor, cu_pools: torch.Tensor, s
     return indices, num_valid
 
 
+def kp_mla_fwd_workspace_bytes(num_q: int, heads: int, d_latent: int, row_width: int) -> int:
+    return int(lib().kp_mla_fwd_workspace_bytes(num_q, heads, d_latent, row_width))
+
+
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, softmax_scale: float,
-                   return_lse: bool = True, out: Optional[torch.Tensor] = None):
+                   return_lse: bool = True, out: Optional[torch.Tensor] = None, split: bool = True,
+                   workspace: Optional[torch.Tensor] = None):
     """Absorbed sparse latent attention: (out bf16 [Tq,H,d_v], lse f32 [Tq,H] or None);
-    d_v = D, except 512 for 576-wide keys (a 64-wide RoPE tail)."""
+    d_v = D, except 512 for 576-wide keys (a 64-wide RoPE tail). ``split``: give
+    the library a workspace, so that few-query launches split their rows."""
     _need(q, "q", torch.bfloat16, (None, None, None))
     Tq, H, D = q.shape
     d_v = 512 if D == 576 else D
@@ -380,12 +387,19 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sof
     _need(indices, "indices", torch.int32, (Tq, None))
     if out is not None:
         _need(out, "out", torch.bfloat16, (Tq, H, d_v))
-    dev = _on(("q", q), ("kv", kv), ("indices", indices), ("out", out))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, (None,))
+    dev = _on(("q", q), ("kv", kv), ("indices", indices), ("out", out), ("workspace", workspace))
     if out is None:
         out = torch.empty((Tq, H, d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Tq, H), dtype=torch.float32, device=dev) if return_lse else None
-    _check(lib().sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), Tq, kv.shape[0], H, D, indices.shape[1],
-                                float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev)))
+    W = indices.shape[1]
+    need = kp_mla_fwd_workspace_bytes(Tq, H, D, W) if split else 0
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = workspace if need > 0 else None
+    _check(lib().sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), Tq, kv.shape[0], H, D, W, float(softmax_scale),
+                                _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
     return out, lse
 
 

@@ -135,11 +135,7 @@ static bool fused_rows(int32_t max_pools, int32_t topk_pools) {
     return max_pools >= 2 * kp::FT_CAP && topk_pools <= kp::FT_CAP / 2;
 }
 
-// Bytes of the fused path's state after q8 and sq: thresholds, counts, candidates.
-static size_t fused_state_bytes(int32_t num_q) {
-    return align256((size_t)num_q * 2 * sizeof(uint32_t)) + align256((size_t)num_q * sizeof(int32_t)) +
-           align256((size_t)num_q * kp::FT_CAP * sizeof(uint2));
-}
+static size_t fused_state_bytes(int32_t num_q) { return kp::fused_state_bytes(num_q); }
 
 size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_idx, int32_t d_idx,
                                   int32_t topk_pools) {
@@ -212,16 +208,15 @@ static kp_status score_topk_launch(const int32_t* cu_seqlens, int32_t num_docs, 
     uint8_t* rest = reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4);
     float* sc = scores ? scores : reinterpret_cast<float*>(rest);
 
+    const bool fused = !scores && fused_rows(max_pools, topk_pools);
+    const kp::FusedState fst = kp::fused_state_at(rest, num_q);
     hipError_t e = kp::launch_rotate_quant(q_idx, (long long)num_q * h_idx, d_idx, hadamard_norm(d_idx), q8, sq,
                                            stream);
     if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
-    if (!scores && fused_rows(max_pools, topk_pools)) {
-        uint32_t* tau = reinterpret_cast<uint32_t*>(rest);
-        int32_t* count = reinterpret_cast<int32_t*>(rest + align256((size_t)num_q * 8));
-        uint2* cand = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(count) + align256((size_t)num_q * 4));
+    if (fused) {
         e = kp::launch_fused_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w_idx, h_idx, d_idx,
                                   pooled_k_fp8, pooled_k_scale, max_pools, nullptr, 0, 0, topk_pools, row_width,
-                                  indices, num_valid, nullptr, tau, count, cand, stream);
+                                  indices, num_valid, nullptr, fst, stream);
         if (e != hipSuccess) return hip_fail(e, "fused score + top-k launch");
         return KP_OK;
     }
@@ -396,16 +391,14 @@ kp_status indexer_score_topk_paged(const int32_t* cu_seqlens, int32_t num_docs, 
     uint8_t* q8 = ws + align256((size_t)(num_docs + 1) * sizeof(int32_t));
     float* sq = reinterpret_cast<float*>(q8 + align256((size_t)num_q * h_idx * d_idx));
     uint8_t* rest = reinterpret_cast<uint8_t*>(sq) + align256((size_t)num_q * h_idx * 4);
-    uint32_t* tau = reinterpret_cast<uint32_t*>(rest);
-    int32_t* count = reinterpret_cast<int32_t*>(rest + align256((size_t)num_q * 8));
-    uint2* cand = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(count) + align256((size_t)num_q * 4));
+    const kp::FusedState fst = kp::fused_state_at(rest, num_q);
     hipError_t e = kp::launch_layout(cu_seqlens, num_docs, kpool, cu_pools, stream);
     if (e != hipSuccess) return hip_fail(e, "layout launch");
     e = kp::launch_rotate_quant(q_idx, (long long)num_q * h_idx, d_idx, hadamard_norm(d_idx), q8, sq, stream);
     if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
     e = kp::launch_fused_topk(cu_seqlens, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w_idx, h_idx, d_idx,
                               k8_pages, sk_pages, num_tokens / kpool, page_table, max_pages, num_pages, topk_pools,
-                              row_width, indices, num_valid, row_path, tau, count, cand, stream);
+                              row_width, indices, num_valid, row_path, fst, stream);
     if (e != hipSuccess) return hip_fail(e, "fused score + top-k launch");
     return ok();
 }
@@ -429,10 +422,17 @@ kp_status indexer_topk_from_scores(const int32_t* cu_seqlens, int32_t num_docs, 
     return ok();
 }
 
+size_t kp_mla_fwd_workspace_bytes(int32_t num_q, int32_t heads, int32_t d_latent, int32_t row_width) {
+    if (num_q <= 0 || heads < 1 || heads > 64 || row_width < 1) return 0;
+    if (d_latent != 512 && d_latent != 64 && d_latent != 576) return 0;
+    return align256(kp::sparse_mla_part_bytes(num_q, heads, d_latent, row_width));
+}
+
 kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
                          int32_t num_q, int32_t num_kv, int32_t heads, int32_t d_latent,
                          int32_t row_width, float softmax_scale,
-                         uint16_t* out, float* lse, hipStream_t stream) {
+                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
     g_err.clear();
     if (num_q < 0 || num_kv < 0 || row_width < 1) return fail(KP_ERR_INVALID_ARG, "bad size");
     if (heads < 1 || heads > 64) return fail(KP_ERR_UNSUPPORTED, "heads must be in 1..64 (got %d)", heads);
@@ -450,11 +450,17 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
     if (num_q == 0) return ok();
     if (!q || !indices || !out || (num_kv > 0 && !kv))
         return fail(KP_ERR_INVALID_ARG, "q, kv, indices and out are required");
+    const size_t need = kp_mla_fwd_workspace_bytes(num_q, heads, d_latent, row_width);
+    if (workspace && need > 0) {
+        if (workspace_bytes < need)
+            return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
     kp_status st = device_check();
     if (st != KP_OK) return st;
     const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
     hipError_t e = kp::launch_sparse_mla(q, kv, indices, num_q, num_kv, heads, d_latent, row_width, scale_log2,
-                                         out, lse, stream);
+                                         out, lse, need > 0 ? workspace : nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
     return ok();
 }

@@ -13,17 +13,18 @@
 //
 //   1. fused_thresh_kernel, one workgroup per query: rows of at most `cap`
 //      visible pools take every pool as a candidate; longer rows score every
-//      s-th pool (s >= 64, at most 16384 samples) and take as threshold the
+//      s-th pool (s >= 128, at most 16384 samples) and take as threshold the
 //      sample of rank r = T*m/n in that order (m samples, n pools, T the
 //      target count max(2k, cap/2)), so about T pools clear it when the
 //      samples are representative. Only its count decides correctness.
 //   2. score_kernel in its emitting form (score.hip) scores every visible
-//      pair and appends the pairs at or above the threshold, as (key, pool),
-//      to the query's candidate list, counting all of them.
+//      pair and appends the pairs at or above the threshold, as (score bits,
+//      pool), to the query's candidate list, counting all of them.
 //   3. fused_select_kernel, one workgroup per query: when the count lies in
 //      [k, cap], a radix select over the candidates in LDS (ties on the key
-//      resolved by a second select over the pools), then a bitonic sort of
-//      the k kept pools; otherwise (adversarial rows only) the workgroup
+//      resolved by a second select over the pools), then the k kept pools in
+//      ascending order through a bitmap of the row (a bitonic sort for rows
+//      too long for it); otherwise (adversarial rows only) the workgroup
 //      rescores every visible pool itself for each digit of an exact radix
 //      select and writes the kept pools in one ordered pass.
 //
@@ -42,8 +43,7 @@
 
 namespace kp {
 
-constexpr int FT_SAMPLE_MAX = 16384;   // sampled pools per query
-constexpr int FT_STRIDE_MIN = 64;      // sampling stride, at least
+constexpr int FT_STRIDE_MIN = 128;     // sampling stride, at least
 constexpr int FT_TH_THREADS = 512;
 constexpr int FT_SEL_THREADS = 1024;
 constexpr int FT_SEL_WAVES = FT_SEL_THREADS / 64;
@@ -153,7 +153,62 @@ __device__ __forceinline__ uint32_t hm_block_key(const HmQuery& hq, int h_idx, i
     return mine;
 }
 
+// Sampled keys: the threshold needs only a good estimate, so the head sum is
+// a tree (each lane sums its own heads, then two cross-group adds) rather
+// than score_kernel's sequential order. B operands of a wave's 4 tiles are
+// loaded together, one block ahead of their use.
+struct HmTiles {
+    i32x8 b[4];
+    float s[4];
+};
+
+__device__ __forceinline__ void hm_load_tiles(HmTiles& t, const KeyRows& kr, int d_idx, const long long (&row)[4]) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int dchunks = d_idx >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
+        float s = 0.0f;
+        if (row[j] >= 0) {
+            const uint8_t* src = kr.k8 + (size_t)row[j] * d_idx + 32 * g;
+            if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src);
+            if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 16);
+            s = kr.sk[row[j]];
+        }
+        t.b[j] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        t.s[j] = s;
+    }
+}
+
+// Key of the pool of lane (16g + n) among the 64 of a loaded block.
+__device__ __forceinline__ uint32_t hm_sample_key(const HmQuery& hq, int h_idx, const HmTiles& t) {
+    const int g = (threadIdx.x & 63) >> 4;
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) {
+            if (16 * hg < h_idx) {
+                const f32x4 d = mfma_fp8_16x16x128(hq.a[hg], t.b[j], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(hq.wv[hg][e], relu_f32(d[e]), acc);
+            }
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        const uint32_t key = score_key(acc * t.s[j]);
+        if (g == j) mine = key;
+    }
+    return mine;
+}
+
 // ------------------------------------------------------------ threshold -----
+// One workgroup per query: each wave scores blocks wave, wave + NW, ... of 64
+// samples, all the loads of its blocks issued before the first MFMA (one
+// memory latency), then the workgroup selects the threshold from the samples
+// in LDS.
+constexpr int FT_TH_BATCH = 4;   // sample blocks per wave per round
 template <bool PAGED>
 __global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
@@ -169,6 +224,10 @@ __global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15;
     const int i = blockIdx.x;
+    // the query's operands depend on i alone: their loads go out before the
+    // document lookup's
+    HmQuery hq;
+    hm_load_query(hq, q8, sq, w, i, h_idx, d_idx);
     const int t = q_pos ? q_pos[i] : i;
     const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
     const int n = qp.n_vis;
@@ -185,14 +244,24 @@ __global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
     const int ss = max(FT_STRIDE_MIN, (n + FT_SAMPLE_MAX - 1) / FT_SAMPLE_MAX);
     const int m = (n + ss - 1) / ss;   // samples: pools pool_lo + ss*j, j < m
     const long long tab = PAGED ? (long long)qp.doc * kr.max_pages : 0;
-    HmQuery hq;
-    hm_load_query(hq, q8, sq, w, i, h_idx, d_idx);
-    for (int b0 = wave * 64; b0 < m; b0 += NW * 64) {
-        const uint32_t key = hm_block_key(hq, h_idx, d_idx, kr, [&](int j) -> long long {
-            const int s = b0 + 16 * j + n16;
-            return s < m ? key_row(kr, qp.pool_lo + ss * s, qp.pool_lo, tab) : -1;
-        });
-        if (b0 + lane < m) keys[b0 + lane] = key;
+    for (int b0 = wave * 64; b0 < m; b0 += FT_TH_BATCH * NW * 64) {
+        HmTiles tb[FT_TH_BATCH];
+#pragma unroll
+        for (int u = 0; u < FT_TH_BATCH; ++u) {
+            long long row[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sidx = b0 + u * NW * 64 + 16 * j + n16;
+                row[j] = sidx < m ? key_row(kr, qp.pool_lo + ss * sidx, qp.pool_lo, tab) : -1;
+            }
+            hm_load_tiles(tb[u], kr, d_idx, row);
+        }
+#pragma unroll
+        for (int u = 0; u < FT_TH_BATCH; ++u) {
+            const int bu = b0 + u * NW * 64;
+            const uint32_t key = hm_sample_key(hq, h_idx, tb[u]);
+            if (bu + lane < m) keys[bu + lane] = key;
+        }
     }
     __syncthreads();
 
@@ -242,6 +311,7 @@ __global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
     __shared__ int hist[2][RS_BINS];
     __shared__ int wave_buf[NW];
     __shared__ int sel[3];
+    __shared__ uint32_t red[2 * NW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15;
     const int i = blockIdx.x;
@@ -276,26 +346,48 @@ __global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
     const int cnt = count[i];
     const bool fits = k > 0 && cnt >= k && cnt <= cap;
     if (fits) {
-        for (int j = tid; j < cnt; j += NTH) {
-            const uint2 c = cand[(size_t)i * cap + j];
-            ckey[j] = c.x;
-            cpool[j] = (int)c.y;
+        // the candidates into LDS, eight loads in flight per thread; keys are
+        // kept relative to the smallest (all candidates cleared one threshold,
+        // so they crowd the top few bins of a plain 32-bit digit)
+        const uint2* src = cand + (size_t)i * cap;
+        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+        for (int j0 = 0; j0 < cnt; j0 += NTH * 8) {
+            uint2 c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + tid + NTH * u;
+                c[u] = j < cnt ? src[j] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + tid + NTH * u;
+                if (j < cnt) {
+                    const uint32_t key = score_key(__uint_as_float(c[u].x));   // (stored as score bits)
+                    ckey[j] = key;
+                    cpool[j] = (int)c[u].y;
+                    kmin = min(kmin, key);
+                    kmax = max(kmax, key);
+                }
+            }
         }
-        __syncthreads();
+        block_min_max<NTH>(kmin, kmax, red, &kmin, &kmax);   // (its barriers publish ckey, cpool)
         uint32_t th = 0u, th2 = 0u;
         int teq = RS_ALL_EQ;
         if (k < cnt) {
+            const int bits = kmax == kmin ? 0 : 32 - __builtin_clz(kmax - kmin);
             radix_select<NTH>([&](auto f) {
-                for (int j = tid; j < cnt; j += NTH) f(ckey[j]);
-            }, k, hist, sel, &th, &teq);
+                for (int j = tid; j < cnt; j += NTH) f(ckey[j] - kmin);
+            }, k, hist, sel, &th, &teq, bits);
+            th += kmin;
             if (teq != RS_ALL_EQ) {
-                // keys equal to th: keep the teq lowest pools (largest ~pool);
+                // keys equal to th: keep the teq lowest pools (hi-1-pool largest);
                 // pools are distinct, so this select is exact
                 int teq2;
+                const int pbits = n <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(n - 1));
                 radix_select<NTH>([&](auto f) {
                     for (int j = tid; j < cnt; j += NTH)
-                        if (ckey[j] == th) f(~(uint32_t)cpool[j]);
-                }, teq, hist, sel, &th2, &teq2);
+                        if (ckey[j] == th) f((uint32_t)(hi - 1 - cpool[j]));
+                }, teq, hist, sel, &th2, &teq2, pbits);
             }
         }
         // kept flags of this thread's candidates j = tid + NTH*s, then their ranks
@@ -306,7 +398,8 @@ __global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
             const int j = tid + NTH * s;
             if (j < cnt) {
                 const uint32_t v = ckey[j];
-                const bool kp = teq == RS_ALL_EQ ? v >= th : (v > th || (v == th && ~(uint32_t)cpool[j] >= th2));
+                const bool kp = teq == RS_ALL_EQ ? v >= th
+                                                 : (v > th || (v == th && (uint32_t)(hi - 1 - cpool[j]) >= th2));
                 keep |= (uint32_t)kp << s;
                 nk += kp;
             }
@@ -314,29 +407,59 @@ __global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
         int tot;
         int pos = block_excl_scan<NTH>(nk, wave_buf, &tot);   // (its barriers end every read of ckey)
         int* list = reinterpret_cast<int*>(ckey);
+        constexpr int MAP_WORDS = FT_CAP;   // the bitmap of a row of up to 32 * FT_CAP pools
+        if (n <= 32 * MAP_WORDS) {
+            // ascending pools through a bitmap of the row's pools: set the kept
+            // ones, then each thread counts a run of words and writes its pools
+            // at their ranks
+            uint32_t* map = ckey;
+            const int words = (n + 31) >> 5;
+            for (int u = tid; u < words; u += NTH) map[u] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < PER; ++s)
+                if (keep >> s & 1u) {
+                    const int l = cpool[tid + NTH * s] - lo;
+                    atomicOr(&map[l >> 5], 1u << (l & 31));
+                }
+            __syncthreads();
+            const int run = (words + NTH - 1) / NTH;
+            const int w0 = min(words, tid * run), w1 = min(words, w0 + run);
+            int c = 0;
+            for (int u = w0; u < w1; ++u) c += __popc(map[u]);
+            int tot2;
+            int r = block_excl_scan<NTH>(c, wave_buf, &tot2);
+            for (int u = w0; u < w1; ++u)
+                for (uint32_t b = map[u]; b; b &= b - 1)
+                    if (r < k) put_pool(r++, lo + 32 * u + __builtin_ctz(b));   // (tot2 == k)
+        } else {
 #pragma unroll
         for (int s = 0; s < PER; ++s)
             if (keep >> s & 1u) list[pos++] = cpool[tid + NTH * s];
-        // ascending pools: bitonic sort of the k kept (tot == k), padded to a power of two
-        int P = 1;
-        while (P < tot) P <<= 1;
-        for (int p = tot + tid; p < P; p += NTH) list[p] = 0x7FFFFFFF;
         __syncthreads();
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int p = tid; p < P / 2; p += NTH) {
-                    const int a_i = 2 * stride * (p / stride) + (p % stride), b_i = a_i + stride;
-                    const bool up = (a_i & size) == 0;
-                    const int a = list[a_i], b = list[b_i];
-                    if ((a > b) == up) {
-                        list[a_i] = b;
-                        list[b_i] = a;
+        {
+            // bitonic sort of the kept pools, padded to a power of two
+            int P = 1;
+            while (P < tot) P <<= 1;
+            for (int p = tot + tid; p < P; p += NTH) list[p] = 0x7FFFFFFF;
+            __syncthreads();
+            for (int size = 2; size <= P; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    for (int p = tid; p < P / 2; p += NTH) {
+                        const int a_i = 2 * stride * (p / stride) + (p % stride), b_i = a_i + stride;
+                        const bool up = (a_i & size) == 0;
+                        const int a = list[a_i], b = list[b_i];
+                        if ((a > b) == up) {
+                            list[a_i] = b;
+                            list[b_i] = a;
+                        }
                     }
+                    __syncthreads();
                 }
-                __syncthreads();
             }
+            for (int p = tid; p < min(tot, k); p += NTH) put_pool(p, list[p]);   // (tot == k)
         }
-        for (int p = tid; p < min(tot, k); p += NTH) put_pool(p, list[p]);   // (tot == k)
+        }
     } else if (k > 0) {
         // exact selection by rescoring every visible pool for each digit
         HmQuery hq;
@@ -387,30 +510,50 @@ hipError_t launch_fused_topk(const int32_t* cu, int num_docs, const int32_t* cu_
                              const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq, const float* w,
                              int h_idx, int d_idx, const uint8_t* k8, const float* sk, int max_pools,
                              const int32_t* page_table, int max_pages, int num_pages, int topk, int row_width,
-                             int32_t* indices, int32_t* num_valid, int32_t* row_path, uint32_t* tau, int32_t* count,
-                             uint2* cand, hipStream_t stream) {
+                             int32_t* indices, int32_t* num_valid, int32_t* row_path, const FusedState& st,
+                             hipStream_t stream) {
     if (num_q == 0) return hipSuccess;
     const KeyRows kr{k8, sk, page_table, max_pages, num_pages};
     if (page_table)
         fused_thresh_kernel<true><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w,
-                                                                      h_idx, d_idx, kr, topk, FT_CAP, tau, count);
+                                                                      h_idx, d_idx, kr, topk, FT_CAP, st.tau,
+                                                                      st.count);
     else
         fused_thresh_kernel<false><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq,
-                                                                       w, h_idx, d_idx, kr, topk, FT_CAP, tau, count);
+                                                                       w, h_idx, d_idx, kr, topk, FT_CAP, st.tau,
+                                                                       st.count);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_score_emit(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx, k8, sk, max_pools,
-                          page_table, max_pages, num_pages, tau, count, cand, FT_CAP, stream);
+                          page_table, max_pages, num_pages, st.tau, st.count, st.cand, FT_CAP, stream);
     if (e != hipSuccess) return e;
     if (page_table)
         fused_select_kernel<true><<<num_q, FT_SEL_THREADS, 0, stream>>>(
-            cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w, h_idx, d_idx, kr, topk, FT_CAP, count, cand, row_width,
-            indices, num_valid, row_path);
+            cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w, h_idx, d_idx, kr, topk, FT_CAP, st.count, st.cand,
+            row_width, indices, num_valid, row_path);
     else
         fused_select_kernel<false><<<num_q, FT_SEL_THREADS, 0, stream>>>(
-            cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w, h_idx, d_idx, kr, topk, FT_CAP, count, cand, row_width,
-            indices, num_valid, row_path);
+            cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w, h_idx, d_idx, kr, topk, FT_CAP, st.count, st.cand,
+            row_width, indices, num_valid, row_path);
     return hipGetLastError();
+}
+
+size_t fused_state_bytes(int num_q) {
+    auto a = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return a((size_t)num_q * 2 * sizeof(uint32_t)) + a((size_t)num_q * sizeof(int32_t)) +
+           a((size_t)num_q * FT_CAP * sizeof(uint2));
+}
+
+FusedState fused_state_at(void* ws, int num_q) {
+    auto a = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    FusedState st;
+    st.tau = reinterpret_cast<uint32_t*>(p);
+    p += a((size_t)num_q * 2 * sizeof(uint32_t));
+    st.count = reinterpret_cast<int32_t*>(p);
+    p += a((size_t)num_q * sizeof(int32_t));
+    st.cand = reinterpret_cast<uint2*>(p);
+    return st;
 }
 
 }  // namespace kp

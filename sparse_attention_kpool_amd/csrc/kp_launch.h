@@ -45,18 +45,28 @@ hipError_t launch_score_emit(const int32_t* cu, int num_docs, const int32_t* cu_
                              int max_pools, const int32_t* page_table, int max_pages, int num_pages,
                              const uint32_t* tau, int32_t* count, uint2* cand, int cap, hipStream_t stream);
 
-// Candidates kept per query by the fused scoring + top-k.
+// Candidates kept per query by the fused scoring + top-k, and sampled pools at most.
 constexpr int FT_CAP = 16384;
+constexpr int FT_SAMPLE_MAX = 16384;
+
+// Workspace of the fused scoring + top-k (fused_state_bytes bytes, 256-byte
+// aligned): per query the threshold, the candidate count and the candidate list.
+struct FusedState {
+    uint32_t* tau;     // [num_q][2]
+    int32_t* count;    // [num_q]
+    uint2* cand;       // [num_q][FT_CAP]
+};
+size_t fused_state_bytes(int num_q);
+FusedState fused_state_at(void* ws, int num_q);
 
 // Fused scoring + top-k (no score tensor): threshold, emission, selection.
-// Workspace: tau [num_q][2] u32, count [num_q] i32, cand [num_q][FT_CAP] uint2.
 // topk <= FT_CAP / 2. With a page table, index rows hold page slots.
 hipError_t launch_fused_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
                              const int32_t* q_pos, int num_q, const uint8_t* q8, const float* sq, const float* w,
                              int h_idx, int d_idx, const uint8_t* k8, const float* sk, int max_pools,
                              const int32_t* page_table, int max_pages, int num_pages, int topk, int row_width,
-                             int32_t* indices, int32_t* num_valid, int32_t* row_path, uint32_t* tau, int32_t* count,
-                             uint2* cand, hipStream_t stream);
+                             int32_t* indices, int32_t* num_valid, int32_t* row_path, const FusedState& st,
+                             hipStream_t stream);
 
 // Top-k index rows from a score tensor (visible entries only are read).
 hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools, int kpool,
@@ -65,9 +75,13 @@ hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools,
                        hipStream_t stream);
 
 // Sparse latent attention over the index rows.
+// With `part` (sparse_mla_part_bytes bytes), rows of few-query launches are
+// split over several workgroups and merged by a second kernel.
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int num_q,
                              int num_kv, int heads, int d_latent, int row_width, float scale_log2,
-                             uint16_t* out, float* lse, hipStream_t stream);
+                             uint16_t* out, float* lse, void* part, hipStream_t stream);
+int sparse_mla_splits(int num_q, int row_width);
+size_t sparse_mla_part_bytes(int num_q, int heads, int d_latent, int row_width);
 
 // Largest index row sparse_mla_fwd accepts for this key width.
 int sparse_mla_max_row_width(int d_latent);

@@ -67,39 +67,52 @@ __device__ __forceinline__ void score_heads(const uint8_t* __restrict__ q_lds, c
     const uint8_t* rowp = q_lds + n * 128;
     const int off0 = ((2 * g) ^ sw) << 4, off1 = ((2 * g + 1) ^ sw) << 4;
     i32x8 a[2];
-    f32x4 wv[2];
     f32x4 c[2][SC_NJ];
     auto load = [&](int slot, int h) __attribute__((always_inline)) {
         const uint8_t* r = rowp + h * (16 * 128);
         const uint4 lo = *reinterpret_cast<const uint4*>(r + off0);
         const uint4 hi = *reinterpret_cast<const uint4*>(r + off1);
         a[slot] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        wv[slot] = *reinterpret_cast<const f32x4*>(wq_lds + h * 16 + 4 * g);
     };
     auto issue = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < SC_NJ; ++j) c[slot][j] = mfma_fp8_16x16x128(a[slot], b[j], f32x4{0.f, 0.f, 0.f, 0.f});
     };
-    auto fold = [&](int slot) __attribute__((always_inline)) {
+    auto fold = [&](int slot, const f32x4& wv) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < SC_NJ; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(wv[slot][e], relu_f32(c[slot][j][e]), acc[j][e]);
+            for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(wv[e], relu_f32(c[slot][j][e]), acc[j][e]);
     };
+    // the loop covers pairs of heads with a head pair after them, with no
+    // condition inside (so the waits on its LDS reads are exact and the reads
+    // may be hoisted); the last one or two heads follow it
     load(0, 0);
     issue(0);
     if (h_idx > 1) load(1, 1);
+    int h = 0;
 #pragma unroll 1
-    for (int h = 0; h < h_idx; h += 2) {
-        // head h: MFMAs in flight in slot 0; head h+1: operands in slot 1
-        if (h + 1 < h_idx) issue(1);
-        fold(0);
-        if (h + 2 < h_idx) load(0, h + 2);
-        if (h + 1 < h_idx) {
-            if (h + 2 < h_idx) issue(0);
-            fold(1);
-            if (h + 3 < h_idx) load(1, h + 3);
-        }
+    for (; h + 2 < h_idx; h += 2) {
+        // head h: MFMAs in flight in slot 0; head h+1: operands in slot 1. The
+        // weights of both heads are read here, so their LDS latency hides behind
+        // the MFMAs of head h+1 (no weight is carried from one iteration to the next)
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wq_lds + h * 16 + 4 * g);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wq_lds + (h + 1) * 16 + 4 * g);
+        issue(1);
+        fold(0, w0);
+        load(0, h + 2);
+        issue(0);
+        fold(1, w1);
+        load(1, min(h + 3, h_idx - 1));
+    }
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(wq_lds + h * 16 + 4 * g);
+    if (h + 1 < h_idx) {
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wq_lds + (h + 1) * 16 + 4 * g);
+        issue(1);
+        fold(0, w0);
+        fold(1, w1);
+    } else {
+        fold(0, w0);
     }
 }
 
@@ -118,7 +131,7 @@ struct PageArgs {
 // Candidate emission of the fused scoring + top-k: query i keeps every
 // visible pool whose (key, pool) is at least (tau[2i], tau[2i+1]) in the
 // order "larger key first, then lower pool first"; count[i] counts them all
-// and the first `cap` go to cand[i*cap ...] as (key, pool) in any order.
+// and the first `cap` go to cand[i*cap ...] as (score bits, pool) in any order.
 struct EmitArgs {
     const uint32_t* tau;
     int32_t* count;
@@ -138,10 +151,11 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
     uint8_t* q_lds = smem;                                                 // [h_idx][QT][128]
     float* wq_lds = reinterpret_cast<float*>(smem + (size_t)h_idx * SC_QT * 128);  // [h_idx][QT]
     __shared__ int lo_s[SC_QT], hi_s[SC_QT];
-    __shared__ int plo_s, phi_s;
-    // emission: thresholds, per-chunk candidate counts and write cursors
-    __shared__ uint32_t tk_s[SC_QT];
-    __shared__ int tp_s[SC_QT], lcnt_s[SC_QT], lcur_s[SC_QT];
+    __shared__ int plo_s, phi_s, maxlo_s, minhi_s;
+    // emission: thresholds (as the score whose key they are, and "every pool"),
+    // per-chunk candidate counts and write cursors
+    __shared__ float tf_s[SC_QT];
+    __shared__ int tp_s[SC_QT], tall_s[SC_QT], lcnt_s[SC_QT], lcur_s[SC_QT];
     // paged keys: the distinct documents of the tile (pool range, table row)
     __shared__ int ndoc_s, dlo_s[SC_QT], dhi_s[SC_QT], dtab_s[SC_QT];
 
@@ -157,6 +171,11 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
     if (tid < SC_QT) {
         int lo = 0, hi = 0, doc = -1;
         int i = q0 + tid;
+        if (EMIT) {   // (a slot past the last query: no pool clears its threshold)
+            tf_s[tid] = __uint_as_float(0x7FFFFFFFu);
+            tall_s[tid] = 0;
+            tp_s[tid] = -1;
+        }
         if (i < num_q) {
             int t = q_pos ? q_pos[i] : i;
             QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
@@ -164,7 +183,12 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
             hi = qp.pool_lo + qp.n_vis;
             doc = qp.doc;
             if (EMIT) {
-                tk_s[tid] = em.tau[2 * i];
+                // key K = tau[2i] as a score: a score s of key k has k >= K exactly when
+                // s >= that score (keys order scores; -0 and +0 share a key and compare
+                // equal). K = 0 (every pool, NaN included) is the flag tall.
+                const uint32_t tk = em.tau[2 * i];
+                tf_s[tid] = __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
+                tall_s[tid] = tk == 0u;
                 tp_s[tid] = (int)em.tau[2 * i + 1];
             }
         }
@@ -174,15 +198,24 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
         if (PAGED) dtab_s[tid] = doc;   // (documents, deduplicated below)
     }
     __syncthreads();
-    if (tid == 0) {   // the pools any query of the tile sees lie in [plo, phi)
-        int plo = 0x7FFFFFFF, phi = 0;
-        for (int q = 0; q < SC_QT; ++q)
+    if (tid == 0) {
+        // the pools any query of the tile sees lie in [plo, phi); every query of
+        // the tile sees all of [maxlo, minhi)
+        int plo = 0x7FFFFFFF, phi = 0, maxlo = 0, minhi = 0x7FFFFFFF;
+        for (int q = 0; q < SC_QT; ++q) {
             if (lo_s[q] < hi_s[q]) {
                 plo = min(plo, lo_s[q]);
                 phi = max(phi, hi_s[q]);
             }
+            if (q0 + q < num_q) {
+                maxlo = max(maxlo, lo_s[q]);
+                minhi = min(minhi, hi_s[q]);
+            }
+        }
         plo_s = plo;
         phi_s = phi;
+        maxlo_s = maxlo;
+        minhi_s = minhi;
         if (PAGED) {
             // per distinct document: its first pool, the end of what the tile's
             // queries see of it, and its row of the page table
@@ -205,7 +238,7 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
         }
     }
     __syncthreads();
-    const int plo = plo_s, phi = phi_s;
+    const int plo = plo_s, phi = phi_s, maxlo = maxlo_s, minhi = minhi_s;
     const int P_first = (plo / SC_PC + split) * SC_PC;
     if (plo >= phi || P_first >= phi) return;
 
@@ -250,9 +283,11 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
     // (the chunk loop is uniform over the workgroup: emission synchronises it)
     for (int P0 = P_first; P0 < phi; P0 += SC_PC * nsplit) {
         const int Pw = P0 + wave * SC_PW;
-        // skip the block if no query of the tile sees any of its pools
-        bool seen = false;
-        for (int q = 0; q < SC_QT; ++q) seen |= max(lo_s[q], Pw) < min(hi_s[q], Pw + SC_PW);
+        // skip the block if it lies outside what the tile's queries see (their
+        // union's hull: a block in a gap is computed and then dropped); a block
+        // every query sees whole needs no per-pool visibility test
+        const bool seen = Pw < phi && Pw + SC_PW > plo;
+        const bool full = Pw >= maxlo && Pw + SC_PW <= minhi;
         if (!EMIT && !seen) continue;
 
         f32x4 acc[SC_NJ];
@@ -302,35 +337,48 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int q = 4 * g + e;
                 if (q0 + q >= num_q) continue;
-                const int lo = lo_s[q], hi = hi_s[q];
                 float* orow = scores + (size_t)(q0 + q) * max_pools;
+                if (full) {
 #pragma unroll
-                for (int j = 0; j < SC_NJ; ++j) {
-                    const int p = Pw + 16 * j + n;
-                    if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
+                    for (int j = 0; j < SC_NJ; ++j) orow[Pw + 16 * j + n] = acc[j][e] * skj[j];
+                } else {
+                    const int lo = lo_s[q], hi = hi_s[q];
+#pragma unroll
+                    for (int j = 0; j < SC_NJ; ++j) {
+                        const int p = Pw + 16 * j + n;
+                        if (p >= lo && p < hi) orow[p] = acc[j][e] * skj[j];
+                    }
                 }
             }
         } else {
             // candidates of this block: bit 4j+e for query 4g+e and pool Pw+16j+n
-            uint32_t cm = 0u, key[SC_NJ][4];
+            // (the threshold test on the score itself; keys are formed in the
+            // select, from the stored score bits)
+            uint32_t cm = 0u;
+            float sc[SC_NJ][4];
             if (seen) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int q = 4 * g + e;
-                    const int lo = lo_s[q], hi = hi_s[q];
-                    const uint32_t tk = tk_s[q];
+                    const float tf = tf_s[q];
                     const int tp = tp_s[q];
+                    const bool tall = tall_s[q] != 0;
+                    // (slots past the last query have lo = hi = 0: never "seen in full")
+                    const bool fq = full && q0 + q < num_q;
+                    const int lo = fq ? 0 : lo_s[q], hi = fq ? 0x7FFFFFFF : hi_s[q];
 #pragma unroll
                     for (int j = 0; j < SC_NJ; ++j) {
                         const int p = Pw + 16 * j + n;
-                        key[j][e] = score_key(acc[j][e] * skj[j]);
-                        const bool c = p >= lo && p < hi && (key[j][e] > tk || (key[j][e] == tk && p <= tp));
+                        sc[j][e] = acc[j][e] * skj[j];
+                        const bool c = p >= lo && p < hi && (tall || sc[j][e] > tf || (sc[j][e] == tf && p <= tp));
                         cm |= (uint32_t)c << (4 * j + e);
                     }
                 }
             }
             // count per query, reserve one range of each query's list, then write
-            for (uint32_t m = cm; m; m &= m - 1) atomicAdd(&lcnt_s[4 * g + (__builtin_ctz(m) & 3)], 1);
+#pragma unroll
+            for (int b = 0; b < 4 * SC_NJ; ++b)
+                if (cm >> b & 1u) atomicAdd(&lcnt_s[4 * g + (b & 3)], 1);
             __syncthreads();
             if (tid < SC_QT) {
                 const int c = lcnt_s[tid];
@@ -338,10 +386,14 @@ __global__ __launch_bounds__(SC_THREADS, 4) void score_kernel(
                 lcnt_s[tid] = 0;
             }
             __syncthreads();
-            for (uint32_t m = cm; m; m &= m - 1) {
-                const int b = __builtin_ctz(m), j = b >> 2, e = b & 3, q = 4 * g + e;
-                const int pos = atomicAdd(&lcur_s[q], 1);
-                if (pos < em.cap) em.cand[(size_t)(q0 + q) * em.cap + pos] = make_uint2(key[j][e], Pw + 16 * j + n);
+#pragma unroll
+            for (int b = 0; b < 4 * SC_NJ; ++b) {
+                const int j = b >> 2, e = b & 3, q = 4 * g + e;
+                if (cm >> b & 1u) {
+                    const int pos = atomicAdd(&lcur_s[q], 1);
+                    if (pos < em.cap)
+                        em.cand[(size_t)(q0 + q) * em.cap + pos] = make_uint2(__float_as_uint(sc[j][e]), Pw + 16 * j + n);
+                }
             }
         }
     }

@@ -108,7 +108,7 @@ template <int D, int DR>
 __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ indices,
     int num_kv, int heads, int row_width, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int nsplit, float* __restrict__ o_part, float* __restrict__ lse_part) {
     constexpr int NW = MLA_NW;
     constexpr int NT = 64 * NW;             // threads
     constexpr int DP = D < 128 ? 128 : D;   // latent width in LDS (zero-padded)
@@ -141,7 +141,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int rh = wave >> 1;   // row half of every tile
     const int hh = wave & 1;    // head half
-    const int i = xcd_query(blockIdx.x, gridDim.x);
+    // one workgroup per query, or (nsplit > 1, few queries) per query and split:
+    // split sp takes the tiles [ntiles*sp/nsplit, ntiles*(sp+1)/nsplit) of the
+    // compacted row and leaves a normalised partial O and its lse for the combine
+    const int i = nsplit == 1 ? xcd_query(blockIdx.x, gridDim.x) : (int)(blockIdx.x / nsplit);
+    const int sp = nsplit == 1 ? 0 : (int)(blockIdx.x % nsplit);
 
     // ---- compact the index row (valid entries, original order) ----------------
     // Entry NT*k + tid is read in round k; the loads of all rounds are issued
@@ -212,14 +216,20 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             if (lane >= o) x += u;
         }
         n_valid = __builtin_amdgcn_readfirstlane(__shfl(x, 63, 64));
+        // this workgroup's entries: [e0, e1) of the compacted row, stored from 0
+        const int nt_all = (n_valid + MLA_TK - 1) / MLA_TK;
+        const int e0 = nt_all * sp / nsplit * MLA_TK;
+        const int e1 = min(n_valid, nt_all * (sp + 1) / nsplit * MLA_TK);
+        n_valid = max(0, e1 - e0);
         const int excl = x - c;   // entries before (round, wave) = lane's pair
 #pragma unroll
         for (int k = 0; k < NRND; ++k) {
             const int base = __shfl(excl, k * NW + wave, 64);
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0u));
-            if (ent[k] >= 0 && ent[k] < num_kv)   // byte offset (the latent is below 4 GiB)
-                list[base + below] = (int32_t)((uint32_t)ent[k] * (uint32_t)(DQK * 2));
+            const int pos = base + (int)below;
+            if (ent[k] >= 0 && ent[k] < num_kv && pos >= e0 && pos < e1)   // byte offset (the latent is below 4 GiB)
+                list[pos - e0] = (int32_t)((uint32_t)ent[k] * (uint32_t)(DQK * 2));
         }
     }
     __syncthreads();
@@ -237,10 +247,16 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     }
     __syncthreads();
 
-    uint16_t* orow = out + (size_t)i * heads * D;
     if (n_valid == 0) {
-        for (int e = tid; e < heads * D; e += NT) orow[e] = 0;
-        if (lse && tid < heads) lse[(size_t)i * heads + tid] = -INFINITY;
+        if (nsplit == 1) {
+            uint16_t* orow = out + (size_t)i * heads * D;
+            for (int e = tid; e < heads * D; e += NT) orow[e] = 0;
+            if (lse && tid < heads) lse[(size_t)i * heads + tid] = -INFINITY;
+        } else {
+            float* prow = o_part + (size_t)blockIdx.x * heads * D;
+            for (int e = tid; e < heads * D; e += NT) prow[e] = 0.0f;
+            if (tid < heads) lse_part[(size_t)blockIdx.x * heads + tid] = -INFINITY;
+        }
         return;
     }
     const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
@@ -636,8 +652,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         const float M = fmaxf(m_ref[ht], mp[0]);
         fa[ht] = __builtin_amdgcn_exp2f(m_ref[ht] - M);
         fb[ht] = __builtin_amdgcn_exp2f(mp[0] - M);
-        if (lse && rh == 0 && g == 0 && head < heads)
-            lse[(size_t)i * heads + head] = (M + log2f(le[ht] * fa[ht] + mp[2] * fb[ht])) * 0.69314718055994530942f;
+        const float lse_h = (M + log2f(le[ht] * fa[ht] + mp[2] * fb[ht])) * 0.69314718055994530942f;
+        if (rh == 0 && g == 0 && head < heads) {
+            if (nsplit > 1) lse_part[(size_t)blockIdx.x * heads + head] = lse_h;
+            else if (lse) lse[(size_t)i * heads + head] = lse_h;
+        }
         const float inv = 1.0f / (lr[ht] * fa[ht] + mp[1] * fb[ht]);
         fa[ht] *= inv;   // the merge weights with the normaliser folded in
         fb[ht] *= inv;
@@ -667,20 +686,146 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             }                                                                                  \
         }                                                                                      \
     }
-    if (rh == 0) {
+    // (a split's partial O in fp32: the combine rounds once, at the end)
+#define KP_FINISH_PART(RH)                                                                     \
+    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
+        const int head_ = 32 * hh + 16 * ht + n;                                               \
+        float* dst_ = o_part + ((size_t)blockIdx.x * heads + head_) * D;                       \
+        f32x4 op_[CT / 2];                                                                     \
+        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
+            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((2 * j + ht) * 64 + lane) * 16);    \
+        if (head_ < heads) {                                                                   \
+            _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                               \
+                const int ct_ = (CT / 2) * (RH) + j;                                           \
+                const int col_ = 16 * ct_ + 4 * g;                                             \
+                if (DP == D || col_ < D) {                                                     \
+                    f32x4 r_;                                                                  \
+                    _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
+                        r_[e] = __builtin_fmaf(o[ct_][ht][e], fa[ht], op_[j][e] * fb[ht]);     \
+                    *reinterpret_cast<f32x4*>(dst_ + col_) = r_;                               \
+                }                                                                              \
+            }                                                                                  \
+        }                                                                                      \
+    }
+    if (nsplit > 1) {
+        if (rh == 0) {
+            KP_FINISH_PART(0)
+        } else {
+            KP_FINISH_PART(1)
+        }
+    } else if (rh == 0) {
         KP_FINISH(0)
     } else {
         KP_FINISH(1)
     }
 #undef KP_FINISH
+#undef KP_FINISH_PART
+}
+
+// Merge of the splits of each (query, head): lse = log sum_s exp(lse_s), and
+// out = sum_s exp(lse_s - lse) O_s, rounded once to bf16. One wave per (query,
+// head); lane l holds columns l*CPL .. +CPL-1.
+template <int D>
+__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ o_part,
+                                                          const float* __restrict__ lse_part, int num_q, int heads,
+                                                          int nsplit, uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+    constexpr int CPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const long long wq = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wq >= (long long)num_q * heads) return;
+    const int i = (int)(wq / heads), h = (int)(wq % heads);
+    // the split lse values, one per lane (nsplit <= 64), and their max
+    const float myl = lane < nsplit ? lse_part[((size_t)i * nsplit + lane) * heads + h] : -INFINITY;
+    float m = myl;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
+    float L = -INFINITY;
+    if (m != -INFINITY) {
+        float e = lane < nsplit ? __expf(myl - m) : 0.0f;
+        float sum = e;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        L = m + __logf(sum);
+        for (int s = 0; s < nsplit; ++s) {
+            const float ls = __shfl(myl, s, 64);
+            if (ls == -INFINITY) continue;
+            const float wgt = __expf(ls - L);
+            const float* src = o_part + (((size_t)i * nsplit + s) * heads + h) * D + lane * CPL;
+            if constexpr (CPL % 4 == 0) {
+#pragma unroll
+                for (int c = 0; c < CPL; c += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(src + c);
+                    acc[c] = __builtin_fmaf(wgt, v.x, acc[c]);
+                    acc[c + 1] = __builtin_fmaf(wgt, v.y, acc[c + 1]);
+                    acc[c + 2] = __builtin_fmaf(wgt, v.z, acc[c + 2]);
+                    acc[c + 3] = __builtin_fmaf(wgt, v.w, acc[c + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[c] = __builtin_fmaf(wgt, src[c], acc[c]);
+            }
+        }
+    }
+    uint16_t* dst = out + ((size_t)i * heads + h) * D + lane * CPL;
+    if constexpr (CPL % 8 == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; c += 8) {
+            uint4 pk;
+            pk.x = f32_to_bf16_rne(acc[c]) | ((uint32_t)f32_to_bf16_rne(acc[c + 1]) << 16);
+            pk.y = f32_to_bf16_rne(acc[c + 2]) | ((uint32_t)f32_to_bf16_rne(acc[c + 3]) << 16);
+            pk.z = f32_to_bf16_rne(acc[c + 4]) | ((uint32_t)f32_to_bf16_rne(acc[c + 5]) << 16);
+            pk.w = f32_to_bf16_rne(acc[c + 6]) | ((uint32_t)f32_to_bf16_rne(acc[c + 7]) << 16);
+            *reinterpret_cast<uint4*>(dst + c) = pk;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) dst[c] = f32_to_bf16_rne(acc[c]);
+    }
+    if (lse && lane == 0) lse[(size_t)i * heads + h] = L;
+}
+
+// Splits per query row: few queries (decode) leave most compute units idle
+// with one workgroup per query, so each row is cut into up to 16 tile ranges
+// (at least two tiles each) when there are fewer than 128 queries.
+int sparse_mla_splits(int num_q, int row_width) {
+    if (num_q <= 0 || num_q >= 128) return 1;
+    const int tiles = (row_width + MLA_TK - 1) / MLA_TK;
+    int s = 256 / num_q;
+    if (s > 16) s = 16;
+    if (s > tiles / 2) s = tiles / 2;
+    return s < 1 ? 1 : s;
+}
+
+size_t sparse_mla_part_bytes(int num_q, int heads, int d_latent, int row_width) {
+    const int s = sparse_mla_splits(num_q, row_width);
+    if (s == 1) return 0;
+    const int dv = d_latent == 576 ? 512 : d_latent;
+    const size_t o = (size_t)num_q * s * heads * dv * sizeof(float);
+    return ((o + 255) & ~(size_t)255) + (size_t)num_q * s * heads * sizeof(float);
 }
 
 template <int D, int DR>
 static hipError_t launch_mla_t(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int num_q,
                                int num_kv, int heads, int row_width, float scale_log2, uint16_t* out,
-                               float* lse, hipStream_t stream) {
-    sparse_mla_kernel<D, DR><<<num_q, 64 * MLA_NW, 0, stream>>>(q, kv, indices, num_kv, heads, row_width,
-                                                                 scale_log2, out, lse);
+                               float* lse, void* part, hipStream_t stream) {
+    const int ns = part ? sparse_mla_splits(num_q, row_width) : 1;
+    float* o_part = static_cast<float*>(part);
+    float* lse_part = nullptr;
+    if (ns > 1) {
+        const size_t o = (size_t)num_q * ns * heads * D * sizeof(float);
+        lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(part) + ((o + 255) & ~(size_t)255));
+    }
+    sparse_mla_kernel<D, DR><<<num_q * ns, 64 * MLA_NW, 0, stream>>>(q, kv, indices, num_kv, heads, row_width,
+                                                                      scale_log2, out, lse, ns, o_part, lse_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1) return e;
+    const long long waves = (long long)num_q * heads;
+    mla_combine_kernel<D><<<(unsigned)((waves + 3) / 4), 256, 0, stream>>>(o_part, lse_part, num_q, heads, ns, out,
+                                                                             lse);
     return hipGetLastError();
 }
 
@@ -688,13 +833,15 @@ int sparse_mla_max_row_width(int d_latent) { return d_latent == 576 ? 2048 : MLA
 
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int num_q,
                              int num_kv, int heads, int d_latent, int row_width, float scale_log2,
-                             uint16_t* out, float* lse, hipStream_t stream) {
+                             uint16_t* out, float* lse, void* part, hipStream_t stream) {
     if (num_q == 0) return hipSuccess;
     if (d_latent == 576)
-        return launch_mla_t<512, 64>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
+        return launch_mla_t<512, 64>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, part,
+                                     stream);
     if (d_latent == 512)
-        return launch_mla_t<512, 0>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
-    return launch_mla_t<64, 0>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, stream);
+        return launch_mla_t<512, 0>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, part,
+                                    stream);
+    return launch_mla_t<64, 0>(q, kv, indices, num_q, num_kv, heads, row_width, scale_log2, out, lse, part, stream);
 }
 
 }  // namespace kp

@@ -54,8 +54,9 @@ def test_workspace_size(L):
     # rows of at least 32768 pools with top-k <= 8192: no score tensor, 128 KiB of
     # candidates per query instead (the 1M-token decode: 64 MiB of scores -> 8 MiB)
     q_part = 64 * 32 * 128 + 64 * 32 * 4
+    per_q = 16384 * 8
     fused = L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128, 512)
-    assert q_part + 64 * 16384 * 8 <= fused < q_part + 64 * 16384 * 8 + 4096
+    assert q_part + 64 * per_q <= fused < q_part + 64 * per_q + 8192
     assert L.kp_indexer_workspace_bytes(64, 1 << 18, 32, 128, 8193) >= 64 * (1 << 18) * 4   # top-k too large
     assert L.kp_indexer_workspace_bytes(64, 32767, 32, 128, 512) >= 64 * 32767 * 4          # rows too short
     # the paged path: the pool layout, the queries and the candidate lists
@@ -94,29 +95,29 @@ def test_invalid_args_rejected_on_host(L):
     assert L.indexer_score_topk(*a) == 1
     assert b"workspace" in L.kp_last_error()
     # unsupported head count / latent width
-    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 65, 512, 128, C.c_float(0.1), fake, None, None) == 2
-    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 640, 128, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 65, 512, 128, C.c_float(0.1), fake, None, None, 0, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 640, 128, C.c_float(0.1), fake, None, None, 0, None) == 2
     # 576-wide keys (the RoPE-tail contract) take index rows of at most 2048 entries
-    assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 576, 2048, C.c_float(0.1), fake, None, None) == 0
-    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 2176, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 576, 2048, C.c_float(0.1), fake, None, None, 0, None) == 0
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 576, 2176, C.c_float(0.1), fake, None, None, 0, None) == 2
     # the backward takes 64- and 512-wide latents
     assert L.sparse_mla_bwd(fake, fake, fake, fake, fake, fake, 4, 10, 64, 576, 128, C.c_float(0.1), fake, fake,
                             fake, 1 << 30, None) == 2
-    assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 1
+    assert L.sparse_mla_fwd(None, fake, fake, 4, 10, 64, 512, 128, C.c_float(0.1), fake, None, None, 0, None) == 1
     # a latent of more than 4 GiB - 4 KiB (the row loads address it from 4 KiB below)
-    assert L.sparse_mla_fwd(fake, fake, fake, 4, 1 << 22, 64, 512, 128, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 1 << 22, 64, 512, 128, C.c_float(0.1), fake, None, None, 0, None) == 2
     assert b"4 GiB" in L.kp_last_error()
     # the boundary: 4,194,300 rows of 1 KiB are exactly 4 GiB - 4 KiB (the descriptor's
     # record count would wrap to 0), one row fewer fits (checked with no queries: no launch)
     edge = ((1 << 32) - 4096) // 1024
-    assert L.sparse_mla_fwd(fake, fake, fake, 0, edge, 64, 512, 128, C.c_float(0.1), fake, None, None) == 2
-    assert L.sparse_mla_fwd(fake, fake, fake, 0, edge - 1, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, edge, 64, 512, 128, C.c_float(0.1), fake, None, None, 0, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, edge - 1, 64, 512, 128, C.c_float(0.1), fake, None, None, 0, None) == 0
     # index rows wider than the attention's LDS list
-    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 4097, C.c_float(0.1), fake, None, None) == 2
+    assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 4097, C.c_float(0.1), fake, None, None, 0, None) == 2
     assert b"row_width" in L.kp_last_error()
-    assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 512, 128, C.c_float(0.1), fake, None, None) == 0
+    assert L.sparse_mla_fwd(fake, fake, fake, 0, 10, 64, 512, 128, C.c_float(0.1), fake, None, None, 0, None) == 0
     for bad in (0.0, -0.1, float("inf"), float("nan")):          # the softmax scale must be positive
-        assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 128, C.c_float(bad), fake, None, None) == 1
+        assert L.sparse_mla_fwd(fake, fake, fake, 4, 10, 64, 512, 128, C.c_float(bad), fake, None, None, 0, None) == 1
     # the allocation-free variant: argument checks as indexer_score_topk's, and sizes
     # whose workspace exceeds the library's device scratch are refused before launch
     nargs = lambda T, nq, qpos: (fake, 1, T, fake, T // 4, fake, fake, qpos, nq, fake, fake, 32, 128, 4, 512, 2176,

@@ -203,15 +203,15 @@ def test_fused_ties(K, oracle_mod):
 
 @pytest.mark.parametrize("mode", ["too_few", "too_many"])
 def test_fused_rescoring_rows(K, oracle_mod, mode):
-    """Key scales that make every 64th pool of a row (the sampled ones) score far
-    above (too_few: fewer than k pools clear the threshold) or far below
+    """Key scales that make every 128th pool of a row (the sampled ones) score
+    far above (too_few: fewer than k pools clear the threshold) or far below
     (too_many: more than 16,384 clear it) the rest: those rows are selected by
     the exact rescoring path, with the same result as the score-tensor path."""
     cu = np.array([0, 1 << 17], np.int32)
     q_pos = np.array([(1 << 17) - 9, (1 << 17) - 2, 70_001, 40_000], np.int32)   # the last: 10,000 pools
     cp, k8, sk, q_idx, w = _rand_case(oracle_mod, 14, cu, q_pos)
     w = np.abs(w)                                      # scores >= 0: nearly every pool clears a tiny threshold
-    sampled = (np.arange(len(sk)) % 64) == 0           # one document: its rows start at pool 0
+    sampled = (np.arange(len(sk)) % 128) == 0          # one document: its rows start at pool 0
     sk[sampled] *= 1000.0 if mode == "too_few" else 1e-3
     _log("fused rescoring", mode)
     _run_all(K, oracle_mod, mode, cu, cp, k8, sk, q_idx, w, q_pos, 512, seed=3,

@@ -295,14 +295,17 @@ def test_mla_fed_oracle_rows(K, oracle_mod, name):
     _log("  ", info)
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("case", ["scattered_mask", "empty_rows", "single", "duplicates", "heads40",
                                   "rising", "rising_tail", "max_width"])
-def test_mla_edge_rows(K, oracle_mod, case):
+def test_mla_edge_rows(K, oracle_mod, case, split):
     """Edge rows of the attention. "rising" and "rising_tail" put rows whose
     scores lie hundreds of log2 units above those of the first tile after it
     (from the second tile on, or only in the last tile): a pass that takes its
     softmax reference from the first tile cannot hold them, so the kernel must
-    fall back to its exact-max passes and still agree with the oracle."""
+    fall back to its exact-max passes and still agree with the oracle. With
+    split, these few-query launches cut each row into tile ranges (2 to 16)
+    that are merged afterwards; without, one workgroup takes each row."""
     rng = np.random.default_rng(3)
     H, D, N, W, Tq = 64, 512, 3000, 256, 9
     if case == "heads40":
@@ -335,8 +338,8 @@ def test_mla_edge_rows(K, oracle_mod, case):
     if case == "max_width":   # row 0 full; rows 1, 2 with masked entries spread over the row
         idx[1:][rng.random((Tq - 1, W)) < 0.3] = -1
         idx[2, W - 50:] = -1
-    _log("mla edge", case)
-    g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), 1 / np.sqrt(D))
+    _log("mla edge", case, "split" if split else "whole rows")
+    g_out, g_lse = K.sparse_mla_fwd(dev_bf16(q), dev_bf16(kv), dev(idx), 1 / np.sqrt(D), split=split)
     # (errors are scaled by sum_j p_j |v_j|, as in the fed-oracle test: the bf16
     # weights perturb each p_j by up to 2^-9 of itself, which moves an output by
     # that much of the spread of the values it mixes)
@@ -398,6 +401,52 @@ def test_mla_many_queries(K, oracle_mod, case):
     # (half the latent rows are scaled by 100: a scaled check)
     info = check_out(host_bf16_f32(g_out), ref_out, case, ref_abs=ref_abs, scaled=True)
     info["lse"] = check_lse(host(g_lse), ref_lse, case, scaled=True)
+    _log("  ", info)
+
+
+@pytest.mark.parametrize("D", [512, 576, 64])
+def test_mla_split_decode(K, oracle_mod, D):
+    """A decode-shaped launch (64 queries, rows of 2176 entries, or 2048 for
+    576-wide keys: four tile ranges per row) with ragged, masked, empty and single-entry rows: the split
+    path against the oracle, and against the whole-row path to within the
+    bf16 rounding of the output (each path rounds its fp32 result once)."""
+    rng = np.random.default_rng(17)
+    H, N, Tq = 64, 5000, 64
+    W = 2048 if D == 576 else 2176                # (576-wide keys take rows of at most 2048)
+    from workloads import f32_to_bf16_bits
+    q = f32_to_bf16_bits(rng.standard_normal((Tq, H, D)))
+    kv = f32_to_bf16_bits(rng.standard_normal((N, D)))
+    idx = rng.integers(0, N, size=(Tq, W)).astype(np.int32)
+    idx[1] = -1                                   # empty
+    idx[2, :] = -1
+    idx[2, 1500] = 9                              # one entry, in the third range
+    idx[3, 600:] = -1                             # ragged: the later ranges are empty
+    idx[4][rng.random(W) < 0.5] = -1              # scattered masks
+    nd = min(2051, W)
+    idx[5, :nd] = rng.integers(0, N, nd)          # the decode row: 2051 entries, then padding
+    idx[5, nd:] = -1
+    assert K.kp_mla_fwd_workspace_bytes(Tq, H, D, W) > 0
+    scale = 1 / np.sqrt(D)
+    qd, kvd, idxd = dev_bf16(q), dev_bf16(kv), dev(idx)
+    s_out, s_lse = K.sparse_mla_fwd(qd, kvd, idxd, scale, split=True)
+    w_out, w_lse = K.sparse_mla_fwd(qd, kvd, idxd, scale, split=False)
+    dv = 512 if D == 576 else D
+    if D == 576:
+        ref_out, ref_lse, ref_abs = oracle_mod.sparse_mla_dv(q, kv, idx, scale, 512, with_abs=True)
+    else:
+        ref_out, ref_lse, ref_abs = oracle_mod.sparse_mla(q, kv, idx, scale, with_abs=True)
+    info = check_out(host_bf16_f32(s_out), ref_out, f"split D={D}", ref_abs=ref_abs)
+    info["lse"] = check_lse(host(s_lse), ref_lse, f"split D={D}")
+    # two bf16 ulps of the larger of the output and the magnitude of the terms it sums
+    a, b = host_bf16_f32(s_out).astype(np.float64), host_bf16_f32(w_out).astype(np.float64)
+    unit = np.maximum(np.maximum(np.abs(b), ref_abs), 2.0 ** -100) * 2.0 ** -8
+    info["split_vs_whole_ulps"] = float((np.abs(a - b) / unit).max())
+    assert info["split_vs_whole_ulps"] <= 2.0, info
+    assert np.array_equal(np.isneginf(host(s_lse)), np.isneginf(host(w_lse)))
+    fin = np.isfinite(host(w_lse))
+    info["lse_split_vs_whole"] = float(np.abs(host(s_lse)[fin] - host(w_lse)[fin]).max())
+    assert info["lse_split_vs_whole"] <= 1e-4
+    assert np.all(host_bf16_f32(s_out)[1] == 0) and s_out.shape == (Tq, H, dv)
     _log("  ", info)
 
 
