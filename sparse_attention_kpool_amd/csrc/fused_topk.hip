@@ -13,10 +13,12 @@
 //
 //   1. fused_thresh_kernel, one workgroup per query: rows of at most `cap`
 //      visible pools take every pool as a candidate; longer rows score every
-//      s-th pool (s >= 128, at most 16384 samples) and take as threshold the
-//      sample of rank r = T*m/n in that order (m samples, n pools, T the
-//      target count max(2k, cap/2)), so about T pools clear it when the
-//      samples are representative. Only its count decides correctness.
+//      s-th pool and take as threshold the sample of rank r = T*m/n in that
+//      order (m samples, n pools, T the target count max(4k, cap/4), at most
+//      3/4 cap; s ~ T/16, so r ~ 16 and at most 16384 samples): about T pools
+//      clear it when the samples are representative, with a spread of about a
+//      quarter of T (1/sqrt(r)); falling below k or above cap needs a count
+//      some seven spreads away. Only its count decides correctness.
 //   2. score_kernel in its emitting form (score.hip) scores every visible
 //      pair and appends the pairs at or above the threshold, as (score bits,
 //      pool), to the query's candidate list, counting all of them.
@@ -43,7 +45,6 @@
 
 namespace kp {
 
-constexpr int FT_STRIDE_MIN = 128;     // sampling stride, at least
 constexpr int FT_TH_THREADS = 512;
 constexpr int FT_SEL_THREADS = 1024;
 constexpr int FT_SEL_WAVES = FT_SEL_THREADS / 64;
@@ -59,8 +60,9 @@ struct KeyRows {
 
 // Row of pool p of the document whose first pool is plo and whose page-table
 // row starts at tab (-1: its page is missing or past the table row).
+template <bool PAGED>
 __device__ __forceinline__ long long key_row(const KeyRows& kr, int p, int plo, long long tab) {
-    if (!kr.table) return p;
+    if (!PAGED) return p;
     const int l = p - plo;
     if ((l >> 5) >= kr.max_pages) return -1;
     const int pn = kr.table[tab + (l >> 5)];
@@ -75,26 +77,41 @@ struct HmQuery {
     float wv[4][4];
 };
 
+// (every load is unconditional, its address clamped into the query's rows and
+// the value zeroed after when it lies outside: a load under a condition costs
+// a wait for all loads in flight)
 __device__ __forceinline__ void hm_load_query(HmQuery& hq, const uint8_t* __restrict__ q8,
                                               const float* __restrict__ sq, const float* __restrict__ w, int i,
                                               int h_idx, int d_idx) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const int dchunks = d_idx >> 4;
+    uint4 lo4[4], hi4[4];
+    float wv[4][4], sv[4][4];
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
-        const int head = 16 * hg + n;
-        uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
-        if (head < h_idx) {
-            const uint8_t* src = q8 + ((size_t)i * h_idx + head) * d_idx + 32 * g;
-            if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src);
-            if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 16);
-        }
-        hq.a[hg] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        const int head = min(16 * hg + n, h_idx - 1);
+        const uint8_t* src = q8 + ((size_t)i * h_idx + head) * d_idx;
+        lo4[hg] = *reinterpret_cast<const uint4*>(src + 16 * min(2 * g, dchunks - 1));
+        hi4[hg] = *reinterpret_cast<const uint4*>(src + 16 * min(2 * g + 1, dchunks - 1));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int h = 16 * hg + 4 * g + e;
-            const size_t o = (size_t)i * h_idx + h;
-            hq.wv[hg][e] = h < h_idx ? w[o] * sq[o] : 0.0f;
+            const size_t o = (size_t)i * h_idx + min(16 * hg + 4 * g + e, h_idx - 1);
+            wv[hg][e] = w[o];
+            sv[hg][e] = sq[o];
+        }
+    }
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+        const bool hv = 16 * hg + n < h_idx;
+        const uint32_t ml = hv && 2 * g < dchunks ? 0xFFFFFFFFu : 0u;
+        const uint32_t mh = hv && 2 * g + 1 < dchunks ? 0xFFFFFFFFu : 0u;
+        const uint4 l = lo4[hg], u = hi4[hg];
+        hq.a[hg] = i32x8{(int)(l.x & ml), (int)(l.y & ml), (int)(l.z & ml), (int)(l.w & ml),
+                         (int)(u.x & mh), (int)(u.y & mh), (int)(u.z & mh), (int)(u.w & mh)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t mw = 16 * hg + 4 * g + e < h_idx ? 0xFFFFFFFFu : 0u;
+            hq.wv[hg][e] = __uint_as_float(__float_as_uint(wv[hg][e] * sv[hg][e]) & mw);
         }
     }
 }
@@ -102,19 +119,32 @@ __device__ __forceinline__ void hm_load_query(HmQuery& hq, const uint8_t* __rest
 // Key of pool n of a 16-pool tile for the query of hq: lane (n, g) names the
 // pool's key row (row < 0: no pool, key 0) and every lane of column n gets the
 // key. Called by whole waves.
+// B operand (32 code bytes of column n per lane) and key scale of the pool in
+// key row `row`; row < 0: zero (the loads read row 0 and are dropped).
+__device__ __forceinline__ void hm_load_pool(i32x8& b, float& s, const KeyRows& kr, int d_idx, long long row) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int dchunks = d_idx >> 4;
+    const size_t r = row >= 0 ? (size_t)row : 0;
+    const uint8_t* src = kr.k8 + r * d_idx;
+    const uint4 lo4 = *reinterpret_cast<const uint4*>(src + 16 * min(2 * g, dchunks - 1));
+    const uint4 hi4 = *reinterpret_cast<const uint4*>(src + 16 * min(2 * g + 1, dchunks - 1));
+    const uint32_t sc = __float_as_uint(kr.sk[r]);
+    // (zeroed by masks, not by selects: the compiler turns a select of a
+    // loaded value into a branch that waits for the load right there)
+    const uint32_t ml = row >= 0 && 2 * g < dchunks ? 0xFFFFFFFFu : 0u;
+    const uint32_t mh = row >= 0 && 2 * g + 1 < dchunks ? 0xFFFFFFFFu : 0u;
+    const uint32_t ms = row >= 0 ? 0xFFFFFFFFu : 0u;
+    b = i32x8{(int)(lo4.x & ml), (int)(lo4.y & ml), (int)(lo4.z & ml), (int)(lo4.w & ml),
+              (int)(hi4.x & mh), (int)(hi4.y & mh), (int)(hi4.z & mh), (int)(hi4.w & mh)};
+    s = __uint_as_float(sc & ms);
+}
+
 __device__ __forceinline__ uint32_t hm_tile_key(const HmQuery& hq, int h_idx, int d_idx, const KeyRows& kr,
                                                 long long row) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const int dchunks = d_idx >> 4;
-    uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
-    float s = 0.0f;
-    if (row >= 0) {
-        const uint8_t* src = kr.k8 + (size_t)row * d_idx + 32 * g;
-        if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src);
-        if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 16);
-        s = kr.sk[row];
-    }
-    const i32x8 b = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+    i32x8 b;
+    float s;
+    hm_load_pool(b, s, kr, d_idx, row);
     f32x4 d[4];
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg)
@@ -163,37 +193,25 @@ struct HmTiles {
 };
 
 __device__ __forceinline__ void hm_load_tiles(HmTiles& t, const KeyRows& kr, int d_idx, const long long (&row)[4]) {
-    const int g = (threadIdx.x & 63) >> 4;
-    const int dchunks = d_idx >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint4 lo4 = make_uint4(0u, 0u, 0u, 0u), hi4 = lo4;
-        float s = 0.0f;
-        if (row[j] >= 0) {
-            const uint8_t* src = kr.k8 + (size_t)row[j] * d_idx + 32 * g;
-            if (2 * g < dchunks) lo4 = *reinterpret_cast<const uint4*>(src);
-            if (2 * g + 1 < dchunks) hi4 = *reinterpret_cast<const uint4*>(src + 16);
-            s = kr.sk[row[j]];
-        }
-        t.b[j] = i32x8{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-        t.s[j] = s;
-    }
+    for (int j = 0; j < 4; ++j) hm_load_pool(t.b[j], t.s[j], kr, d_idx, row[j]);
 }
 
-// Key of the pool of lane (16g + n) among the 64 of a loaded block.
-__device__ __forceinline__ uint32_t hm_sample_key(const HmQuery& hq, int h_idx, const HmTiles& t) {
+// Key of the pool of lane (16g + n) among the 64 of a loaded block; NHG head
+// groups of 16 (a compile-time count: a branch per group would keep the
+// compiler from interleaving the tiles' MFMAs).
+template <int NHG>
+__device__ __forceinline__ uint32_t hm_sample_key(const HmQuery& hq, const HmTiles& t) {
     const int g = (threadIdx.x & 63) >> 4;
     uint32_t mine = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float acc = 0.0f;
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) {
-            if (16 * hg < h_idx) {
-                const f32x4 d = mfma_fp8_16x16x128(hq.a[hg], t.b[j], f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int hg = 0; hg < NHG; ++hg) {
+            const f32x4 d = mfma_fp8_16x16x128(hq.a[hg], t.b[j], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(hq.wv[hg][e], relu_f32(d[e]), acc);
-            }
+            for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(hq.wv[hg][e], relu_f32(d[e]), acc);
         }
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
@@ -208,8 +226,8 @@ __device__ __forceinline__ uint32_t hm_sample_key(const HmQuery& hq, int h_idx, 
 // samples, all the loads of its blocks issued before the first MFMA (one
 // memory latency), then the workgroup selects the threshold from the samples
 // in LDS.
-constexpr int FT_TH_BATCH = 4;   // sample blocks per wave per round
-template <bool PAGED>
+constexpr int FT_TH_BATCH = 2;   // sample blocks per wave per round
+template <bool PAGED, int NHG>
 __global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, const uint8_t* __restrict__ q8, const float* __restrict__ sq,
@@ -241,7 +259,10 @@ __global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
         }
         return;
     }
-    const int ss = max(FT_STRIDE_MIN, (n + FT_SAMPLE_MAX - 1) / FT_SAMPLE_MAX);
+    // target count T = max(4k, cap/4) (at most 3/4 cap), stride about T/16, so
+    // that the threshold is the sample of rank r ~ 16 (T = r n / m)
+    const int target = min(cap / 4 * 3, max(4 * k, cap / 4));
+    const int ss = max((n + FT_SAMPLE_MAX - 1) / FT_SAMPLE_MAX, max(1, target / 16));
     const int m = (n + ss - 1) / ss;   // samples: pools pool_lo + ss*j, j < m
     const long long tab = PAGED ? (long long)qp.doc * kr.max_pages : 0;
     for (int b0 = wave * 64; b0 < m; b0 += FT_TH_BATCH * NW * 64) {
@@ -252,21 +273,20 @@ __global__ __launch_bounds__(FT_TH_THREADS) void fused_thresh_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int sidx = b0 + u * NW * 64 + 16 * j + n16;
-                row[j] = sidx < m ? key_row(kr, qp.pool_lo + ss * sidx, qp.pool_lo, tab) : -1;
+                row[j] = sidx < m ? key_row<PAGED>(kr, qp.pool_lo + ss * sidx, qp.pool_lo, tab) : -1;
             }
             hm_load_tiles(tb[u], kr, d_idx, row);
         }
 #pragma unroll
         for (int u = 0; u < FT_TH_BATCH; ++u) {
             const int bu = b0 + u * NW * 64;
-            const uint32_t key = hm_sample_key(hq, h_idx, tb[u]);
+            const uint32_t key = hm_sample_key<NHG>(hq, tb[u]);
             if (bu + lane < m) keys[bu + lane] = key;
         }
     }
     __syncthreads();
 
-    const long long target = max(2 * k, cap / 2);
-    const int r = (int)max(1LL, min((long long)m, target * m / n));
+    const int r = (int)max(1LL, min((long long)m, (long long)target * m / n));
     uint32_t th;
     int teq;
     radix_select<NTH>([&](auto f) {
@@ -354,10 +374,8 @@ __global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
         for (int j0 = 0; j0 < cnt; j0 += NTH * 8) {
             uint2 c[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + tid + NTH * u;
-                c[u] = j < cnt ? src[j] : make_uint2(0u, 0u);
-            }
+            for (int u = 0; u < 8; ++u)   // (unconditional loads: entries past cnt re-read the last)
+                c[u] = src[min(j0 + tid + NTH * u, cnt - 1)];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = j0 + tid + NTH * u;
@@ -467,7 +485,7 @@ __global__ __launch_bounds__(FT_SEL_THREADS) void fused_select_kernel(
         auto block_key = [&](int base) -> uint32_t {   // key of pool base + lane (0 past hi)
             return hm_block_key(hq, h_idx, d_idx, kr, [&](int j) -> long long {
                 const int p = base + 16 * j + n16;
-                return p < hi ? key_row(kr, p, lo, tab) : -1;
+                return p < hi ? key_row<PAGED>(kr, p, lo, tab) : -1;
             });
         };
         uint32_t th;
@@ -514,14 +532,19 @@ hipError_t launch_fused_topk(const int32_t* cu, int num_docs, const int32_t* cu_
                              hipStream_t stream) {
     if (num_q == 0) return hipSuccess;
     const KeyRows kr{k8, sk, page_table, max_pages, num_pages};
-    if (page_table)
-        fused_thresh_kernel<true><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq, w,
-                                                                      h_idx, d_idx, kr, topk, FT_CAP, st.tau,
-                                                                      st.count);
-    else
-        fused_thresh_kernel<false><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq,
-                                                                       w, h_idx, d_idx, kr, topk, FT_CAP, st.tau,
-                                                                       st.count);
+#define KP_TH(PG, NH)                                                                                     \
+    fused_thresh_kernel<PG, NH><<<num_q, FT_TH_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, q8, sq, \
+                                                                     w, h_idx, d_idx, kr, topk, FT_CAP, st.tau,    \
+                                                                     st.count)
+    const int nhg = (h_idx + 15) / 16;
+    if (page_table) {
+        if (nhg == 1) KP_TH(true, 1); else if (nhg == 2) KP_TH(true, 2); else if (nhg == 3) KP_TH(true, 3);
+        else KP_TH(true, 4);
+    } else {
+        if (nhg == 1) KP_TH(false, 1); else if (nhg == 2) KP_TH(false, 2); else if (nhg == 3) KP_TH(false, 3);
+        else KP_TH(false, 4);
+    }
+#undef KP_TH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_score_emit(cu, num_docs, cu_pools, kpool, q_pos, num_q, q8, sq, w, h_idx, d_idx, k8, sk, max_pools,

@@ -203,10 +203,11 @@ def test_fused_ties(K, oracle_mod):
 
 @pytest.mark.parametrize("mode", ["too_few", "too_many"])
 def test_fused_rescoring_rows(K, oracle_mod, mode):
-    """Key scales that make every 128th pool of a row (the sampled ones) score
-    far above (too_few: fewer than k pools clear the threshold) or far below
-    (too_many: more than 16,384 clear it) the rest: those rows are selected by
-    the exact rescoring path, with the same result as the score-tensor path."""
+    """Key scales that make every 128th pool of a row (among them every pool
+    the threshold samples: every 256th at this length) score far above
+    (too_few: fewer than k pools clear the threshold) or far below (too_many:
+    more than 16,384 clear it) the rest: those rows are selected by the exact
+    rescoring path, with the same result as the score-tensor path."""
     cu = np.array([0, 1 << 17], np.int32)
     q_pos = np.array([(1 << 17) - 9, (1 << 17) - 2, 70_001, 40_000], np.int32)   # the last: 10,000 pools
     cp, k8, sk, q_idx, w = _rand_case(oracle_mod, 14, cu, q_pos)
