@@ -272,7 +272,7 @@ def main():
         d_out = torch.randn((s.Tq, s.H, s.D), generator=g, device=dev).to(torch.bfloat16)
         d_q = torch.empty_like(d_out)
         d_kv = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
-        bws = K.kp_mla_bwd_workspace_bytes(s.Tq, W)
+        bws = K.kp_mla_bwd_workspace_bytes(s.Tq, s.D, W)
         bw_ws = torch.empty(bws, dtype=torch.uint8, device=dev)
 
         def bstep():
@@ -296,7 +296,9 @@ def main():
         btf = bflop / (bmed / 1e3) / 1e12
         bwd = {"ms_median": bmed, "ms_min": float(min(bt)), "tflops": btf, "frac_bf16_peak": btf / BF16_PEAK_TFLOPS,
                "algorithmic": f"10*H*D = {10 * s.H * s.D} flop per valid slot x {wc['sum_n_valid']} slots",
-               "workspace_bytes": bws, "kernels": "mla_bwd_dq_kernel + mla_bwd_dkv_kernel (+ dKV zero fill)"}
+               "workspace_bytes": bws,
+               "kernels": "per chunk of 2048 queries: mla_bwd_dq_kernel, mla_bwd_dkv_part_kernel, a radix sort of "
+                          "the slots by row, the ordered dKV reduction (+ dKV zero fill)"}
         log(f"sparse MLA backward: {bmed:.3f} ms median, {btf:.1f} TFLOP/s ({100 * btf / BF16_PEAK_TFLOPS:.1f}% "
             f"bf16 peak)")
 

@@ -375,8 +375,9 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
                          uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
-/* Bytes of workspace sparse_mla_bwd needs for these sizes. */
-size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width);
+/* Bytes of workspace sparse_mla_bwd needs for these sizes (0 when num_q <= 0,
+ * row_width < 1 or d_latent is not 64 or 512). */
+size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t d_latent, int32_t row_width);
 
 /*
  * sparse_mla_bwd -- backward of sparse_mla_fwd: the gradients of a loss with
@@ -390,10 +391,11 @@ size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width);
  *   d_q[i,h]   = softmax_scale * sum_j ds_j kv[r_j]
  *   d_kv[r_j] += softmax_scale * ds_j q[i,h] + p_j d_out[i,h]   (key and value)
  * summed over every query, head and valid entry (repeats count each time).
- * bf16 inputs, fp32 accumulation; p and ds enter the products rounded to bf16.
- * d_kv is written in full (zeroed, then accumulated with fp32 atomic adds: its
- * value is exact to fp32 rounding, its last bits may differ between runs);
- * d_q is bit-reproducible. A row with no valid entry gives d_q = 0.
+ * bf16 inputs, fp32 accumulation; p and ds enter the products rounded to bf16,
+ * and so does each (query, entry) term of d_kv before the sum over queries.
+ * d_kv is written in full; its sum over queries runs in a fixed order (queries
+ * in chunks of 2048, within a chunk by position in the index rows), so d_q and
+ * d_kv are bit-reproducible. A row with no valid entry gives d_q = 0.
  *
  *   q, kv, indices  as passed to sparse_mla_fwd
  *   out, lse        the outputs of that sparse_mla_fwd call (lse required)
@@ -401,8 +403,11 @@ size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width);
  *   heads           1 .. 64;  d_latent 64 or 512;  row_width 1 .. 4096
  *   d_q             device bf16 [num_q, heads, d_latent]   (out)
  *   d_kv            device fp32 [num_kv, d_latent]         (out)
- *   workspace       device memory of kp_mla_bwd_workspace_bytes(num_q, row_width)
- *                   bytes, 256-byte aligned (the per-slot softmax coefficients)
+ *   workspace       device memory of kp_mla_bwd_workspace_bytes(num_q, d_latent,
+ *                   row_width) bytes, 256-byte aligned: per chunk of up to 2048
+ *                   queries, the per-slot softmax coefficients, the per-slot
+ *                   d_kv terms (bf16), the sort of the slots by row and the
+ *                   reduction's carries (about 5.9 GB at 2048 x 2176 x 512)
  */
 kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
                          const uint16_t* out, const float* lse, const uint16_t* d_out,

@@ -41,7 +41,7 @@ SIGNATURES = [
     ("indexer_topk_from_scores", _I, [_P, _I, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
     ("kp_mla_fwd_workspace_bytes", _Z, [_I, _I, _I, _I]),
     ("sparse_mla_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _P]),
-    ("kp_mla_bwd_workspace_bytes", _Z, [_I, _I]),
+    ("kp_mla_bwd_workspace_bytes", _Z, [_I, _I, _I]),
     ("sparse_mla_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _P]),
     ("kp_check_inputs", _I, [_P, _I, _I, _P, _I, _P]),
 ]
@@ -403,8 +403,8 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sof
     return out, lse
 
 
-def kp_mla_bwd_workspace_bytes(num_q: int, row_width: int) -> int:
-    return int(lib().kp_mla_bwd_workspace_bytes(num_q, row_width))
+def kp_mla_bwd_workspace_bytes(num_q: int, d_latent: int, row_width: int) -> int:
+    return int(lib().kp_mla_bwd_workspace_bytes(num_q, d_latent, row_width))
 
 
 def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, out: torch.Tensor,
@@ -423,7 +423,7 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, out
     dev = _on(("q", q), ("kv", kv), ("indices", indices), ("out", out), ("lse", lse), ("d_out", d_out),
               ("workspace", workspace))
     W = indices.shape[1]
-    need = kp_mla_bwd_workspace_bytes(Tq, W)
+    need = kp_mla_bwd_workspace_bytes(Tq, D, W)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     d_q = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)

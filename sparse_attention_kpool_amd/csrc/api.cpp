@@ -465,9 +465,9 @@ kp_status sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
     return ok();
 }
 
-size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t row_width) {
-    if (num_q <= 0 || row_width < 1) return 0;
-    return align256(kp::sparse_mla_bwd_coef_bytes(num_q, row_width));
+size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t d_latent, int32_t row_width) {
+    if (num_q <= 0 || row_width < 1 || (d_latent != 512 && d_latent != 64)) return 0;
+    return align256(kp::sparse_mla_bwd_ws_bytes(num_q, d_latent, row_width));
 }
 
 kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
@@ -491,7 +491,7 @@ kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* i
     if (num_kv > 0 && !d_kv) return fail(KP_ERR_INVALID_ARG, "d_kv is required");
     if (num_q > 0 && (!q || !kv || !indices || !out || !lse || !d_out || !d_q))
         return fail(KP_ERR_INVALID_ARG, "q, kv, indices, out, lse, d_out and d_q are required");
-    const size_t need = kp_mla_bwd_workspace_bytes(num_q, row_width);
+    const size_t need = kp_mla_bwd_workspace_bytes(num_q, d_latent, row_width);
     if (num_q > 0 && (!workspace || workspace_bytes < need))
         return fail(KP_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (((uintptr_t)workspace & 255) != 0) return fail(KP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");

@@ -86,12 +86,12 @@ size_t sparse_mla_part_bytes(int num_q, int heads, int d_latent, int row_width);
 // Largest index row sparse_mla_fwd accepts for this key width.
 int sparse_mla_max_row_width(int d_latent);
 
-// Backward of the sparse latent attention: dq (bf16) and dkv (fp32, zeroed, then
-// accumulated); workspace of sparse_mla_bwd_coef_bytes bytes.
+// Backward of the sparse latent attention: dq (bf16) and dkv (fp32, written in
+// full, bit-reproducible); workspace of sparse_mla_bwd_ws_bytes bytes.
 hipError_t launch_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const uint16_t* out,
                                  const float* lse, const uint16_t* d_out, int num_q, int num_kv, int heads,
                                  int d_latent, int row_width, float scale, uint16_t* d_q, float* d_kv,
                                  void* workspace, hipStream_t stream);
-size_t sparse_mla_bwd_coef_bytes(int num_q, int row_width);
+size_t sparse_mla_bwd_ws_bytes(int num_q, int d_latent, int row_width);
 
 }  // namespace kp
