@@ -10,9 +10,10 @@ namespace kp {
 // -0 is folded onto +0 and NaN sorts below -inf (key 0).
 __device__ __forceinline__ uint32_t score_key(float f) {
     uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;                       // -0 == +0
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0u;  // NaN: lowest
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    u = u == 0x80000000u ? 0u : u;                                      // -0 == +0
+    // negative: all bits flipped; otherwise the sign bit set
+    const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : k;                    // NaN: lowest
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):

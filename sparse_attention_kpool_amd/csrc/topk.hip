@@ -228,6 +228,330 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     if (tid == 0 && num_valid) num_valid[i] = base + n_tail;
 }
 
+// ------------------------------------------------------- one wave per row ----
+// When no row has more than TW_KEYS visible pools, each row gets one wave that
+// holds the row's keys in registers (lane l: pools 64*r + l, r < TW_R). The
+// same radix select then runs with no barrier: the histogram is the wave's own
+// LDS array (lane l owns the 32 or 16 bins below nb - per*l, which it reads to
+// pick the digit and clears for the next one), and the ordered final pass is a
+// ballot over each register's 64 pools: a pool's rank among the kept ones is
+// the count kept in earlier registers plus the kept lanes below it. Registers
+// are visited in chunks of TW_C, one scalar test per chunk.
+constexpr int TW_KEYS = 8192, TW_R = TW_KEYS / 64, TW_WAVES = 4, TW_C = 16;
+
+// BODY runs for r = 0 .. TW_C*nch - 1 (r a compile-time constant in it). nch
+// passes through an empty asm first, so the compiler recomputes the scalar
+// chunk tests in each loop instead of keeping them live across the kernel.
+#define TW_FOR_REGS(nch, BODY)                                                   \
+    {                                                                            \
+        int nc_ = (nch);                                                         \
+        __asm__ volatile("" : "+s"(nc_));                                        \
+        _Pragma("unroll") for (int c_ = 0; c_ < R / TW_C; ++c_) {                \
+            if (c_ < nc_) {                                                      \
+                _Pragma("unroll") for (int u_ = 0; u_ < TW_C; ++u_) {            \
+                    const int r = TW_C * c_ + u_;                                \
+                    BODY                                                         \
+                }                                                                \
+            }                                                                    \
+        }                                                                        \
+    }
+
+// R key registers per lane: this instance takes the rows with 64*(R/2) < n <=
+// 64*R visible pools (R == 64: also every shorter row), so that short rows run
+// with fewer registers and more waves per SIMD.
+template <bool KP4, int R>
+__global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kernel(
+    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
+    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid, int num_q) {
+    static_assert(R % TW_C == 0 && R <= TW_R, "register count");
+    // per wave: TK_BINS bins, then one spare word per lane that takes the counts
+    // and writes of lanes with nothing to count or keep (no branch around them)
+    __shared__ __align__(16) int hist_all[TW_WAVES][TK_BINS + 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = __builtin_amdgcn_readfirstlane(blockIdx.x * TW_WAVES + wave);
+    if (i >= num_q) return;
+    if (KP4) kpool = 4;
+    int* hist = hist_all[wave];
+    const int t = q_pos ? q_pos[i] : i;
+    const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
+    const int n = __builtin_amdgcn_readfirstlane(qp.n_vis);
+    if (n > 64 * R || (R > 64 && n <= 32 * R)) return;   // the other instance's row
+    const int k = n < topk ? n : topk;
+    const int doc_start = cu[qp.doc];
+    int32_t* row = indices + (size_t)i * row_width;
+    const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
+    const uint64_t below = (1ull << lane) - 1ull;
+    auto put = [&](int pos, int j) __attribute__((always_inline)) {
+        const int tok = doc_start + kpool * j;
+        if (KP4) {   // the four tokens of the pool as one 16-byte store
+            *reinterpret_cast<int4*>(row + 4 * pos) = make_int4(tok, tok + 1, tok + 2, tok + 3);
+        } else {
+            for (int q = 0; q < kpool; ++q) row[pos * kpool + q] = tok + q;
+        }
+    };
+
+    if (k >= n) {
+        // every visible pool is kept, in order
+        for (int j = lane; j < n; j += 64) put(j, j);
+    } else if (k > 0) {
+        const int nch = (n + 64 * TW_C - 1) / (64 * TW_C);   // chunks of registers in use
+        const int n_pad = 64 * TW_C * nch - n;               // their lanes past the row's end
+        uint32_t key[R];
+        // the sample (below) is loaded first, then the row: a buffer of n scores, so
+        // lanes past its end read 0
+        const float sample = srow[(lane * n) >> 6];
+        const __amdgpu_buffer_rsrc_t srsc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, 4 * n, 0x00020000);
+        TW_FOR_REGS(nch, key[r] = __builtin_amdgcn_raw_buffer_load_b32(srsc, 4 * lane + 256 * r, 0, 0);)
+        // A lower bound lo (in key space) from 64 pools sampled along the row: the
+        // largest sample with at least t samples above it, t about twice the expected
+        // 64 k / n plus 4, so that the k-th largest key lies above lo but for rare
+        // rows. Only keys at or above lo enter the histograms; a row where fewer than
+        // k do is selected again over every key (lo = 0: the plain radix select).
+        uint32_t lo = 0u;
+        if (n >= 2048) {
+            const uint32_t sk = score_key(sample);
+            int gt = 0;
+#pragma unroll
+            for (int m = 0; m < 64; ++m) gt += (uint32_t)__builtin_amdgcn_readlane((int)sk, m) > sk;
+            const int t = min(63, (128 * k + n - 1) / n + 4);
+            uint32_t cand = gt >= t ? sk : 0u;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) cand = max(cand, (uint32_t)__shfl_xor((int)cand, m, 64));
+            lo = __builtin_amdgcn_readfirstlane(cand);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) *reinterpret_cast<int4*>(hist + 32 * lane + 4 * q) = make_int4(0, 0, 0, 0);
+
+        int remaining = k;
+        uint32_t prefix = 0u, pmask = 0u;
+        bool pad_bin0 = false;   // the padding lanes (key 0) are counted in bin 0
+        // the digit of bits [shift, shift + width) of the counted offsets from the
+        // counts in hist: the bin holding the remaining-th largest key. Returns 1 when
+        // that whole bin is kept, 0 when not, -1 when fewer than `remaining` keys were
+        // counted (then nothing has changed but the histogram, which is cleared).
+        auto pick = [&](int shift, int width) __attribute__((always_inline)) -> int {
+            const int nb = 1 << width;
+            // a wave's LDS operations complete in order
+            if (lane == 0 && pad_bin0 && prefix == 0u && n_pad > 0) hist[0] -= n_pad;
+            // lane l owns bins [nb - per*(l+1), nb - per*l): a scan over lanes counts
+            // the keys in the bins above each lane's
+            const int per = nb >> 6;    // 1 .. 32
+            const int base = nb - per * (lane + 1);
+            int own = 0;
+            if (per >= 4) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (4 * q < per) {
+                        const int4 v = *reinterpret_cast<const int4*>(hist + base + 4 * q);
+                        own += (v.x + v.y) + (v.z + v.w);
+                    }
+            } else {
+                own = hist[base] + (per == 2 ? hist[base + 1] : 0);
+            }
+            const int incl = wave_incl_scan(own);
+            const bool enough = __builtin_amdgcn_readlane(incl, 63) >= remaining;
+            int res = -1;
+            if (enough) {
+                // the lane whose bins hold the remaining-th largest key; then one of its
+                // bins per lane (lane m: the m-th from the top) and a scan over them
+                const int before = incl - own;
+                const int src = __builtin_ctzll(__ballot(before < remaining && incl >= remaining));
+                const int acc0 = __builtin_amdgcn_readlane(before, src);
+                const int top_bin = nb - 1 - per * src;
+                const int c = lane < per ? hist[top_bin - lane] : 0;
+                const int ci = wave_incl_scan(c);
+                const int m = __builtin_ctzll(__ballot(lane < per && acc0 + ci - c < remaining && acc0 + ci >= remaining));
+                const int sel_digit = top_bin - m;
+                const int sel_above = acc0 + __builtin_amdgcn_readlane(ci - c, m);
+                const int sel_cnt = __builtin_amdgcn_readlane(c, m);
+                remaining -= sel_above;
+                prefix |= (uint32_t)sel_digit << shift;
+                pmask |= (uint32_t)(nb - 1) << shift;
+                res = sel_cnt == remaining ? 1 : 0;
+            }
+            // clear the bins for the next digit (after the reads above)
+            if (per >= 4) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (4 * q < per) *reinterpret_cast<int4*>(hist + base + 4 * q) = make_int4(0, 0, 0, 0);
+            } else {
+                hist[base] = 0;
+                if (per == 2) hist[base + 1] = 0;
+            }
+            return res;
+        };
+        // count one for lane's value in bin b when `in` (else in the lane's spare word)
+        int* const spare = hist + TK_BINS + lane;
+        auto count = [&](bool in, uint32_t b) __attribute__((always_inline)) {
+            atomicAdd(in ? hist + b : spare, 1);
+        };
+        bool whole = false;
+        uint32_t thr, top;   // the threshold and the largest counted value, in the keys' units
+
+        // Positive bound: every kept pool has a positive score, and the raw bits of
+        // positive floats order as the scores do, so the keys stay raw. A raw value
+        // v is counted when lo_raw <= v <= +inf (0x7F800000), one unsigned test that
+        // also drops negative scores (sign bit set) and NaN; the digits are cut from
+        // the span [lo_raw, largest counted value] as in the general path below.
+        bool fast = lo > 0x80000000u;
+        if (fast) {
+            const uint32_t lo_raw = lo & 0x7FFFFFFFu, lim0 = 0x7F800000u - lo_raw;
+            uint32_t omax = 0u;   // largest counted offset v - lo_raw
+            TW_FOR_REGS(nch, {
+                const uint32_t o = key[r] - lo_raw;
+                omax = max(omax, o <= lim0 ? o : 0u);
+            })
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) omax = max(omax, (uint32_t)__shfl_xor((int)omax, m, 64));
+            omax = __builtin_amdgcn_readfirstlane(omax);
+            const int B = omax == 0u ? 0 : 32 - __builtin_clz(omax);
+            const int P = (B + 10) / 11;
+            const int W = P > 0 ? (B + P - 1) / P : 0;
+            // P == 0: every counted value equals lo_raw (handled by the final pass)
+            if (P > 0) {
+                const int w0 = P == 1 ? max(B, 6) : W;
+                const int s0 = P == 1 ? 0 : B - W;
+                TW_FOR_REGS(nch, {
+                    const uint32_t o = key[r] - lo_raw;
+                    count(o <= lim0, o >> s0);
+                })
+                const int res = pick(s0, w0);
+                if (res < 0) {
+                    fast = false;
+                    lo = 0u;
+                } else {
+                    whole = res > 0;
+#pragma unroll 1
+                    for (int pass = 1; pass < P && !whole; ++pass) {
+                        const int shift = pass == P - 1 ? 0 : B - W * (pass + 1);
+                        const int width = pass == P - 1 ? B - W * (P - 1) : W;
+                        const uint32_t kb0 = lo_raw + prefix, lim = 1u << (shift + width);
+                        TW_FOR_REGS(nch, {
+                            const uint32_t o = key[r] - kb0;
+                            count(o < lim, o >> shift);
+                        })
+                        whole = pick(shift, width) > 0;
+                    }
+                }
+            } else {
+                // nothing above lo_raw: the count of values equal to lo_raw decides
+                int cnt = 0;
+                TW_FOR_REGS(nch, cnt += __popcll(__ballot(key[r] == lo_raw));)
+                if (cnt < k) {
+                    fast = false;
+                    lo = 0u;
+                }
+            }
+            if (fast) {
+                thr = lo_raw + prefix;
+                top = 0x7F800000u;
+            }
+        }
+        if (!fast) {
+            // order-preserving keys; lanes past the row's end get key 0
+            TW_FOR_REGS(nch, key[r] = 64 * r + lane < n ? score_key(__uint_as_float(key[r])) : 0u;)
+            uint32_t kmax = 0u;
+            TW_FOR_REGS(nch, kmax = max(kmax, key[r]);)
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
+            kmax = __builtin_amdgcn_readfirstlane(kmax);
+#pragma unroll 1
+            for (int attempt = 0; attempt < 2; ++attempt) {
+                pad_bin0 = lo == 0u;
+                // the span's significant bits are cut into 1 to 3 digits of 6 to 11 bits
+                const uint32_t span = kmax - lo;
+                const int B = span == 0u ? 0 : 32 - __builtin_clz(span);
+                const int P = (B + 10) / 11;
+                const int W = P > 0 ? (B + P - 1) / P : 0;
+                if (P == 0) break;   // every key at or above lo is equal: ties in pool order
+                // first digit: every key at or above lo
+                const int w0 = P == 1 ? max(B, 6) : W;
+                const int s0 = P == 1 ? 0 : B - W;
+                TW_FOR_REGS(nch, count(key[r] >= lo, (key[r] - lo) >> s0);)
+                const int res = pick(s0, w0);
+                if (res < 0) {   // lo was above the k-th largest key: all keys
+                    lo = 0u;
+                    continue;
+                }
+                whole = res > 0;
+                // later digits: the keys matching the digits so far, lo + prefix <= key <
+                // lo + prefix + 2^(shift + width) (a bound that changes every pass, so no
+                // test is hoisted)
+#pragma unroll 1
+                for (int pass = 1; pass < P && !whole; ++pass) {
+                    const int shift = pass == P - 1 ? 0 : B - W * (pass + 1);
+                    const int width = pass == P - 1 ? B - W * (P - 1) : W;
+                    const uint32_t kb0 = lo + prefix, lim = 1u << (shift + width);
+                    TW_FOR_REGS(nch, count(key[r] - kb0 < lim, (key[r] - kb0) >> shift);)
+                    whole = pick(shift, width) > 0;
+                }
+                break;
+            }
+            thr = lo + prefix;
+            top = 0xFFFFFFFFu;
+        }
+
+        // Ordered final pass: with a whole bin kept, every value v with thr <= v <=
+        // top (thr is above 0: fewer than n pools are kept); otherwise those above thr
+        // and the first `remaining` equal to it. The padding lanes (0, after every
+        // pool of the row) are never kept: 0 is below thr, and at least `remaining`
+        // pools of the row equal thr before them.
+        const uint32_t lge = top - thr;
+        const bool has_gt = thr < top;
+        const uint32_t agt = thr + 1u, lgt = top - thr - 1u;
+        int pos = 0;
+        auto mbcnt = [&](uint64_t m, int add) __attribute__((always_inline)) {
+            return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, add));
+        };
+        // pools of 4 tokens and k <= TK_BINS: the kept pools' numbers go to the wave's
+        // histogram array at their ranks, and the index row is written from there
+        // with contiguous 16-byte stores; otherwise each kept pool is stored directly
+        const bool via_lds = KP4 && k <= TK_BINS;
+#define TW_FINAL(EMIT)                                                                                    \
+    if (whole) {                                                                                          \
+        TW_FOR_REGS(nch, {                                                                                \
+            const bool keep = key[r] - thr <= lge;                                                        \
+            const uint64_t kb = __ballot(keep);                                                           \
+            EMIT(keep, mbcnt(kb, pos), r);                                                                \
+            pos += __popcll(kb);                                                                          \
+        })                                                                                                \
+    } else {                                                                                              \
+        int eq_seen = 0;                                                                                  \
+        TW_FOR_REGS(nch, {                                                                                \
+            const bool eq = key[r] == thr;                                                                \
+            const uint64_t eb = __ballot(eq);                                                             \
+            const bool keep = (has_gt & (key[r] - agt <= lgt)) | (eq & (mbcnt(eb, eq_seen) < remaining)); \
+            eq_seen += __popcll(eb);                                                                      \
+            const uint64_t kb = __ballot(keep);                                                           \
+            EMIT(keep, mbcnt(kb, pos), r);                                                                \
+            pos += __popcll(kb);                                                                          \
+        })                                                                                                \
+    }
+#define TW_EMIT_LDS(keep, p, r) (*((keep) ? hist + (p) : spare) = 64 * (r) + lane)
+#define TW_EMIT_PUT(keep, p, r) \
+    if (keep) put((p), 64 * (r) + lane)
+        if (via_lds) {
+            TW_FINAL(TW_EMIT_LDS)
+        } else {
+            TW_FINAL(TW_EMIT_PUT)
+        }
+#undef TW_FINAL
+#undef TW_EMIT_LDS
+#undef TW_EMIT_PUT
+        if (via_lds) {
+            for (int q = lane; q < k; q += 64) put(q, hist[q]);
+        }
+    }
+    // own incomplete pool, then padding
+    const int base = k * kpool;
+    const int n_tail = t - qp.tail_start + 1;
+    for (int r = lane; r < row_width - base; r += 64) row[base + r] = r < n_tail ? qp.tail_start + r : -1;
+    if (lane == 0 && num_valid) num_valid[i] = base + n_tail;
+}
+#undef TW_FOR_REGS
+
 // ------------------------------------------------------------- long rows ----
 // Rows with more visible pools than the LDS key cache (decode over a long
 // context) go to the many-workgroup kernels below when their index rows have
@@ -694,6 +1018,23 @@ hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools,
     const int chunks = (max_pools + TM_CHUNK - 1) / TM_CHUNK;
     const bool many = has_long && (long long)kpool * topk >= TK_BINS &&
                       (long long)row_width >= (long long)kpool * topk + kpool + TM_STATE + 2 * chunks;
+    if (!has_long) {
+        // rows of up to 4096 pools with 64 key registers per lane, longer ones with 128
+        const int g = (num_q + TW_WAVES - 1) / TW_WAVES;
+#define KP_TW(KP4, R)                                                                                          \
+    topk_wave_kernel<KP4, R><<<g, 64 * TW_WAVES, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores,    \
+                                                              max_pools, topk, row_width, indices, num_valid, \
+                                                              num_q)
+        if (kpool == 4) {
+            KP_TW(true, 64);
+            if (max_pools > 4096) KP_TW(true, 128);
+        } else {
+            KP_TW(false, 64);
+            if (max_pools > 4096) KP_TW(false, 128);
+        }
+#undef KP_TW
+        return hipGetLastError();
+    }
     topk_kernel<<<num_q, TK_THREADS, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores, max_pools,
                                                   topk, row_width, indices, num_valid,
                                                   !has_long ? 0 : (many ? 2 : 1));

@@ -197,7 +197,8 @@ def test_scores_fed_oracle_keys(K, oracle_mod, name):
 # ------------------------------------------------------------------ top-k -----
 @pytest.mark.parametrize("case", ["tiny", "2k", "packed4k", "ties", "zeros", "negzero", "nan", "topk0",
                                   "decode1m_rows", "long_rand", "long_ties", "long_zeros", "long_nan",
-                                  "long_bigk", "long_smallk"])
+                                  "long_bigk", "long_smallk", "mid_rand", "mid_ties", "mid_nan",
+                                  "mid_sampled_top"])
 def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
     rng = np.random.default_rng(7)
     if case in ("tiny", "2k", "packed4k"):
@@ -239,6 +240,30 @@ def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
         # (a small k leaves the rows no room for the many-workgroup scratch: the
         # one-workgroup long-row kernel runs instead)
         topk = 5000 if case == "long_bigk" else (37 if case == "long_smallk" else 512)
+    elif case.startswith("mid_"):
+        # rows of up to 8192 pools (the one-wave-per-row kernels: rows of 2048 or
+        # more pools first bound the histogrammed keys from 64 sampled pools)
+        T = 32768
+        cu = np.array([0, T], np.int32)
+        cp, _ = oracle_mod.layout(cu, T, 4)
+        qpos = np.array([5, 4000, 8191, 8195, 9000, 12000, 16383, 16387, 16390, 20000, 24575, 28000, 30001,
+                         32766, 32767], np.int32)
+        sc = rng.standard_normal((len(qpos), T // 4)).astype(np.float32)
+        if case == "mid_ties":
+            sc = np.round(sc * 2).astype(np.float32)
+        if case == "mid_nan":
+            sc[rng.random(sc.shape) < 0.01] = np.nan
+            sc[rng.random(sc.shape) < 0.01] = -np.inf
+            sc[rng.random(sc.shape) < 0.2] = -0.0
+        if case == "mid_sampled_top":
+            # the 64 sampled pools of each row hold its largest scores: fewer than
+            # top-k pools lie above the sampled bound, so the row is selected again
+            # over every key
+            for r, t in enumerate(qpos):
+                n = (int(t) + 1) // 4
+                if n >= 64:
+                    sc[r, (np.arange(64) * n) >> 6] = 100.0 + np.arange(64)
+        topk = 512
     else:
         T = 5000
         cu = np.array([0, 700, 700, 2900, 2903, 5000], np.int32)
