@@ -230,13 +230,19 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
 
 // ------------------------------------------------------- one wave per row ----
 // When no row has more than TW_KEYS visible pools, each row gets one wave that
-// holds the row's keys in registers (lane l: pools 64*r + l, r < TW_R). The
-// same radix select then runs with no barrier: the histogram is the wave's own
-// LDS array (lane l owns the 32 or 16 bins below nb - per*l, which it reads to
-// pick the digit and clears for the next one), and the ordered final pass is a
-// ballot over each register's 64 pools: a pool's rank among the kept ones is
-// the count kept in earlier registers plus the kept lanes below it. Registers
-// are visited in chunks of TW_C, one scalar test per chunk.
+// holds the row's keys in registers. The same radix select then runs with no
+// barrier: the histogram is the wave's own LDS array (lane l owns the bins
+// below nb - per*l, which it reads to pick the digit and clears for the next
+// one), counting is branchless, and the ordered final pass ranks the kept pools
+// with ballots or a scan over lanes. Registers are visited in chunks of TW_C,
+// one scalar test per chunk.
+//
+// Slots: the row is read from `base`, its first score or (with 16-byte loads)
+// the 16-byte boundary at or below it, a = 0..3 slots earlier; slot s holds pool
+// s - a. With 16-byte loads (vec4: the score rows' stride is a multiple of four
+// and the buffer is 16-byte aligned, so a row's 16-byte chunks lie in its own
+// row) register 4g + c of lane l holds slot 256g + 4l + c; otherwise register r
+// holds slot 64r + l.
 constexpr int TW_KEYS = 8192, TW_R = TW_KEYS / 64, TW_WAVES = 4, TW_C = 16;
 
 // BODY runs for r = 0 .. TW_C*nch - 1 (r a compile-time constant in it). nch
@@ -255,19 +261,57 @@ constexpr int TW_KEYS = 8192, TW_R = TW_KEYS / 64, TW_WAVES = 4, TW_C = 16;
             }                                                                    \
         }                                                                        \
     }
+// the same over groups g of four registers (4g .. 4g+3)
+#define TW_FOR_GROUPS(nch, BODY)                                                 \
+    {                                                                            \
+        int nc_ = (nch);                                                         \
+        __asm__ volatile("" : "+s"(nc_));                                        \
+        _Pragma("unroll") for (int c_ = 0; c_ < R / TW_C; ++c_) {                \
+            if (c_ < nc_) {                                                      \
+                _Pragma("unroll") for (int u_ = 0; u_ < TW_C / 4; ++u_) {        \
+                    const int g = TW_C / 4 * c_ + u_;                            \
+                    BODY                                                         \
+                }                                                                \
+            }                                                                    \
+        }                                                                        \
+    }
 
-// R key registers per lane: this instance takes the rows with 64*(R/2) < n <=
-// 64*R visible pools (R == 64: also every shorter row), so that short rows run
-// with fewer registers and more waves per SIMD.
-template <bool KP4, int R>
-__global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kernel(
+// add + the lanes below this one set in each of the four masks
+__device__ __forceinline__ int tw_mbcnt4(uint64_t b0, uint64_t b1, uint64_t b2, uint64_t b3, int add) {
+    uint32_t x = __builtin_amdgcn_mbcnt_lo((uint32_t)b0, (uint32_t)add);
+    x = __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), x);
+    x = __builtin_amdgcn_mbcnt_lo((uint32_t)b1, x);
+    x = __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), x);
+    x = __builtin_amdgcn_mbcnt_lo((uint32_t)b2, x);
+    x = __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), x);
+    x = __builtin_amdgcn_mbcnt_lo((uint32_t)b3, x);
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b3 >> 32), x);
+}
+
+// One compare-exchange step of a bitonic sort of one value per lane: the partner
+// is lane ^ J; in blocks of KK lanes with (lane & KK) == 0 the lower lane keeps
+// the larger value (descending), in the others the smaller.
+#define TW_BITONIC_STEP(KK, J)                                                                   \
+    {                                                                                            \
+        const uint32_t p_ = __float_as_uint(lane_xor<J>(__uint_as_float(v)));                   \
+        const bool desc_ = (lane & (KK)) == 0 || (KK) == 64, low_ = (lane & (J)) == 0;           \
+        v = desc_ == low_ ? max(v, p_) : min(v, p_);                                             \
+    }
+
+// R key registers per lane: this instance takes the rows of 64*RLO < S <= 64*R
+// slots, so that shorter rows run with fewer registers and more waves per SIMD.
+template <bool KP4, int R, int RLO>
+__global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 5) void topk_wave_kernel(
     const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools, int kpool,
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int max_pools, int topk,
-    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid, int num_q) {
+    int row_width, int32_t* __restrict__ indices, int32_t* __restrict__ num_valid, int num_q, int vec4) {
     static_assert(R % TW_C == 0 && R <= TW_R, "register count");
-    // per wave: TK_BINS bins, then one spare word per lane that takes the counts
-    // and writes of lanes with nothing to count or keep (no branch around them)
-    __shared__ __align__(16) int hist_all[TW_WAVES][TK_BINS + 64];
+    // digits of at most MAXW bits: 2048 bins for the long rows, 1024 for the short
+    // ones (a smaller LDS share per wave, so that more waves fit per SIMD)
+    constexpr int NB = R > 64 ? 2048 : 1024, MAXW = R > 64 ? 11 : 10;
+    // per wave: NB bins, then one spare word per lane that takes the counts and
+    // writes of lanes with nothing to count or keep (no branch around them)
+    __shared__ __align__(16) int hist_all[TW_WAVES][NB + 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = __builtin_amdgcn_readfirstlane(blockIdx.x * TW_WAVES + wave);
     if (i >= num_q) return;
@@ -276,11 +320,13 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
     const int t = q_pos ? q_pos[i] : i;
     const QueryPools qp = query_pools(cu, num_docs, cu_pools, kpool, t);
     const int n = __builtin_amdgcn_readfirstlane(qp.n_vis);
-    if (n > 64 * R || (R > 64 && n <= 32 * R)) return;   // the other instance's row
+    const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
+    const int a = vec4 ? (int)(((uintptr_t)srow >> 2) & 3) : 0;   // slots before the row's first pool
+    const int S = n + a;                                            // slots up to the row's last pool
+    if (S > 64 * R || (RLO > 0 && S <= 64 * RLO)) return;          // another instance's row
     const int k = n < topk ? n : topk;
     const int doc_start = cu[qp.doc];
     int32_t* row = indices + (size_t)i * row_width;
-    const float* srow = scores + (size_t)i * max_pools + qp.pool_lo;
     const uint64_t below = (1ull << lane) - 1ull;
     auto put = [&](int pos, int j) __attribute__((always_inline)) {
         const int tok = doc_start + kpool * j;
@@ -290,43 +336,77 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
             for (int q = 0; q < kpool; ++q) row[pos * kpool + q] = tok + q;
         }
     };
+    // the slot of register r in this lane
+    auto slot_of = [&](int r) __attribute__((always_inline)) {
+        return vec4 ? 256 * (r >> 2) + 4 * lane + (r & 3) : 64 * r + lane;
+    };
 
     if (k >= n) {
         // every visible pool is kept, in order
         for (int j = lane; j < n; j += 64) put(j, j);
     } else if (k > 0) {
-        const int nch = (n + 64 * TW_C - 1) / (64 * TW_C);   // chunks of registers in use
-        const int n_pad = 64 * TW_C * nch - n;               // their lanes past the row's end
+        const int nch = (S + 64 * TW_C - 1) / (64 * TW_C);   // chunks of registers in use
+        const int n_pad = 64 * TW_C * nch - n;               // their slots outside the row
         uint32_t key[R];
-        // the sample (below) is loaded first, then the row: a buffer of n scores, so
-        // lanes past its end read 0
+        // the sample (below) is loaded first, then the row: a buffer that ends with
+        // the row (with 16-byte loads: with the 16-byte chunk holding its last pool),
+        // so slots past its end read 0
         const float sample = srow[(lane * n) >> 6];
-        const __amdgpu_buffer_rsrc_t srsc =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, 4 * n, 0x00020000);
-        TW_FOR_REGS(nch, key[r] = __builtin_amdgcn_raw_buffer_load_b32(srsc, 4 * lane + 256 * r, 0, 0);)
+        const __amdgpu_buffer_rsrc_t srsc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(srow - a), 0, vec4 ? 4 * ((S + 3) & ~3) : 4 * n, 0x00020000);
+        if (vec4) {
+            typedef int v4i __attribute__((ext_vector_type(4)));
+            TW_FOR_GROUPS(nch, {
+                const v4i v = __builtin_amdgcn_raw_buffer_load_b128(srsc, 16 * lane + 1024 * g, 0, 0);
+                key[4 * g] = v.x; key[4 * g + 1] = v.y; key[4 * g + 2] = v.z; key[4 * g + 3] = v.w;
+            })
+            // slots of the first and last 16-byte chunks outside the row: 0
+            if (lane == 0) {
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    if (c < a) key[c] = 0u;
+            }
+            const int gl = (S - 1) >> 8, ll = ((S - 1) >> 2) & 63, cl = (S - 1) & 3;
+            TW_FOR_GROUPS(nch, {
+                if (g == gl && lane == ll) {
+                    if (cl < 1) key[4 * g + 1] = 0u;
+                    if (cl < 2) key[4 * g + 2] = 0u;
+                    if (cl < 3) key[4 * g + 3] = 0u;
+                }
+            })
+        } else {
+            TW_FOR_REGS(nch, key[r] = __builtin_amdgcn_raw_buffer_load_b32(srsc, 4 * lane + 256 * r, 0, 0);)
+        }
         // A lower bound lo (in key space) from 64 pools sampled along the row: the
-        // largest sample with at least t samples above it, t about twice the expected
-        // 64 k / n plus 4, so that the k-th largest key lies above lo but for rare
-        // rows. Only keys at or above lo enter the histograms; a row where fewer than
-        // k do is selected again over every key (lo = 0: the plain radix select).
-        uint32_t lo = 0u;
+        // sample of rank t from the top (t samples at least as large before it), t
+        // about twice the expected 64 k / n plus 4, so that the k-th largest key lies
+        // above lo but for rare rows. Only keys at or above lo enter the histograms;
+        // a row where fewer than k do is selected again over every key (lo = 0: the
+        // plain radix select).
+        uint32_t lo = 0u, smax = 0u;   // smax: the largest sample
         if (n >= 2048) {
-            const uint32_t sk = score_key(sample);
-            int gt = 0;
-#pragma unroll
-            for (int m = 0; m < 64; ++m) gt += (uint32_t)__builtin_amdgcn_readlane((int)sk, m) > sk;
-            const int t = min(63, (128 * k + n - 1) / n + 4);
-            uint32_t cand = gt >= t ? sk : 0u;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) cand = max(cand, (uint32_t)__shfl_xor((int)cand, m, 64));
-            lo = __builtin_amdgcn_readfirstlane(cand);
+            // the samples' keys sorted across the wave, largest in lane 0 (bitonic:
+            // blocks of kk lanes, even blocks descending, merged at distance j)
+            uint32_t v = score_key(sample);
+            TW_BITONIC_STEP(2, 1)
+            TW_BITONIC_STEP(4, 2) TW_BITONIC_STEP(4, 1)
+            TW_BITONIC_STEP(8, 4) TW_BITONIC_STEP(8, 2) TW_BITONIC_STEP(8, 1)
+            TW_BITONIC_STEP(16, 8) TW_BITONIC_STEP(16, 4) TW_BITONIC_STEP(16, 2) TW_BITONIC_STEP(16, 1)
+            TW_BITONIC_STEP(32, 16) TW_BITONIC_STEP(32, 8) TW_BITONIC_STEP(32, 4) TW_BITONIC_STEP(32, 2)
+            TW_BITONIC_STEP(32, 1)
+            TW_BITONIC_STEP(64, 32) TW_BITONIC_STEP(64, 16) TW_BITONIC_STEP(64, 8) TW_BITONIC_STEP(64, 4)
+            TW_BITONIC_STEP(64, 2) TW_BITONIC_STEP(64, 1)
+            const int tr = min(63, (128 * k + n - 1) / n + 4);
+            lo = (uint32_t)__builtin_amdgcn_readlane((int)v, tr);
+            smax = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) *reinterpret_cast<int4*>(hist + 32 * lane + 4 * q) = make_int4(0, 0, 0, 0);
+        for (int q = 0; q < NB / 256; ++q)
+            *reinterpret_cast<int4*>(hist + (NB / 64) * lane + 4 * q) = make_int4(0, 0, 0, 0);
 
         int remaining = k;
         uint32_t prefix = 0u, pmask = 0u;
-        bool pad_bin0 = false;   // the padding lanes (key 0) are counted in bin 0
+        bool pad_bin0 = false;   // the slots outside the row (key 0) are counted in bin 0
         // the digit of bits [shift, shift + width) of the counted offsets from the
         // counts in hist: the bin holding the remaining-th largest key. Returns 1 when
         // that whole bin is kept, 0 when not, -1 when fewer than `remaining` keys were
@@ -335,19 +415,20 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
             const int nb = 1 << width;
             // a wave's LDS operations complete in order
             if (lane == 0 && pad_bin0 && prefix == 0u && n_pad > 0) hist[0] -= n_pad;
-            // lane l owns bins [nb - per*(l+1), nb - per*l): a scan over lanes counts
-            // the keys in the bins above each lane's
-            const int per = nb >> 6;    // 1 .. 32
+            // lane l owns bins [nb - per*(l+1), nb - per*l) (with fewer than 64 bins,
+            // lanes l < nb own one each): a scan over lanes counts the keys in the bins
+            // above each lane's
+            const int per = nb >= 64 ? nb >> 6 : 1;   // 1 .. NB / 64
             const int base = nb - per * (lane + 1);
             int own = 0;
             if (per >= 4) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
+                for (int q = 0; q < NB / 256; ++q)
                     if (4 * q < per) {
                         const int4 v = *reinterpret_cast<const int4*>(hist + base + 4 * q);
                         own += (v.x + v.y) + (v.z + v.w);
                     }
-            } else {
+            } else if (base >= 0) {
                 own = hist[base] + (per == 2 ? hist[base + 1] : 0);
             }
             const int incl = wave_incl_scan(own);
@@ -374,16 +455,16 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
             // clear the bins for the next digit (after the reads above)
             if (per >= 4) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
+                for (int q = 0; q < NB / 256; ++q)
                     if (4 * q < per) *reinterpret_cast<int4*>(hist + base + 4 * q) = make_int4(0, 0, 0, 0);
-            } else {
+            } else if (base >= 0) {
                 hist[base] = 0;
                 if (per == 2) hist[base + 1] = 0;
             }
             return res;
         };
         // count one for lane's value in bin b when `in` (else in the lane's spare word)
-        int* const spare = hist + TK_BINS + lane;
+        int* const spare = hist + NB + lane;
         auto count = [&](bool in, uint32_t b) __attribute__((always_inline)) {
             atomicAdd(in ? hist + b : spare, 1);
         };
@@ -391,51 +472,71 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
         uint32_t thr, top;   // the threshold and the largest counted value, in the keys' units
 
         // Positive bound: every kept pool has a positive score, and the raw bits of
-        // positive floats order as the scores do, so the keys stay raw. A raw value
-        // v is counted when lo_raw <= v <= +inf (0x7F800000), one unsigned test that
-        // also drops negative scores (sign bit set) and NaN; the digits are cut from
-        // the span [lo_raw, largest counted value] as in the general path below.
+        // positive floats order as the scores do, so the keys stay raw (slots outside
+        // the row hold +0, never counted). A raw value v is counted when lo_raw <= v
+        // <= +inf (0x7F800000), one unsigned test that also drops negative scores
+        // (sign bit set) and NaN; the digits are cut from the span [lo_raw, largest
+        // counted value] as in the general path below.
         bool fast = lo > 0x80000000u;
         if (fast) {
             const uint32_t lo_raw = lo & 0x7FFFFFFFu, lim0 = 0x7F800000u - lo_raw;
-            uint32_t omax = 0u;   // largest counted offset v - lo_raw
-            TW_FOR_REGS(nch, {
-                const uint32_t o = key[r] - lo_raw;
-                omax = max(omax, o <= lim0 ? o : 0u);
-            })
+            // the first digit's span from the largest sample (values above it are
+            // counted in the top bin); should the k-th largest value fall in that top
+            // bin, the row is counted again with the span from its largest value
+            int B = 32 - __builtin_clz(((smax & 0x7FFFFFFFu) - lo_raw) | 1u);
+            bool est = smax > lo;
+#pragma unroll 1
+            for (int tries = 0; tries < 2; ++tries) {
+                // (the bound passes through an empty asm, so that no per-register test is
+                // hoisted out of this loop)
+                uint32_t lr = lo_raw;
+                __asm__ volatile("" : "+s"(lr));
+                if (!est) {
+                    uint32_t omax = 0u;   // largest counted offset v - lo_raw
+                    TW_FOR_REGS(nch, {
+                        const uint32_t o = key[r] - lr;
+                        omax = max(omax, o <= lim0 ? o : 0u);
+                    })
 #pragma unroll
-            for (int m = 1; m < 64; m <<= 1) omax = max(omax, (uint32_t)__shfl_xor((int)omax, m, 64));
-            omax = __builtin_amdgcn_readfirstlane(omax);
-            const int B = omax == 0u ? 0 : 32 - __builtin_clz(omax);
-            const int P = (B + 10) / 11;
-            const int W = P > 0 ? (B + P - 1) / P : 0;
-            // P == 0: every counted value equals lo_raw (handled by the final pass)
-            if (P > 0) {
-                const int w0 = P == 1 ? max(B, 6) : W;
-                const int s0 = P == 1 ? 0 : B - W;
+                    for (int m = 1; m < 64; m <<= 1) omax = max(omax, (uint32_t)__shfl_xor((int)omax, m, 64));
+                    omax = __builtin_amdgcn_readfirstlane(omax);
+                    B = omax == 0u ? 0 : 32 - __builtin_clz(omax);
+                }
+                // B == 0: every counted value equals lo_raw (handled by the final pass)
+                if (B == 0) break;
+                const int s0 = max(B - MAXW, 0), w0 = B - s0;
+                const uint32_t top0 = (1u << w0) - 1u;
                 TW_FOR_REGS(nch, {
-                    const uint32_t o = key[r] - lo_raw;
-                    count(o <= lim0, o >> s0);
+                    const uint32_t o = key[r] - lr;
+                    count(o <= lim0, min(o >> s0, top0));
                 })
                 const int res = pick(s0, w0);
                 if (res < 0) {
                     fast = false;
                     lo = 0u;
-                } else {
-                    whole = res > 0;
-#pragma unroll 1
-                    for (int pass = 1; pass < P && !whole; ++pass) {
-                        const int shift = pass == P - 1 ? 0 : B - W * (pass + 1);
-                        const int width = pass == P - 1 ? B - W * (P - 1) : W;
-                        const uint32_t kb0 = lo_raw + prefix, lim = 1u << (shift + width);
-                        TW_FOR_REGS(nch, {
-                            const uint32_t o = key[r] - kb0;
-                            count(o < lim, o >> shift);
-                        })
-                        whole = pick(shift, width) > 0;
-                    }
+                    break;
                 }
-            } else {
+                if (est && (prefix >> s0) == top0) {   // the top bin (clamped values): exact span
+                    est = false;
+                    remaining = k;
+                    prefix = pmask = 0u;
+                    continue;
+                }
+                whole = res > 0;
+#pragma unroll 1
+                for (int low = s0; low > 0 && !whole;) {
+                    const int width = min(low, MAXW), shift = low - width;
+                    low = shift;
+                    const uint32_t kb0 = lo_raw + prefix, lim = 1u << (shift + width);
+                    TW_FOR_REGS(nch, {
+                        const uint32_t o = key[r] - kb0;
+                        count(o < lim, o >> shift);
+                    })
+                    whole = pick(shift, width) > 0;
+                }
+                break;
+            }
+            if (fast && B == 0) {
                 // nothing above lo_raw: the count of values equal to lo_raw decides
                 int cnt = 0;
                 TW_FOR_REGS(nch, cnt += __popcll(__ballot(key[r] == lo_raw));)
@@ -450,8 +551,9 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
             }
         }
         if (!fast) {
-            // order-preserving keys; lanes past the row's end get key 0
-            TW_FOR_REGS(nch, key[r] = 64 * r + lane < n ? score_key(__uint_as_float(key[r])) : 0u;)
+            // order-preserving keys; slots outside the row get key 0
+            TW_FOR_REGS(nch, key[r] = (uint32_t)(slot_of(r) - a) < (uint32_t)n ? score_key(__uint_as_float(key[r]))
+                                                                                : 0u;)
             uint32_t kmax = 0u;
             TW_FOR_REGS(nch, kmax = max(kmax, key[r]);)
 #pragma unroll
@@ -460,15 +562,13 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
 #pragma unroll 1
             for (int attempt = 0; attempt < 2; ++attempt) {
                 pad_bin0 = lo == 0u;
-                // the span's significant bits are cut into 1 to 3 digits of 6 to 11 bits
+                // the span's significant bits are cut into digits from the top, MAXW bits
+                // each but the last (the first digit as fine as the bins allow)
                 const uint32_t span = kmax - lo;
                 const int B = span == 0u ? 0 : 32 - __builtin_clz(span);
-                const int P = (B + 10) / 11;
-                const int W = P > 0 ? (B + P - 1) / P : 0;
-                if (P == 0) break;   // every key at or above lo is equal: ties in pool order
+                if (B == 0) break;   // every key at or above lo is equal: ties in pool order
                 // first digit: every key at or above lo
-                const int w0 = P == 1 ? max(B, 6) : W;
-                const int s0 = P == 1 ? 0 : B - W;
+                const int s0 = max(B - MAXW, 0), w0 = B - s0;
                 TW_FOR_REGS(nch, count(key[r] >= lo, (key[r] - lo) >> s0);)
                 const int res = pick(s0, w0);
                 if (res < 0) {   // lo was above the k-th largest key: all keys
@@ -480,9 +580,9 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
                 // lo + prefix + 2^(shift + width) (a bound that changes every pass, so no
                 // test is hoisted)
 #pragma unroll 1
-                for (int pass = 1; pass < P && !whole; ++pass) {
-                    const int shift = pass == P - 1 ? 0 : B - W * (pass + 1);
-                    const int width = pass == P - 1 ? B - W * (P - 1) : W;
+                for (int low = s0; low > 0 && !whole;) {
+                    const int width = min(low, MAXW), shift = low - width;
+                    low = shift;
                     const uint32_t kb0 = lo + prefix, lim = 1u << (shift + width);
                     TW_FOR_REGS(nch, count(key[r] - kb0 < lim, (key[r] - kb0) >> shift);)
                     whole = pick(shift, width) > 0;
@@ -495,9 +595,9 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
 
         // Ordered final pass: with a whole bin kept, every value v with thr <= v <=
         // top (thr is above 0: fewer than n pools are kept); otherwise those above thr
-        // and the first `remaining` equal to it. The padding lanes (0, after every
-        // pool of the row) are never kept: 0 is below thr, and at least `remaining`
-        // pools of the row equal thr before them.
+        // and the first `remaining` equal to it, in pool order. Slots outside the row
+        // (0) are never kept: 0 is below thr, those after the row come after every
+        // pool equal to thr, and those before it are left out of the equal ones.
         const uint32_t lge = top - thr;
         const bool has_gt = thr < top;
         const uint32_t agt = thr + 1u, lgt = top - thr - 1u;
@@ -505,16 +605,17 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
         auto mbcnt = [&](uint64_t m, int add) __attribute__((always_inline)) {
             return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, add));
         };
-        // pools of 4 tokens and k <= TK_BINS: the kept pools' numbers go to the wave's
+        // pools of 4 tokens and k <= NB: the kept pools' numbers go to the wave's
         // histogram array at their ranks, and the index row is written from there
         // with contiguous 16-byte stores; otherwise each kept pool is stored directly
-        const bool via_lds = KP4 && k <= TK_BINS;
-#define TW_FINAL(EMIT)                                                                                    \
+        const bool via_lds = KP4 && k <= NB;
+        // register r: ranks by ballot (slot 64r + lane)
+#define TW_FINAL_REGS(EMIT)                                                                               \
     if (whole) {                                                                                          \
         TW_FOR_REGS(nch, {                                                                                \
             const bool keep = key[r] - thr <= lge;                                                        \
             const uint64_t kb = __ballot(keep);                                                           \
-            EMIT(keep, mbcnt(kb, pos), r);                                                                \
+            EMIT(keep, mbcnt(kb, pos), 64 * r + lane);                                                    \
             pos += __popcll(kb);                                                                          \
         })                                                                                                \
     } else {                                                                                              \
@@ -525,19 +626,64 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
             const bool keep = (has_gt & (key[r] - agt <= lgt)) | (eq & (mbcnt(eb, eq_seen) < remaining)); \
             eq_seen += __popcll(eb);                                                                      \
             const uint64_t kb = __ballot(keep);                                                           \
-            EMIT(keep, mbcnt(kb, pos), r);                                                                \
+            EMIT(keep, mbcnt(kb, pos), 64 * r + lane);                                                    \
             pos += __popcll(kb);                                                                          \
         })                                                                                                \
     }
-#define TW_EMIT_LDS(keep, p, r) (*((keep) ? hist + (p) : spare) = 64 * (r) + lane)
-#define TW_EMIT_PUT(keep, p, r) \
-    if (keep) put((p), 64 * (r) + lane)
-        if (via_lds) {
-            TW_FINAL(TW_EMIT_LDS)
+        // group g (slots 256g + 4*lane + c): a kept slot's rank is the count kept in
+        // earlier groups, in the lanes below (all four registers: one ballot each,
+        // counted with a chain of mbcnt), and in the lane's own earlier registers
+#define TW_MBCNT4(b0, b1, b2, b3, add) tw_mbcnt4(b0, b1, b2, b3, add)
+#define TW_FINAL_GROUPS(EMIT)                                                                             \
+    {                                                                                                     \
+        int eq_seen = 0;                                                                                  \
+        TW_FOR_GROUPS(nch, {                                                                              \
+            bool kp[4];                                                                                   \
+            if (whole) {                                                                                  \
+                _Pragma("unroll") for (int c = 0; c < 4; ++c) kp[c] = key[4 * g + c] - thr <= lge;        \
+            } else {                                                                                      \
+                bool eq[4];                                                                               \
+                uint64_t eb[4];                                                                           \
+                _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                           \
+                    eq[c] = key[4 * g + c] == thr && (g > 0 || lane > 0 || c >= a);                       \
+                    eb[c] = __ballot(eq[c]);                                                              \
+                }                                                                                         \
+                int er = TW_MBCNT4(eb[0], eb[1], eb[2], eb[3], eq_seen);                                  \
+                _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                           \
+                    kp[c] = (has_gt & (key[4 * g + c] - agt <= lgt)) | (eq[c] & (er < remaining));        \
+                    er += eq[c];                                                                          \
+                    eq_seen += __popcll(eb[c]);                                                           \
+                }                                                                                         \
+            }                                                                                             \
+            uint64_t kb[4];                                                                               \
+            _Pragma("unroll") for (int c = 0; c < 4; ++c) kb[c] = __ballot(kp[c]);                        \
+            int p = TW_MBCNT4(kb[0], kb[1], kb[2], kb[3], pos);                                           \
+            _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                               \
+                EMIT(kp[c], p, 256 * g + 4 * lane + c - a);                                               \
+                p += kp[c];                                                                               \
+                pos += __popcll(kb[c]);                                                                   \
+            }                                                                                             \
+        })                                                                                                \
+    }
+#define TW_EMIT_LDS(keep, p, j) (*((keep) ? hist + (p) : spare) = (j))
+#define TW_EMIT_PUT(keep, p, j) \
+    if (keep) put((p), (j))
+        if (vec4) {
+            if (via_lds) {
+                TW_FINAL_GROUPS(TW_EMIT_LDS)
+            } else {
+                TW_FINAL_GROUPS(TW_EMIT_PUT)
+            }
         } else {
-            TW_FINAL(TW_EMIT_PUT)
+            if (via_lds) {
+                TW_FINAL_REGS(TW_EMIT_LDS)
+            } else {
+                TW_FINAL_REGS(TW_EMIT_PUT)
+            }
         }
-#undef TW_FINAL
+#undef TW_FINAL_REGS
+#undef TW_FINAL_GROUPS
+#undef TW_MBCNT4
 #undef TW_EMIT_LDS
 #undef TW_EMIT_PUT
         if (via_lds) {
@@ -551,6 +697,8 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 4) void topk_wave_kerne
     if (lane == 0 && num_valid) num_valid[i] = base + n_tail;
 }
 #undef TW_FOR_REGS
+#undef TW_FOR_GROUPS
+#undef TW_BITONIC_STEP
 
 // ------------------------------------------------------------- long rows ----
 // Rows with more visible pools than the LDS key cache (decode over a long
@@ -1019,18 +1167,23 @@ hipError_t launch_topk(const int32_t* cu, int num_docs, const int32_t* cu_pools,
     const bool many = has_long && (long long)kpool * topk >= TK_BINS &&
                       (long long)row_width >= (long long)kpool * topk + kpool + TM_STATE + 2 * chunks;
     if (!has_long) {
-        // rows of up to 4096 pools with 64 key registers per lane, longer ones with 128
+        // rows of up to 4096 slots with 64 key registers per lane, longer ones with 128
+        // (a launch per instance: each wave first looks up its row's length, so a
+        // third instance costs more than its extra waves per SIMD gain);
+        // 16-byte loads when every row's 16-byte chunks lie in the score tensor's row
+        // (a row's slots then end at most at its stride, a multiple of four)
         const int g = (num_q + TW_WAVES - 1) / TW_WAVES;
-#define KP_TW(KP4, R)                                                                                          \
-    topk_wave_kernel<KP4, R><<<g, 64 * TW_WAVES, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos, scores,    \
-                                                              max_pools, topk, row_width, indices, num_valid, \
-                                                              num_q)
+        const int vec4 = max_pools % 4 == 0 && ((uintptr_t)scores & 15) == 0;
+#define KP_TW(KP4, R, RLO)                                                                                     \
+    topk_wave_kernel<KP4, R, RLO><<<g, 64 * TW_WAVES, 0, stream>>>(cu, num_docs, cu_pools, kpool, q_pos,       \
+                                                                   scores, max_pools, topk, row_width, indices, \
+                                                                   num_valid, num_q, vec4)
         if (kpool == 4) {
-            KP_TW(true, 64);
-            if (max_pools > 4096) KP_TW(true, 128);
+            KP_TW(true, 64, 0);
+            if (max_pools > 4096) KP_TW(true, 128, 64);
         } else {
-            KP_TW(false, 64);
-            if (max_pools > 4096) KP_TW(false, 128);
+            KP_TW(false, 64, 0);
+            if (max_pools > 4096) KP_TW(false, 128, 64);
         }
 #undef KP_TW
         return hipGetLastError();

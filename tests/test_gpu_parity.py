@@ -198,7 +198,7 @@ def test_scores_fed_oracle_keys(K, oracle_mod, name):
 @pytest.mark.parametrize("case", ["tiny", "2k", "packed4k", "ties", "zeros", "negzero", "nan", "topk0",
                                   "decode1m_rows", "long_rand", "long_ties", "long_zeros", "long_nan",
                                   "long_bigk", "long_smallk", "mid_rand", "mid_ties", "mid_nan",
-                                  "mid_sampled_top"])
+                                  "mid_sampled_top", "mid_multidoc", "mid_multidoc_nan"])
 def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
     rng = np.random.default_rng(7)
     if case in ("tiny", "2k", "packed4k"):
@@ -240,6 +240,20 @@ def test_topk_from_oracle_scores_bitexact(K, oracle_mod, case):
         # (a small k leaves the rows no room for the many-workgroup scratch: the
         # one-workgroup long-row kernel runs instead)
         topk = 5000 if case == "long_bigk" else (37 if case == "long_smallk" else 512)
+    elif case.startswith("mid_multidoc"):
+        # documents whose first pools sit 1, 2 and 1 floats past a 16-byte boundary
+        # of the score rows (a stride of 8192 pools: the 16-byte-load layout)
+        T = 32768
+        cu = np.array([0, 4101, 4105, 16390, 32768], np.int32)
+        cp, _ = oracle_mod.layout(cu, T, 4)
+        qpos = np.array([0, 3, 2000, 4100, 4101, 4104, 4200, 9000, 12291, 16389, 16390, 16393, 17000, 24000,
+                         28675, 32767], np.int32)
+        sc = rng.standard_normal((len(qpos), T // 4)).astype(np.float32)
+        if case == "mid_multidoc_nan":
+            sc = np.round(sc * 2).astype(np.float32)
+            sc[rng.random(sc.shape) < 0.02] = np.nan
+            sc[rng.random(sc.shape) < 0.2] = -0.0
+        topk = 512
     elif case.startswith("mid_"):
         # rows of up to 8192 pools (the one-wave-per-row kernels: rows of 2048 or
         # more pools first bound the histogrammed keys from 64 sampled pools)
