@@ -206,7 +206,7 @@ size_t kp_indexer_workspace_bytes(int32_t num_q, int32_t max_pools, int32_t h_id
  *
  * Rows of many pools (decode over a long context): when scores == NULL,
  * max_pools >= 32768 and topk_pools <= 8192, no score tensor is formed. Per
- * query, a threshold is taken from the scores of every s-th pool (s >= 64);
+ * query, a threshold is taken from the scores of every s-th pool (s >= 256);
  * the scoring pass keeps only the (score, pool) pairs at or above it, at most
  * 16384 per query, and the top-k is selected among them. The kept pools are
  * the first k in the order "higher score first, then lower pool first", so
