@@ -172,4 +172,17 @@ __device__ __forceinline__ QueryPools query_pools(const int32_t* __restrict__ cu
     return r;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast 15 and 31 carry the
+// row totals into the rows above.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 }  // namespace kp

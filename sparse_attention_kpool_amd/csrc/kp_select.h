@@ -1,5 +1,5 @@
 // Selection helpers shared by the top-k kernels: the order-preserving score
-// key, wave and block scans, and a most-significant-digit-first radix select.
+// key, a block scan, and a most-significant-digit-first radix select.
 #pragma once
 
 #include "kp_device.h"
@@ -14,19 +14,6 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     // negative: all bits flipped; otherwise the sign bit set
     const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
     return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : k;                    // NaN: lowest
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
-// row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast 15 and 31 carry the
-// row totals into the rows above.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
-    return x;
 }
 
 // Exclusive scan of one int per thread over a block of NTH threads; returns

@@ -76,6 +76,11 @@ __device__ __forceinline__ float sum_over_groups(float v) {
 __device__ __forceinline__ void mfma_acc(f32x4& c, bf16x8 a, bf16x8 b) {
     __asm__ __volatile__("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
+// The same with a zero accumulator (the first tile of a pass): c = a . b, so O
+// needs no zeroing and is not live before the pass.
+__device__ __forceinline__ void mfma_set(f32x4& c, bf16x8 a, bf16x8 b) {
+    __asm__ __volatile__("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+}
 
 // The weights, computed by VALU code, become the B operands of the PV MFMAs:
 // the empty-bodied assembly makes them opaque from here on (the compiler can
@@ -84,6 +89,17 @@ __device__ __forceinline__ void mfma_acc(f32x4& c, bf16x8 a, bf16x8 b) {
 // read of them (gfx950 asks for 2).
 __device__ __forceinline__ void kp_pin_weights(bf16x8& a, bf16x8& b) {
     __asm__ __volatile__("s_nop 2" : "+v"(a), "+v"(b));
+}
+
+// Empty-bodied assembly that takes a value as an operand: the instructions that
+// compute it stay where they are written (the compiler would otherwise sink them
+// to their first use, past the matrix-core work they are meant to overlap).
+__device__ __forceinline__ void kp_keep(float& x) { __asm__ __volatile__("" : "+v"(x)); }
+__device__ __forceinline__ void kp_keep_lo(bf16x8& x) {
+    // the four weights of sub-tile 0 (the low half of the B operand)
+    auto u = __builtin_bit_cast(u32x4, x);
+    __asm__ __volatile__("" : "+v"(u[0]), "+v"(u[1]));
+    x = __builtin_bit_cast(bf16x8, u);
 }
 
 // The 64-column RoPE tail of a latent row (keys 576 wide, the GLM-5.2
@@ -103,8 +119,11 @@ __device__ __forceinline__ void lds_dma16_lane(u32x4 rsrc, uint32_t voff, uint32
 
 // D: width of the values and of the keys' NoPE part; DR: width of the keys'
 // RoPE tail (0, or 64 for the 576-wide keys of the GLM-5.2 contract, whose
-// values are the first 512 columns).
-template <int D, int DR>
+// values are the first 512 columns). SPLIT: the rows are split over nsplit
+// workgroups per query, which write fp32 partials (with SPLIT false, nsplit is 1;
+// the two epilogues are separate kernels so that neither takes registers from
+// the other).
+template <int D, int DR, bool SPLIT>
 __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ indices,
     int num_kv, int heads, int row_width, float scale_log2, uint16_t* __restrict__ out,
@@ -129,6 +148,9 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     static_assert(NW == 4 && MLA_TK == 64 && RPW == 16 && CH >= 8 && CH <= 64, "tile split");
     static_assert(4 * XB <= MLA_NBUF * TILE_B, "row-half merge fits the ring");
     static_assert(DR == 0 || (D == 512 && DR == 64), "RoPE tail: 512 + 64 only");
+    // the interleaved step (sub-tile 0's weights under sub-tile 1's k-steps) needs
+    // ten k-steps of room and no RoPE k-steps
+    constexpr bool IL = DR == 0 && KS >= 12;
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
     __shared__ __align__(16) int32_t list[MAXR];   // byte offsets of the listed latent rows
@@ -144,8 +166,9 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // one workgroup per query, or (nsplit > 1, few queries) per query and split:
     // split sp takes the tiles [ntiles*sp/nsplit, ntiles*(sp+1)/nsplit) of the
     // compacted row and leaves a normalised partial O and its lse for the combine
-    const int i = nsplit == 1 ? xcd_query(blockIdx.x, gridDim.x) : (int)(blockIdx.x / nsplit);
-    const int sp = nsplit == 1 ? 0 : (int)(blockIdx.x % nsplit);
+    const int ns = SPLIT ? nsplit : 1;
+    const int i = SPLIT ? (int)(blockIdx.x / ns) : xcd_query(blockIdx.x, gridDim.x);
+    const int sp = SPLIT ? (int)(blockIdx.x % ns) : 0;
 
     // ---- compact the index row (valid entries, original order) ----------------
     // Entry NT*k + tid is read in round k; the loads of all rounds are issued
@@ -198,6 +221,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         for (int e = tid; e < MLA_NBUF * TILE_B / 16; e += NT)
             reinterpret_cast<uint4*>(ring)[e] = make_uint4(0u, 0u, 0u, 0u);
     }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     unsigned long long bal[NRND];
 #pragma unroll
     for (int k = 0; k < NRND; ++k) {
@@ -205,50 +229,43 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         if (lane == 0) rcnt[k * NW + wave] = __popcll(bal[k]);
     }
     __syncthreads();
+    // The list holds, for local position p, the byte offset of its latent row plus
+    // 4096 - row_base(p % 4): entry p is loaded at immediate offset row_base(p % 4)
+    // within its group of four rows, through a descriptor based 4 KB below the
+    // latent (all offsets stay positive; the latent is below 4 GiB). It is padded to
+    // whole tiles with valid rows of the same list (position n + m repeats position
+    // m % n; the scores of those rows are masked), so the gather needs no bounds test.
     int n_valid;
     {
         static_assert(NRND * NW <= 64, "one count per lane");
         const int c = lane < NRND * NW ? rcnt[lane] : 0;
-        int x = c;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int u = __shfl_up(x, o, 64);
-            if (lane >= o) x += u;
-        }
-        n_valid = __builtin_amdgcn_readfirstlane(__shfl(x, 63, 64));
+        const int x = wave_incl_scan(c);
+        const int n_all = __builtin_amdgcn_readlane(x, 63);
         // this workgroup's entries: [e0, e1) of the compacted row, stored from 0
-        const int nt_all = (n_valid + MLA_TK - 1) / MLA_TK;
-        const int e0 = nt_all * sp / nsplit * MLA_TK;
-        const int e1 = min(n_valid, nt_all * (sp + 1) / nsplit * MLA_TK);
+        const int nt_all = (n_all + MLA_TK - 1) / MLA_TK;
+        const int e0 = nt_all * sp / ns * MLA_TK;
+        const int e1 = min(n_all, nt_all * (sp + 1) / ns * MLA_TK);
         n_valid = max(0, e1 - e0);
+        const int n_pad = (n_valid + MLA_TK - 1) / MLA_TK * MLA_TK - n_valid;
         const int excl = x - c;   // entries before (round, wave) = lane's pair
 #pragma unroll
         for (int k = 0; k < NRND; ++k) {
-            const int base = __shfl(excl, k * NW + wave, 64);
+            const int base = __builtin_amdgcn_readlane(excl, k * NW + wave_u);
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0u));
-            const int pos = base + (int)below;
-            if (ent[k] >= 0 && ent[k] < num_kv && pos >= e0 && pos < e1)   // byte offset (the latent is below 4 GiB)
-                list[pos - e0] = (int32_t)((uint32_t)ent[k] * (uint32_t)(DQK * 2));
+            const int p = base + (int)below - e0;
+            if (ent[k] >= 0 && ent[k] < num_kv && p >= 0 && p < n_valid) {
+                const uint32_t off = (uint32_t)ent[k] * (uint32_t)(DQK * 2) + 4096u;
+                list[p] = (int32_t)(off - (uint32_t)row_base<RB>(p & 3));
+                for (int m = p; m < n_pad; m += n_valid)
+                    list[n_valid + m] = (int32_t)(off - (uint32_t)row_base<RB>((n_valid + m) & 3));
+            }
         }
-    }
-    __syncthreads();
-    // pad the list to whole tiles with a valid row (its scores are masked), so
-    // the gather needs no bounds test
-    {
-        const int pad_end = (n_valid + MLA_TK - 1) / MLA_TK * MLA_TK;
-        if (n_valid > 0 && tid < pad_end - n_valid) list[n_valid + tid] = list[0];
-        __syncthreads();
-        // entry p is loaded at immediate offset row_base(p % 4) within its group of
-        // four rows, through a descriptor based 4 KB below the latent (all offsets stay
-        // positive): the list holds byte offset + 4096 - row_base(p % 4)
-        for (int p = tid; p < pad_end; p += NT)
-            list[p] = (int32_t)((uint32_t)list[p] + 4096u - (uint32_t)row_base<RB>(p & 3));
     }
     __syncthreads();
 
     if (n_valid == 0) {
-        if (nsplit == 1) {
+        if (!SPLIT) {
             uint16_t* orow = out + (size_t)i * heads * D;
             for (int e = tid; e < heads * D; e += NT) orow[e] = 0;
             if (lse && tid < heads) lse[(size_t)i * heads + tid] = -INFINITY;
@@ -329,7 +346,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) o[ct][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ht = 0; ht < 2; ++ht)
+            if (!IL) o[ct][ht] = f32x4{0.f, 0.f, 0.f, 0.f};   // (with IL the first tile writes O)
     // softmax state of head 32*hh + 16*ht + n over this wave's rows (the four lanes
     // of a head hold the same reference max and their own partial sums). O is
     // never rescaled inside the loop (its accumulators live in AGPRs, and a
@@ -478,11 +496,36 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         lds_barrier();                                                                         \
         ++kt;
 
+// PV by pairs of column tiles, V read three pairs ahead (each pair interleaves
+// its four MFMAs with the four reads of a later pair); the first three pairs'
+// V fragments are in vf_ already
+#define KP_PV(FRESH)                                                                           \
+        _Pragma("unroll") for (int c = 0; c < CT / 2; ++c) {                                   \
+            const bool ld_ = c + KP_RING_V - 1 < CT / 2;                                       \
+            bf16x4 vh_[2][2];                                                                  \
+            _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                    \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                if (FRESH) mfma_set(o[2 * c + u][0], vf_[c % KP_RING_V][u], pb_[0]);           \
+                else mfma_acc(o[2 * c + u][0], vf_[c % KP_RING_V][u], pb_[0]);                 \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                if (ld_) vh_[u][0] = KP_V_HALF(c + KP_RING_V - 1, u, 0);                      \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                if (FRESH) mfma_set(o[2 * c + u][1], vf_[c % KP_RING_V][u], pb_[1]);           \
+                else mfma_acc(o[2 * c + u][1], vf_[c % KP_RING_V][u], pb_[1]);                 \
+                __builtin_amdgcn_sched_barrier(0);                                             \
+                if (ld_) {                                                                     \
+                    vh_[u][1] = KP_V_HALF(c + KP_RING_V - 1, u, 1);                            \
+                    vf_[(c + KP_RING_V - 1) % KP_RING_V][u] =                                  \
+                        __builtin_shufflevector(vh_[u][0], vh_[u][1], 0, 1, 2, 3, 4, 5, 6, 7);  \
+                }                                                                              \
+            }                                                                                  \
+        }                                                                                      \
+
     // one attention step on tile kt; with FIRST, the reference of a head is set by
     // its first tile with a valid row and a weight above 2^MLA_HEADROOM raises the
     // flag. Once set, the reference does not depend on the tile, so the weights
     // are computed straight from the scores: no cross-lane max on the way to PV.
-#define KP_STEP(FIRST)                                                                         \
+#define KP_STEP(FIRST, FRESH)                                                                  \
     {                                                                                          \
         KP_QK()                                                                                \
         /* the first V chunks do not depend on the softmax: their reads are issued now, */    \
@@ -517,26 +560,91 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         /* (a sum over the bound with no single weight over it only costs an exact pass) */   \
         if (FIRST && __ballot(wmax_ > MLA_WEIGHT_MAX)) rflag[kt & 1] = 1;                      \
         kp_pin_weights(pb_[0], pb_[1]);                                                        \
-        /* PV by pairs of column tiles, V read three pairs ahead */                            \
-        /* (each pair interleaves its four MFMAs with the four reads of a later pair) */       \
-        _Pragma("unroll") for (int c = 0; c < CT / 2; ++c) {                                   \
-            const bool ld_ = c + KP_RING_V - 1 < CT / 2;                                       \
-            bf16x4 vh_[2][2];                                                                  \
-            _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                    \
-                __builtin_amdgcn_sched_barrier(0);                                             \
-                mfma_acc(o[2 * c + u][0], vf_[c % KP_RING_V][u], pb_[0]);                      \
-                __builtin_amdgcn_sched_barrier(0);                                             \
-                if (ld_) vh_[u][0] = KP_V_HALF(c + KP_RING_V - 1, u, 0);                      \
-                __builtin_amdgcn_sched_barrier(0);                                             \
-                mfma_acc(o[2 * c + u][1], vf_[c % KP_RING_V][u], pb_[1]);                      \
-                __builtin_amdgcn_sched_barrier(0);                                             \
-                if (ld_) {                                                                     \
-                    vh_[u][1] = KP_V_HALF(c + KP_RING_V - 1, u, 1);                            \
-                    vf_[(c + KP_RING_V - 1) % KP_RING_V][u] =                                  \
-                        __builtin_shufflevector(vh_[u][0], vh_[u][1], 0, 1, 2, 3, 4, 5, 6, 7);  \
-                }                                                                              \
+        KP_PV(FRESH)                                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        KP_STEP_END()                                                                          \
+    }
+    // A step after the first tile of a pass: the reference of every head is set
+    // (all 64 rows of the first tile are valid whenever a second tile exists), so
+    // the weights of sub-tile 0 are computed while the matrix core runs the k-steps
+    // of sub-tile 1, and the reads of the first V fragments fill the last k-steps.
+    // In a ragged last tile the rows past the end are masked, sub-tile by sub-tile,
+    // before their weights. The arithmetic is that of KP_STEP, in the same order:
+    // the two give the same bits.
+#define KP_MASK_SUB(s_)                                                                        \
+    {                                                                                          \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e)                                          \
+            if (4 * (s_) + e >= lim_) {                                                        \
+                sacc_[s_][0][e] = -INFINITY;                                                   \
+                sacc_[s_][1][e] = -INFINITY;                                                   \
+            }                                                                                  \
+    }
+#define KP_KU(u_) ku_[(u_) % 4] = *reinterpret_cast<const bf16x8*>(tbk_[(u_) / KS] + 64 * ((u_) % KS));
+#define KP_STEP_IL(CHECK)                                                                      \
+    {                                                                                          \
+        const int buf_ = kt & 1;                                                               \
+        /* (the last tile gathers its own rows again, as in KP_QK) */                          \
+        const int ktn_ = kt + 1 < ntiles ? kt + 1 : kt;                                        \
+        KP_ROWS_OF(ktn_)                                                                       \
+        const uint8_t* tb_ = ring + buf_ * TILE_B;                                             \
+        const uint8_t* tbk_[2] = {tb_ + kb[0], tb_ + kb[1]};                                   \
+        const uint8_t* tbv_[2] = {tb_ + vb[0], tb_ + vb[1]};                                   \
+        const bool ragged_ = (kt + 1) * MLA_TK > n_valid;                                      \
+        const int lim_ = n_valid - (kt * MLA_TK + 32 * rh + 8 * g);   /* rows 4s+e < lim_ valid */ \
+        f32x4 sacc_[2][2];                                                                     \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s)                                          \
+            _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) sacc_[s][ht] = f32x4{0.f, 0.f, 0.f, 0.f}; \
+        /* K fragment u: sub-tile u / KS, k-step u % KS, read three ahead of its MFMAs */     \
+        bf16x8 ku_[4];                                                                         \
+        KP_KU(0) KP_KU(1) KP_KU(2)                                                             \
+        bf16x8 vf_[KP_RING_V][2];                                                              \
+        float w_[2][8];                                                                        \
+        float ws0_[2];                                                                         \
+        bf16x8 pb_[2];                                                                         \
+        _Pragma("unroll") for (int u = 0; u < 2 * KS; ++u) {                                   \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            sacc_[u / KS][0] = mfma_bf16_16x16x32(ku_[u % 4], qf[0][u % KS], sacc_[u / KS][0]); \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (u + 3 < 2 * KS) {                                                              \
+                KP_KU(u + 3)                                                                   \
+            } else {                                                                           \
+                KP_V_CHUNK(u + 3 - 2 * KS)                                                     \
+            }                                                                                  \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            sacc_[u / KS][1] = mfma_bf16_16x16x32(ku_[u % 4], qf[1][u % KS], sacc_[u / KS][1]); \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            _Pragma("unroll") for (int j = u * RPW / (2 * KS); j < (u + 1) * RPW / (2 * KS); ++j) \
+                KP_ISSUE_ROW(j, buf_ ^ 1)                                                      \
+            if (u == KS && ragged_) KP_MASK_SUB(0)                                             \
+            /* sub-tile 0: one weight per k-step of sub-tile 1, then its sums and bf16 */     \
+            if (u >= KS + 1 && u < KS + 9) {                                                   \
+                const int h_ = (u - KS - 1) / 4, e_ = (u - KS - 1) % 4;                        \
+                w_[h_][e_] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc_[0][h_][e_], scale_log2, -m_ref[h_])); \
+                kp_keep(w_[h_][e_]);                                                           \
+            }                                                                                  \
+            if (u == KS + 9 || u == KS + 10) {                                                 \
+                const int h_ = u - KS - 9;                                                     \
+                ws0_[h_] = (w_[h_][0] + w_[h_][1]) + (w_[h_][2] + w_[h_][3]);                  \
+                kp_keep(ws0_[h_]);                                                             \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e) pb_[h_][e] = (__bf16)w_[h_][e];  \
+                kp_keep_lo(pb_[h_]);                                                           \
             }                                                                                  \
         }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (ragged_) KP_MASK_SUB(1)                                                            \
+        float wmax_ = 0.f;                                                                     \
+        _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                     \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e)                                      \
+                w_[ht][4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc_[1][ht][e], scale_log2, -m_ref[ht])); \
+            _Pragma("unroll") for (int e = 4; e < 8; ++e) pb_[ht][e] = (__bf16)w_[ht][e];      \
+            lsum[ht] = mfma_bf16_16x16x32(ones, pb_[ht], lsum[ht]);                            \
+            const float ws_ = ws0_[ht] + ((w_[ht][4] + w_[ht][5]) + (w_[ht][6] + w_[ht][7]));  \
+            l_lse[ht] += ws_;                                                                  \
+            wmax_ = fmaxf(wmax_, ws_);                                                         \
+        }                                                                                      \
+        if (CHECK && __ballot(wmax_ > MLA_WEIGHT_MAX)) rflag[kt & 1] = 1;                      \
+        kp_pin_weights(pb_[0], pb_[1]);                                                        \
+        KP_PV(false)                                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                     \
         KP_STEP_END()                                                                          \
     }
@@ -569,34 +677,61 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         for (int c = 0; c < RK; ++c)
             if (!(head < heads)) qr[ht][c] = bf16x8{};
     }
-    for (int kt = 0;;) {
-        // the flag of the previous step is final (set before the last barrier) and
-        // is not written again before the next one: every wave reads the same value
-        // and leaves the loop at the same step
-        const int over_prev = __builtin_amdgcn_readfirstlane(rflag[(kt & 1) ^ 1]);
-        KP_STEP(true)
-        if (over_prev || kt >= ntiles) break;
+    // a score rose too far above its first-tile reference: the pass is dropped,
+    // a sweep finds the exact max of every head, and the attention runs again with it
+#define KP_RESET_PASS()                                                                        \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct)                                          \
+        _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                                       \
+            if (!IL) o[ct][ht] = f32x4{0.f, 0.f, 0.f, 0.f};                                    \
+    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
+        m_ref[ht] = -1e30f;                                                                    \
+        lsum[ht] = f32x4{0.f, 0.f, 0.f, 0.f};                                                  \
+        l_lse[ht] = 0.f;                                                                       \
     }
-    // read after the last barrier of the pass: the same value in every wave
-    if (__builtin_amdgcn_readfirstlane(rflag[0] | rflag[1])) {
-        // a score rose too far above its first-tile reference: drop the pass, sweep
-        // for the exact max of every head, and run the attention again with it
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) o[ct][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            m_ref[ht] = -1e30f;
-            lsum[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-            l_lse[ht] = 0.f;
+    if (IL) {
+        // The first tile sets the references, the later ones run the interleaved
+        // step. A flag raised by a step is final after that step's barrier and is not
+        // written again before the next one: every wave reads the same value and
+        // leaves at the same step. The second pass (after the exact-max sweep) runs
+        // the same steps: its weights are at most 1, so it raises no flag, and O stays
+        // in the same accumulators through both passes.
+        for (int pass = 0;; ++pass) {
+            int kt = 0;
+            KP_STEP(true, true)
+            while (kt < ntiles) {
+                const int over_prev = __builtin_amdgcn_readfirstlane(rflag[(kt & 1) ^ 1]);
+                KP_STEP_IL(true)
+                if (over_prev) break;
+            }
+            // read after the last barrier of the pass: the same value in every wave
+            if (pass == 1 || !__builtin_amdgcn_readfirstlane(rflag[0] | rflag[1])) break;
+            KP_RESET_PASS()
+            KP_FIRST_TILE()
+            if (tid < 2) rflag[tid] = 0;   // every wave read the flags before that barrier
+            for (kt = 0; kt < ntiles;) KP_MAX_STEP()
+            KP_FIRST_TILE()
         }
-        KP_FIRST_TILE()
-        for (int kt = 0; kt < ntiles;) KP_MAX_STEP()
-        KP_FIRST_TILE()
-        for (int kt = 0; kt < ntiles;) KP_STEP(false)
+    } else {
+        for (int kt = 0;;) {
+            const int over_prev = __builtin_amdgcn_readfirstlane(rflag[(kt & 1) ^ 1]);
+            KP_STEP(true, false)
+            if (over_prev || kt >= ntiles) break;
+        }
+        // read after the last barrier of the pass: the same value in every wave
+        if (__builtin_amdgcn_readfirstlane(rflag[0] | rflag[1])) {
+            KP_RESET_PASS()
+            KP_FIRST_TILE()
+            for (int kt = 0; kt < ntiles;) KP_MAX_STEP()
+            KP_FIRST_TILE()
+            for (int kt = 0; kt < ntiles;) KP_STEP(false, false)
+        }
     }
+#undef KP_RESET_PASS
 #undef KP_STEP
+#undef KP_STEP_IL
+#undef KP_KU
+#undef KP_MASK_SUB
+#undef KP_PV
 #undef KP_MAX_STEP
 #undef KP_QK
 #undef KP_TILE_MAX
@@ -614,6 +749,14 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #undef KP_ROWS_OF
 
     // ---- merge the two row halves and write ---------------------------------------
+    // (the lane and wave indices are derived again from the lane count and the
+    // scalar wave index: the values the prologue derived from the thread index would
+    // otherwise stay live across the main loop, which leaves them no registers)
+    {
+    int lane_x = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    __asm__ __volatile__("" : "+v"(lane_x));
+    const int lane = lane_x, n = lane_x & 15, g = lane_x >> 4;
+    const int wave = wave_s, rh = wave_s >> 1, hh = wave_s & 1;
     // wave (rh, hh) finishes the column half rh of its heads: it hands its O of
     // the other column half, and its softmax state, to the partner (1-rh, hh)
     float lr[2], le[2];
@@ -629,7 +772,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         uint8_t* xo_ = ring + (2 * hh + (1 - (RH))) * XB;                                      \
         _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
             _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                                   \
-                *reinterpret_cast<f32x4*>(xo_ + ((2 * j + ht) * 64 + lane) * 16) = o[(CT / 2) * (1 - (RH)) + j][ht]; \
+                *reinterpret_cast<f32x4*>(xo_ + ((ht * (CT / 2) + j) * 64 + lane) * 16) = o[(CT / 2) * (1 - (RH)) + j][ht]; \
     }
     if (rh == 0) KP_HAND_OVER(0) else KP_HAND_OVER(1)
 #undef KP_HAND_OVER
@@ -654,7 +797,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         fb[ht] = __builtin_amdgcn_exp2f(mp[0] - M);
         const float lse_h = (M + log2f(le[ht] * fa[ht] + mp[2] * fb[ht])) * 0.69314718055994530942f;
         if (rh == 0 && g == 0 && head < heads) {
-            if (nsplit > 1) lse_part[(size_t)blockIdx.x * heads + head] = lse_h;
+            if (SPLIT) lse_part[(size_t)blockIdx.x * heads + head] = lse_h;
             else if (lse) lse[(size_t)i * heads + head] = lse_h;
         }
         const float inv = 1.0f / (lr[ht] * fa[ht] + mp[1] * fb[ht]);
@@ -672,7 +815,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         uint16_t* dst_ = out + ((size_t)i_late * heads + head_) * D;                           \
         f32x4 op_[CT / 2];                                                                     \
         _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
-            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((2 * j + ht) * 64 + lane) * 16);    \
+            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((ht * (CT / 2) + j) * 64 + lane) * 16);    \
         if (head_ < heads) {                                                                   \
             _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                               \
                 const int ct_ = (CT / 2) * (RH) + j;                                           \
@@ -693,7 +836,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         float* dst_ = o_part + ((size_t)blockIdx.x * heads + head_) * D;                       \
         f32x4 op_[CT / 2];                                                                     \
         _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
-            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((2 * j + ht) * 64 + lane) * 16);    \
+            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((ht * (CT / 2) + j) * 64 + lane) * 16);    \
         if (head_ < heads) {                                                                   \
             _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                               \
                 const int ct_ = (CT / 2) * (RH) + j;                                           \
@@ -707,17 +850,63 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             }                                                                                  \
         }                                                                                      \
     }
-    if (nsplit > 1) {
+    // (full-width latent: each wave stages its finished values as bf16 in the
+    // hand-over region it has just read, 16 head rows of D/2 columns per head tile
+    // at a pitch of SPH bytes, so that the 8-byte writes of a pass of 16 lanes (16 heads) fall in
+    // distinct banks; after a barrier each wave stores 16 whole head rows of the
+    // query's contiguous output, 16 bytes per lane, the two column halves of a row
+    // coming from the regions of the two row-half waves: every store instruction
+    // writes D*2 contiguous bytes)
+    constexpr int SPH = D + 16;
+    static_assert(DP != D || 16 * SPH <= XB / 2, "output staging fits a hand-over region");
+#define KP_STAGE(RH)                                                                           \
+    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
+        /* head tile ht's hand-over sits in half ht of the region: it is read whole, */       \
+        /* then overwritten by the staged rows */                                              \
+        f32x4 op_[CT / 2];                                                                     \
+        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j)                                     \
+            op_[j] = *reinterpret_cast<const f32x4*>(xi + ((ht * (CT / 2) + j) * 64 + lane) * 16); \
+        uint8_t* srow_ = ring + (2 * hh + (RH)) * XB + ht * (XB / 2) + n * SPH;                \
+        _Pragma("unroll") for (int j = 0; j < CT / 2; ++j) {                                   \
+            bf16x4 r_;                                                                         \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e)                                      \
+                r_[e] = (__bf16)(__builtin_fmaf(o[(CT / 2) * (RH) + j][ht][e], fa[ht], op_[j][e] * fb[ht])); \
+            *reinterpret_cast<bf16x4*>(srow_ + 2 * (16 * j + 4 * g)) = r_;                     \
+        }                                                                                      \
+    }
+    if (SPLIT) {
         if (rh == 0) {
             KP_FINISH_PART(0)
         } else {
             KP_FINISH_PART(1)
         }
-    } else if (rh == 0) {
-        KP_FINISH(0)
+    } else if (DP != D) {
+        if (rh == 0) {
+            KP_FINISH(0)
+        } else {
+            KP_FINISH(1)
+        }
     } else {
-        KP_FINISH(1)
+        if (rh == 0) {
+            KP_STAGE(0)
+        } else {
+            KP_STAGE(1)
+        }
+        __syncthreads();
+        // wave w stores heads 16w .. 16w+15, one 1 KB row per instruction: lane l
+        // brings 16 bytes of column half l / 32 from the staged rows of head tile
+        // w % 2 in the regions of the waves (0, w / 2) and (1, w / 2)
+        static_assert(DP != D || D == 512, "one row per store instruction");
+        const uint8_t* const src =
+            ring + (2 * (wave >> 1) + (lane >> 5)) * XB + (wave & 1) * (XB / 2) + 16 * (lane & 31);
+        uint8_t* const dst = reinterpret_cast<uint8_t*>(out + ((size_t)i_late * heads + 16 * wave) * D) + 16 * lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (16 * wave + r < heads)
+                *reinterpret_cast<uint4*>(dst + r * (2 * D)) = *reinterpret_cast<const uint4*>(src + r * SPH);
     }
+    }
+#undef KP_STAGE
 #undef KP_FINISH
 #undef KP_FINISH_PART
 }
@@ -819,8 +1008,12 @@ static hipError_t launch_mla_t(const uint16_t* q, const uint16_t* kv, const int3
         const size_t o = (size_t)num_q * ns * heads * D * sizeof(float);
         lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(part) + ((o + 255) & ~(size_t)255));
     }
-    sparse_mla_kernel<D, DR><<<num_q * ns, 64 * MLA_NW, 0, stream>>>(q, kv, indices, num_kv, heads, row_width,
-                                                                      scale_log2, out, lse, ns, o_part, lse_part);
+    if (ns > 1)
+        sparse_mla_kernel<D, DR, true><<<num_q * ns, 64 * MLA_NW, 0, stream>>>(
+            q, kv, indices, num_kv, heads, row_width, scale_log2, out, lse, ns, o_part, lse_part);
+    else
+        sparse_mla_kernel<D, DR, false><<<num_q, 64 * MLA_NW, 0, stream>>>(
+            q, kv, indices, num_kv, heads, row_width, scale_log2, out, lse, 1, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const long long waves = (long long)num_q * heads;
