@@ -151,6 +151,13 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // the interleaved step (sub-tile 0's weights under sub-tile 1's k-steps) needs
     // ten k-steps of room and no RoPE k-steps
     constexpr bool IL = DR == 0 && KS >= 12;
+    // Q of the 512-wide latent comes in through LDS (ring tile 1, free until the
+    // first step gathers into it): one 1 KB head row per direct-to-LDS load, rows
+    // QP bytes apart, a pitch at which the operand reads of 16 heads x one chunk
+    // column hit distinct banks in every read pass
+    constexpr bool QDMA = IL && D == 512;
+    constexpr int QP = 2 * D + 32;
+    static_assert(!QDMA || 64 * QP <= TILE_B, "Q fits a ring tile");
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
     __shared__ __align__(16) int32_t list[MAXR];   // byte offsets of the listed latent rows
@@ -195,6 +202,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     bf16x8 qf[2][KS];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
+        if (QDMA) break;
         const int head = 32 * hh + 16 * ht + n;
         const uint16_t* qrow = q + ((size_t)i * heads + min(head, heads - 1)) * DQK;
 #pragma unroll
@@ -227,6 +235,21 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     for (int k = 0; k < NRND; ++k) {
         bal[k] = __ballot(ent[k] >= 0 && ent[k] < num_kv);
         if (lane == 0) rcnt[k * NW + wave] = __popcll(bal[k]);
+    }
+    if (QDMA) {
+        // (issued once the index row has landed, so that no wait for it waits for
+        // these too) wave w brings head rows 16w .. 16w+15 of the query; rows past
+        // `heads` lie outside the descriptor's range and land as zeros
+        const uint64_t qa = reinterpret_cast<uint64_t>(q) + (uint64_t)i * (uint64_t)(heads * DQK * 2);
+        const u32x4 q_rsrc = u32x4{(uint32_t)qa, (uint32_t)(qa >> 32) & 0xFFFFu, (uint32_t)(heads * DQK * 2),
+                                   0x00020000u};
+        const uint32_t q_lds = lds_addr(ring) + (uint32_t)TILE_B;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int head = 16 * wave_u + r;
+            lds_dma16_row_at<0>(q_rsrc, 16u * lane, (uint32_t)(head * DQK * 2),
+                                __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)(head * QP)));
+        }
     }
     __syncthreads();
     // The list holds, for local position p, the byte offset of its latent row plus
@@ -399,6 +422,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // chunks ahead of its MFMAs, a V chunk KP_RING_V-1
 #define KP_RING_K 4
 #define KP_RING_V 4
+#define KP_RING_U 4   // the interleaved step's K fragments (one sub-tile each)
 #define KP_K_FRAG(c_, s_)                                                                      \
     kf_[(c_) % KP_RING_K][s_] = *reinterpret_cast<const bf16x8*>(tbk_[s_] + 64 * (c_));
 #define KP_K_CHUNK(c_) { KP_K_FRAG(c_, 0) KP_K_FRAG(c_, 1) }
@@ -579,7 +603,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
                 sacc_[s_][1][e] = -INFINITY;                                                   \
             }                                                                                  \
     }
-#define KP_KU(u_) ku_[(u_) % 4] = *reinterpret_cast<const bf16x8*>(tbk_[(u_) / KS] + 64 * ((u_) % KS));
+#define KP_KU(u_) ku_[(u_) % KP_RING_U] = *reinterpret_cast<const bf16x8*>(tbk_[(u_) / KS] + 64 * ((u_) % KS));
 #define KP_STEP_IL(CHECK)                                                                      \
     {                                                                                          \
         const int buf_ = kt & 1;                                                               \
@@ -594,24 +618,21 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         f32x4 sacc_[2][2];                                                                     \
         _Pragma("unroll") for (int s = 0; s < 2; ++s)                                          \
             _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) sacc_[s][ht] = f32x4{0.f, 0.f, 0.f, 0.f}; \
-        /* K fragment u: sub-tile u / KS, k-step u % KS, read three ahead of its MFMAs */     \
-        bf16x8 ku_[4];                                                                         \
-        KP_KU(0) KP_KU(1) KP_KU(2)                                                             \
+        /* K fragment u: sub-tile u / KS, k-step u % KS, read KP_RING_U-1 ahead of its MFMAs */ \
+        bf16x8 ku_[KP_RING_U];                                                                 \
+        _Pragma("unroll") for (int u = 0; u < KP_RING_U - 1; ++u) KP_KU(u)                     \
         bf16x8 vf_[KP_RING_V][2];                                                              \
         float w_[2][8];                                                                        \
         float ws0_[2];                                                                         \
         bf16x8 pb_[2];                                                                         \
         _Pragma("unroll") for (int u = 0; u < 2 * KS; ++u) {                                   \
             __builtin_amdgcn_sched_barrier(0);                                                 \
-            sacc_[u / KS][0] = mfma_bf16_16x16x32(ku_[u % 4], qf[0][u % KS], sacc_[u / KS][0]); \
+            sacc_[u / KS][0] = mfma_bf16_16x16x32(ku_[u % KP_RING_U], qf[0][u % KS], sacc_[u / KS][0]); \
             __builtin_amdgcn_sched_barrier(0);                                                 \
-            if (u + 3 < 2 * KS) {                                                              \
-                KP_KU(u + 3)                                                                   \
-            } else {                                                                           \
-                KP_V_CHUNK(u + 3 - 2 * KS)                                                     \
-            }                                                                                  \
+            if (u + KP_RING_U - 1 < 2 * KS) KP_KU(u + KP_RING_U - 1)                           \
+            if (u >= 2 * KS - (KP_RING_V - 1)) KP_V_CHUNK(u - (2 * KS - (KP_RING_V - 1)))      \
             __builtin_amdgcn_sched_barrier(0);                                                 \
-            sacc_[u / KS][1] = mfma_bf16_16x16x32(ku_[u % 4], qf[1][u % KS], sacc_[u / KS][1]); \
+            sacc_[u / KS][1] = mfma_bf16_16x16x32(ku_[u % KP_RING_U], qf[1][u % KS], sacc_[u / KS][1]); \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             _Pragma("unroll") for (int j = u * RPW / (2 * KS); j < (u + 1) * RPW / (2 * KS); ++j) \
                 KP_ISSUE_ROW(j, buf_ ^ 1)                                                      \
@@ -667,6 +688,17 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     compiler_fence();
     KP_FIRST_TILE()
     __builtin_amdgcn_sched_barrier(0);
+    if (QDMA) {
+        // Q from LDS into the operand registers, then a barrier: every wave has its Q
+        // before the first step gathers into ring tile 1
+        const uint8_t* qb = ring + TILE_B;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qb + (32 * hh + 16 * ht + n) * QP + 64 * ks + 16 * g);
+        lds_barrier();
+    }
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
         const int head = 32 * hh + 16 * ht + n;
@@ -743,6 +775,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #undef KP_V_CHUNK
 #undef KP_RING_K
 #undef KP_RING_V
+#undef KP_RING_U
 #undef KP_ISSUE_TILE
 #undef KP_ISSUE_ROPE
 #undef KP_ISSUE_ROW
