@@ -107,28 +107,35 @@ __device__ __forceinline__ float max4_in_8(float a, float b, float c, float d) {
 // v from lane (lane ^ M). Distances below 16 stay inside a 16-lane DPP row and
 // are made of row moves that run on the vector ALU: quad_perm swaps for 1 and 2
 // (and 3); the half-row mirror reads lane ^ 7 and the row mirror lane ^ 15, so
-// 4 = 3 then 7 and 8 = 7 then 15. Larger distances go through ds_bpermute.
-// The source lane must be active (callers keep whole lane groups together).
+// 4 = 3 then 7 and 8 = 7 then 15. Distances 16 and 32 use gfx950's lane swaps:
+// v_permlane16_swap with both operands v leaves the odd 16-lane rows' values in
+// the first result's odd rows and the even rows' in the second result's even
+// rows, so lane l takes its partner l ^ 16 from the first result when l is in an
+// odd row and from the second otherwise; v_permlane32_swap does the same for the
+// two halves of the wave. The source lane must be active (callers keep whole
+// lane groups together).
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
-    if constexpr (M >= 16) {
-        return shfl_xor(v, M);
+    int i = __float_as_int(v);
+    if constexpr (M == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+        i = (int)((threadIdx.x & 32) ? p[0] : p[1]);
+    } else if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
+        i = (int)((threadIdx.x & 16) ? p[0] : p[1]);
+    } else if constexpr (M == 1) {
+        i = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);           // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        i = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);           // quad_perm [2,3,0,1]
+    } else if constexpr (M == 4) {
+        i = __builtin_amdgcn_mov_dpp(i, 0x1B, 0xF, 0xF, false);           // quad_perm [3,2,1,0]
+        i = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false);          // row_half_mirror
     } else {
-        int i = __float_as_int(v);
-        if constexpr (M == 1) {
-            i = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);           // quad_perm [1,0,3,2]
-        } else if constexpr (M == 2) {
-            i = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);           // quad_perm [2,3,0,1]
-        } else if constexpr (M == 4) {
-            i = __builtin_amdgcn_mov_dpp(i, 0x1B, 0xF, 0xF, false);           // quad_perm [3,2,1,0]
-            i = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false);          // row_half_mirror
-        } else {
-            static_assert(M == 8, "lane_xor: power-of-two distance");
-            i = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false);          // row_half_mirror
-            i = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, false);          // row_mirror
-        }
-        return __int_as_float(i);
+        static_assert(M == 8, "lane_xor: power-of-two distance up to 32");
+        i = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false);          // row_half_mirror
+        i = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, false);          // row_mirror
     }
+    return __int_as_float(i);
 }
 
 template <int W, int M = 1>
