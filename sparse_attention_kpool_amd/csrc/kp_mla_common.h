@@ -69,6 +69,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // wait until none of this wave's vector-memory operations is outstanding
 // (vmcnt 0; expcnt 7 and lgkmcnt 15 mean "do not wait" on those counters)
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until at most N of this wave's vector-memory operations are outstanding
+// (vmcnt N: bits 3:0 and 15:14 of the wait's immediate)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Barrier that orders LDS traffic between waves but does not wait for the
 // gathers in flight (a __syncthreads would also wait for them).

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int rh = wave >> 1;   // row half of every tile
     const int hh = wave & 1;    // head half
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
     // one workgroup per query, or (nsplit > 1, few queries) per query and split:
     // split sp takes the tiles [ntiles*sp/nsplit, ntiles*(sp+1)/nsplit) of the
     // compacted row and leaves a normalised partial O and its lse for the combine
@@ -185,14 +186,48 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     constexpr int NRND = MAXR / NT;
     const int32_t* irow = indices + (size_t)i * row_width;
     int ent[NRND];
+    if (QDMA) {
+        // The index row comes in through LDS (the list array, which the compaction
+        // then rewrites): direct-to-LDS loads of 1 KB, chunk c by wave c % NW. Q's
+        // row loads follow (wave w brings head rows 16w .. 16w+15 of the query into
+        // ring tile 1; rows past `heads` lie outside the descriptor's range and land
+        // as zeros), and one wait lets them stay in flight: a wave's loads complete
+        // in order, so at most 16 outstanding means its index chunks have landed.
+        const uint64_t ia = reinterpret_cast<uint64_t>(irow);
+        const u32x4 i_rsrc = u32x4{(uint32_t)ia, (uint32_t)(ia >> 32) & 0xFFFFu, (uint32_t)(row_width * 4),
+                                   0x00020000u};
+        const uint32_t list_lds = lds_addr(list);
+        for (int c = wave_u; 256 * c < row_width; c += NW)
+            lds_dma16_row_at<0>(i_rsrc, 16u * lane, (uint32_t)(1024 * c),
+                                __builtin_amdgcn_readfirstlane(list_lds + (uint32_t)(1024 * c)));
+        const uint64_t qa = reinterpret_cast<uint64_t>(q) + (uint64_t)i * (uint64_t)(heads * DQK * 2);
+        const u32x4 q_rsrc = u32x4{(uint32_t)qa, (uint32_t)(qa >> 32) & 0xFFFFu, (uint32_t)(heads * DQK * 2),
+                                   0x00020000u};
+        const uint32_t q_lds = lds_addr(ring) + (uint32_t)TILE_B;
 #pragma unroll
-    for (int k = 0; k < NRND; ++k) {
-        const int j = NT * k + tid;
-        ent[k] = -1;
-        if (NT * k < row_width && j < row_width) ent[k] = irow[j];
+        for (int r = 0; r < 16; ++r) {
+            const int head = 16 * wave_u + r;
+            lds_dma16_row_at<0>(q_rsrc, 16u * lane, (uint32_t)(head * DQK * 2),
+                                __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)(head * QP)));
+        }
+        wait_vm<16>();
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < NRND; ++k) {
+            const int j = NT * k + tid;
+            ent[k] = NT * k < row_width && j < row_width ? list[j] : -1;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NRND; ++k) {
+            const int j = NT * k + tid;
+            ent[k] = -1;
+            if (NT * k < row_width && j < row_width) ent[k] = irow[j];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // ---- Q: B operand of S^T = K . Q^T for this wave's 32 heads. Its loads are
+    // ---- Q: B operand of S^T = K . Q^T for this wave's 32 heads (through LDS, above,
+    // for the 512-wide latent). Otherwise its loads go straight to the registers,
     // issued after the index row's, so the compaction waits for the index row only
     // (the memory counter retires loads in order) and Q lands under the compaction
     // and the first tile's gather.
@@ -229,27 +264,11 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         for (int e = tid; e < MLA_NBUF * TILE_B / 16; e += NT)
             reinterpret_cast<uint4*>(ring)[e] = make_uint4(0u, 0u, 0u, 0u);
     }
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     unsigned long long bal[NRND];
 #pragma unroll
     for (int k = 0; k < NRND; ++k) {
         bal[k] = __ballot(ent[k] >= 0 && ent[k] < num_kv);
         if (lane == 0) rcnt[k * NW + wave] = __popcll(bal[k]);
-    }
-    if (QDMA) {
-        // (issued once the index row has landed, so that no wait for it waits for
-        // these too) wave w brings head rows 16w .. 16w+15 of the query; rows past
-        // `heads` lie outside the descriptor's range and land as zeros
-        const uint64_t qa = reinterpret_cast<uint64_t>(q) + (uint64_t)i * (uint64_t)(heads * DQK * 2);
-        const u32x4 q_rsrc = u32x4{(uint32_t)qa, (uint32_t)(qa >> 32) & 0xFFFFu, (uint32_t)(heads * DQK * 2),
-                                   0x00020000u};
-        const uint32_t q_lds = lds_addr(ring) + (uint32_t)TILE_B;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int head = 16 * wave_u + r;
-            lds_dma16_row_at<0>(q_rsrc, 16u * lane, (uint32_t)(head * DQK * 2),
-                                __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)(head * QP)));
-        }
     }
     __syncthreads();
     // The list holds, for local position p, the byte offset of its latent row plus
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // lane l copies the row's 16-byte chunk l to LDS chunk l of ring
     // row r (lanes whose chunk lies in the zero padding of a narrow latent idle)
     const uint32_t ring_lds = lds_addr(ring);
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
+    const int wave_s = wave_u;
     const uint32_t wave_lds = ring_lds + (uint32_t)row_base<RB>(RPW * wave_s);   // LDS row 16w of buffer 0
     const uint32_t lane16 = 16u * lane;   // the lane's byte offset in a gathered row
     const uint32_t rope_lds = lds_addr(rope);
@@ -936,7 +955,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             if (16 * wave + r < heads)
-                *reinterpret_cast<uint4*>(dst + r * (2 * D)) = *reinterpret_cast<const uint4*>(src + r * SPH);
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src + r * SPH),
+                                            reinterpret_cast<u32x4*>(dst + r * (2 * D)));
     }
     }
 #undef KP_STAGE
