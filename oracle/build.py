@@ -15,12 +15,13 @@ LIB = os.path.join(HERE, "libkpool_oracle.so")
 
 def build(verbose: bool = False) -> str:
     src = os.path.join(HERE, "kpool_oracle.c")
+    tmp = f"{LIB}.tmp{os.getpid()}"     # per process: parallel test workers may build at once
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", LIB + ".tmp", src, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(tmp, LIB)
     return LIB
 
 
