@@ -11,6 +11,9 @@ constexpr int MLA_TK = 64;    // latent rows per tile
 constexpr int MLA_NW = 4;     // waves per workgroup (one per SIMD)
 constexpr int MLA_NBUF = 2;   // LDS tiles in the gather ring
 constexpr int MLA_MAX_ROW = 4096;  // index-row entries the LDS list holds
+// index-row entries of the two-wave attention form (two of its workgroups share a
+// compute unit's 160 KB of LDS: a ring of two 32-row tiles and this list each)
+constexpr int MLA_W2_MAX_ROW = 2560;
 
 // LDS layout of a tile row: row r starts at byte r*(RB + 48) + 16*(r & 1) of its
 // tile (RB bytes of latent, chunks in order). gfx950 services a 16-byte LDS read

@@ -123,30 +123,34 @@ __device__ __forceinline__ void lds_dma16_lane(u32x4 rsrc, uint32_t voff, uint32
 // workgroups per query, which write fp32 partials (with SPLIT false, nsplit is 1;
 // the two epilogues are separate kernels so that neither takes registers from
 // the other).
-template <int D, int DR, bool SPLIT>
-__global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
+template <int D, int DR, bool SPLIT, bool W2>
+__global__ __launch_bounds__(W2 ? 128 : 64 * MLA_NW, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ indices,
     int num_kv, int heads, int row_width, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nsplit, float* __restrict__ o_part, float* __restrict__ lse_part) {
-    constexpr int NW = MLA_NW;
+    constexpr int NW = W2 ? 2 : MLA_NW;     // waves
+    constexpr int TK = W2 ? 32 : MLA_TK;    // latent rows per tile
     constexpr int NT = 64 * NW;             // threads
     constexpr int DP = D < 128 ? 128 : D;   // latent width in LDS (zero-padded)
     constexpr int RB = DP * 2;              // LDS bytes per latent row
     constexpr int CH = D / 8;               // 16-byte chunks a gathered row brings
     constexpr int KS = DP / 32;             // QK k-steps (32 columns each)
     constexpr int CT = DP / 16;             // 16-wide O column tiles
-    constexpr int TILE_B = MLA_TK * (RB + 48);   // bytes per LDS tile (row_base of row 64)
-    constexpr int RPW = MLA_TK / NW;        // rows each wave gathers per tile
+    constexpr int TILE_B = TK * (RB + 48);  // bytes per LDS tile (row_base of row TK)
+    constexpr int RPW = TK / NW;            // rows each wave gathers per tile
     constexpr int XB = (CT / 2) * 2 * 64 * 16;  // bytes of O one wave hands to its partner
     constexpr int DQK = D + DR;             // key (and q) width in memory
     constexpr int RK = DR / 32;             // QK k-steps over the RoPE tail
     constexpr int ROPE_RB = DR * 2;         // LDS bytes per RoPE tail row
-    constexpr int ROPE_TB = MLA_TK * ROPE_RB;
+    constexpr int ROPE_TB = TK * ROPE_RB;
     // the index list: 4096 entries, or 2048 with a RoPE tail (its top-k is at most
-    // 2048 tokens) so that the tail's LDS tiles fit
-    constexpr int MAXR = DR > 0 ? 2048 : MLA_MAX_ROW;
-    static_assert(NW == 4 && MLA_TK == 64 && RPW == 16 && CH >= 8 && CH <= 64, "tile split");
-    static_assert(4 * XB <= MLA_NBUF * TILE_B, "row-half merge fits the ring");
+    // 2048 tokens) so that the tail's LDS tiles fit, or MLA_W2_MAX_ROW for the
+    // two-wave form (two of its workgroups share a compute unit's LDS)
+    constexpr int MAXR = W2 ? MLA_W2_MAX_ROW : DR > 0 ? 2048 : MLA_MAX_ROW;
+    static_assert(RPW == 16 && CH >= 8 && CH <= 64, "tile split");
+    static_assert(W2 ? (NW == 2 && TK == 32) : (NW == 4 && TK == 64), "wave and tile shape");
+    static_assert(!W2 || (D == 512 && DR == 0 && !SPLIT), "two-wave form: 512-wide latent, whole rows");
+    static_assert(W2 || 4 * XB <= MLA_NBUF * TILE_B, "row-half merge fits the ring");
     static_assert(DR == 0 || (D == 512 && DR == 64), "RoPE tail: 512 + 64 only");
     // the interleaved step (sub-tile 0's weights under sub-tile 1's k-steps) needs
     // ten k-steps of room and no RoPE k-steps
@@ -157,19 +161,19 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // column hit distinct banks in every read pass
     constexpr bool QDMA = IL && D == 512;
     constexpr int QP = 2 * D + 32;
-    static_assert(!QDMA || 64 * QP <= TILE_B, "Q fits a ring tile");
+    static_assert(!QDMA || 64 * QP <= (W2 ? 2 : 1) * TILE_B, "Q fits its LDS region");
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
     __shared__ __align__(16) int32_t list[MAXR];   // byte offsets of the listed latent rows
-    __shared__ float mls[2][64][3];   // per row half and head: reference max, sums
-    __shared__ int rcnt[MAXR / NT * NW];   // valid entries per (round, wave) of the compaction
+    __shared__ float mls[W2 ? 1 : 2][64][3];   // per row half and head: reference max, sums
+    __shared__ int wsum[NW];          // valid entries per wave of the compaction
     __shared__ int rflag[2];          // a wave saw a score too far above its reference, by step parity
     __shared__ __align__(16) uint8_t rope[DR > 0 ? MLA_NBUF * ROPE_TB : 16];   // RoPE tail tiles
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int rh = wave >> 1;   // row half of every tile
-    const int hh = wave & 1;    // head half
+    const int rh = W2 ? 0 : wave >> 1;   // row half of every tile (the two-wave form: all rows)
+    const int hh = W2 ? wave : wave & 1; // head half
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the wave index, in a scalar register
     // one workgroup per query, or (nsplit > 1, few queries) per query and split:
     // split sp takes the tiles [ntiles*sp/nsplit, ntiles*(sp+1)/nsplit) of the
@@ -179,20 +183,22 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     const int sp = SPLIT ? (int)(blockIdx.x % ns) : 0;
 
     // ---- compact the index row (valid entries, original order) ----------------
-    // Entry NT*k + tid is read in round k; the loads of all rounds are issued
-    // together (one memory latency), each wave counts its valid entries of a
-    // round with a ballot, and one scan over the (round, wave) counts places
-    // every entry.
-    constexpr int NRND = MAXR / NT;
+    // Thread t owns the NE consecutive entries from NE*t on: it counts its valid
+    // ones, one scan over the workgroup's counts gives its first position, and it
+    // writes its valid entries from there. Every entry is read before the scan's
+    // barrier and positions only move down, so the list is rewritten in place.
+    constexpr int NE = MAXR / NT;
+    static_assert(NE % 4 == 0, "whole 16-byte groups per thread");
     const int32_t* irow = indices + (size_t)i * row_width;
-    int ent[NRND];
+    int ent[NE];
     if (QDMA) {
         // The index row comes in through LDS (the list array, which the compaction
         // then rewrites): direct-to-LDS loads of 1 KB, chunk c by wave c % NW. Q's
-        // row loads follow (wave w brings head rows 16w .. 16w+15 of the query into
-        // ring tile 1; rows past `heads` lie outside the descriptor's range and land
-        // as zeros), and one wait lets them stay in flight: a wave's loads complete
-        // in order, so at most 16 outstanding means its index chunks have landed.
+        // row loads follow (wave w brings head rows QR*w .. QR*w+QR-1 of the query
+        // into ring tile 1, or into the whole ring in the two-wave form; rows past
+        // `heads` lie outside the descriptor's range and land as zeros), and one wait
+        // lets them stay in flight: a wave's loads complete in order, so at most QR
+        // outstanding means its index chunks have landed.
         const uint64_t ia = reinterpret_cast<uint64_t>(irow);
         const u32x4 i_rsrc = u32x4{(uint32_t)ia, (uint32_t)(ia >> 32) & 0xFFFFu, (uint32_t)(row_width * 4),
                                    0x00020000u};
@@ -203,26 +209,42 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         const uint64_t qa = reinterpret_cast<uint64_t>(q) + (uint64_t)i * (uint64_t)(heads * DQK * 2);
         const u32x4 q_rsrc = u32x4{(uint32_t)qa, (uint32_t)(qa >> 32) & 0xFFFFu, (uint32_t)(heads * DQK * 2),
                                    0x00020000u};
-        const uint32_t q_lds = lds_addr(ring) + (uint32_t)TILE_B;
+        const uint32_t q_lds = lds_addr(ring) + (uint32_t)(W2 ? 0 : TILE_B);
+        constexpr int QR = 64 / NW;   // Q rows each wave brings
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int head = 16 * wave_u + r;
+        for (int r = 0; r < QR; ++r) {
+            const int head = QR * wave_u + r;
             lds_dma16_row_at<0>(q_rsrc, 16u * lane, (uint32_t)(head * DQK * 2),
                                 __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)(head * QP)));
         }
-        wait_vm<16>();
+        wait_vm<QR>();
         lds_barrier();
+        // (list entries at or past row_width hold zeros or stale values: the
+        // validity test below drops them by position)
 #pragma unroll
-        for (int k = 0; k < NRND; ++k) {
-            const int j = NT * k + tid;
-            ent[k] = NT * k < row_width && j < row_width ? list[j] : -1;
+        for (int k = 0; k < NE / 4; ++k) {
+            const int4 e4 = *reinterpret_cast<const int4*>(list + NE * tid + 4 * k);
+            ent[4 * k] = e4.x;
+            ent[4 * k + 1] = e4.y;
+            ent[4 * k + 2] = e4.z;
+            ent[4 * k + 3] = e4.w;
+        }
+    } else if ((reinterpret_cast<uintptr_t>(irow) & 15) == 0) {
+        // (row_width is a multiple of 128: a group of four is wholly in the row or past it)
+#pragma unroll
+        for (int k = 0; k < NE / 4; ++k) {
+            int4 e4 = make_int4(-1, -1, -1, -1);
+            if (NE * tid + 4 * k < row_width) e4 = *reinterpret_cast<const int4*>(irow + NE * tid + 4 * k);
+            ent[4 * k] = e4.x;
+            ent[4 * k + 1] = e4.y;
+            ent[4 * k + 2] = e4.z;
+            ent[4 * k + 3] = e4.w;
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < NRND; ++k) {
-            const int j = NT * k + tid;
-            ent[k] = -1;
-            if (NT * k < row_width && j < row_width) ent[k] = irow[j];
+        for (int k = 0; k < NE; ++k) {
+            const int j = NE * tid + k;
+            ent[k] = j < row_width ? irow[j] : -1;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -264,49 +286,50 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         for (int e = tid; e < MLA_NBUF * TILE_B / 16; e += NT)
             reinterpret_cast<uint4*>(ring)[e] = make_uint4(0u, 0u, 0u, 0u);
     }
-    unsigned long long bal[NRND];
+    // bit k: entry NE*tid + k is a row of the latent
+    uint32_t vmask = 0;
 #pragma unroll
-    for (int k = 0; k < NRND; ++k) {
-        bal[k] = __ballot(ent[k] >= 0 && ent[k] < num_kv);
-        if (lane == 0) rcnt[k * NW + wave] = __popcll(bal[k]);
-    }
+    for (int k = 0; k < NE; ++k)
+        if ((uint32_t)ent[k] < (uint32_t)num_kv && NE * tid + k < row_width) vmask |= 1u << k;
+    const int vcnt = __builtin_popcount(vmask);
+    const int vscan = wave_incl_scan(vcnt);
+    if (lane == 63) wsum[wave] = vscan;
     __syncthreads();
     // The list holds, for local position p, the byte offset of its latent row plus
     // 4096 - row_base(p % 4): entry p is loaded at immediate offset row_base(p % 4)
     // within its group of four rows, through a descriptor based 4 KB below the
     // latent (all offsets stay positive; the latent is below 4 GiB). It is padded to
-    // whole tiles with valid rows of the same list (position n + m repeats position
-    // m % n; the scores of those rows are masked), so the gather needs no bounds test.
+    // whole tiles with latent row 0 (the scores of those rows are masked), so the
+    // gather needs no bounds test.
     int n_valid;
     {
-        static_assert(NRND * NW <= 64, "one count per lane");
-        const int c = lane < NRND * NW ? rcnt[lane] : 0;
-        const int x = wave_incl_scan(c);
-        const int n_all = __builtin_amdgcn_readlane(x, 63);
-        // this workgroup's entries: [e0, e1) of the compacted row, stored from 0
-        const int nt_all = (n_all + MLA_TK - 1) / MLA_TK;
-        const int e0 = nt_all * sp / ns * MLA_TK;
-        const int e1 = min(n_all, nt_all * (sp + 1) / ns * MLA_TK);
-        n_valid = max(0, e1 - e0);
-        const int n_pad = (n_valid + MLA_TK - 1) / MLA_TK * MLA_TK - n_valid;
-        const int excl = x - c;   // entries before (round, wave) = lane's pair
+        int n_all = 0, base = vscan - vcnt;
 #pragma unroll
-        for (int k = 0; k < NRND; ++k) {
-            const int base = __builtin_amdgcn_readlane(excl, k * NW + wave_u);
-            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0u));
-            const int p = base + (int)below - e0;
-            if (ent[k] >= 0 && ent[k] < num_kv && p >= 0 && p < n_valid) {
-                const uint32_t off = (uint32_t)ent[k] * (uint32_t)(DQK * 2) + 4096u;
-                list[p] = (int32_t)(off - (uint32_t)row_base<RB>(p & 3));
-                for (int m = p; m < n_pad; m += n_valid)
-                    list[n_valid + m] = (int32_t)(off - (uint32_t)row_base<RB>((n_valid + m) & 3));
-            }
+        for (int w = 0; w < NW; ++w) {
+            const int c = wsum[w];
+            n_all += c;
+            if (w < wave_u) base += c;
         }
+        // this workgroup's entries: [e0, e1) of the compacted row, stored from 0
+        const int nt_all = (n_all + TK - 1) / TK;
+        const int e0 = nt_all * sp / ns * TK;
+        const int e1 = min(n_all, nt_all * (sp + 1) / ns * TK);
+        n_valid = max(0, e1 - e0);
+        const int n_pad = (n_valid + TK - 1) / TK * TK - n_valid;
+        int p = base - e0;
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const bool v = (vmask >> k) & 1u;
+            if (v && (uint32_t)p < (uint32_t)n_valid)
+                list[p] = (int32_t)((uint32_t)ent[k] * (uint32_t)(DQK * 2) + 4096u - (uint32_t)row_base<RB>(p & 3));
+            p += v ? 1 : 0;
+        }
+        if (tid < n_pad) list[n_valid + tid] = (int32_t)(4096u - (uint32_t)row_base<RB>((n_valid + tid) & 3));
     }
     __syncthreads();
 
     if (n_valid == 0) {
+        if (QDMA) wait_vm0();   // (Q's row loads into LDS end before the workgroup does)
         if (!SPLIT) {
             uint16_t* orow = out + (size_t)i * heads * D;
             for (int e = tid; e < heads * D; e += NT) orow[e] = 0;
@@ -318,7 +341,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         }
         return;
     }
-    const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
+    const int ntiles = (n_valid + TK - 1) / TK;
 
     // ---- gather: wave w brings tile rows 16w .. 16w+15 straight into the ring;
     // lane l copies the row's 16-byte chunk l to LDS chunk l of ring
@@ -341,7 +364,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #define KP_ROWS_OF(kt_)                                                                        \
     int rws_[RPW];   /* wave-uniform: scalar registers */                                      \
     _Pragma("unroll") for (int c4_ = 0; c4_ < RPW / 4; ++c4_) {                                \
-        const int4 rw_ = *reinterpret_cast<const int4*>(list + (kt_) * MLA_TK + RPW * wave_s + 4 * c4_); \
+        const int4 rw_ = *reinterpret_cast<const int4*>(list + (kt_) * TK + RPW * wave_s + 4 * c4_); \
         rws_[4 * c4_] = __builtin_amdgcn_readfirstlane(rw_.x);                                 \
         rws_[4 * c4_ + 1] = __builtin_amdgcn_readfirstlane(rw_.y);                             \
         rws_[4 * c4_ + 2] = __builtin_amdgcn_readfirstlane(rw_.z);                             \
@@ -369,7 +392,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #define KP_ISSUE_ROPE(kt_, m_, buf_)                                                           \
     if (DR > 0) {                                                                              \
         const int jr_ = RPW * wave + 8 * (m_) + (lane >> 3);                                   \
-        const uint32_t voff_ = (uint32_t)list[(kt_) * MLA_TK + jr_] + (uint32_t)row_base<RB>(jr_ & 3) + \
+        const uint32_t voff_ = (uint32_t)list[(kt_) * TK + jr_] + (uint32_t)row_base<RB>(jr_ & 3) + \
                                (uint32_t)(2 * D) + 16u * (uint32_t)((lane & 7) ^ rope_swz(jr_)); \
         const uint32_t m0r_ = __builtin_amdgcn_readfirstlane(                                   \
             rope_lds + (uint32_t)((buf_) * ROPE_TB + (RPW * wave_s + 8 * (m_)) * ROPE_RB));     \
@@ -513,8 +536,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
             sacc_[1][1] = mfma_bf16_16x16x32(kr1_, qr[1][c], sacc_[1][1]);                     \
         }                                                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                     \
-        if ((kt + 1) * MLA_TK > n_valid) {   /* ragged last tile: mask rows past the end */    \
-            const int rb0_ = kt * MLA_TK + 32 * rh + 8 * g;                                    \
+        if ((kt + 1) * TK > n_valid) {   /* ragged last tile: mask rows past the end */        \
+            const int rb0_ = kt * TK + 32 * rh + 8 * g;                                        \
             _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
                 _Pragma("unroll") for (int e = 0; e < 4; ++e)                                  \
                     if (rb0_ + 4 * s + e >= n_valid) {                                         \
@@ -632,8 +655,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
         const uint8_t* tb_ = ring + buf_ * TILE_B;                                             \
         const uint8_t* tbk_[2] = {tb_ + kb[0], tb_ + kb[1]};                                   \
         const uint8_t* tbv_[2] = {tb_ + vb[0], tb_ + vb[1]};                                   \
-        const bool ragged_ = (kt + 1) * MLA_TK > n_valid;                                      \
-        const int lim_ = n_valid - (kt * MLA_TK + 32 * rh + 8 * g);   /* rows 4s+e < lim_ valid */ \
+        const bool ragged_ = (kt + 1) * TK > n_valid;                                          \
+        const int lim_ = n_valid - (kt * TK + 32 * rh + 8 * g);   /* rows 4s+e < lim_ valid */  \
         f32x4 sacc_[2][2];                                                                     \
         _Pragma("unroll") for (int s = 0; s < 2; ++s)                                          \
             _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) sacc_[s][ht] = f32x4{0.f, 0.f, 0.f, 0.f}; \
@@ -705,28 +728,53 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
     // the compiler adds no wait of its own at Q's first use inside the loop, where
     // the gathers of later tiles are in flight)
     compiler_fence();
-    KP_FIRST_TILE()
-    __builtin_amdgcn_sched_barrier(0);
-    if (QDMA) {
-        // Q from LDS into the operand registers, then a barrier: every wave has its Q
-        // before the first step gathers into ring tile 1
+    if (W2) {
+        // Q fills the ring: every wave's Q rows land, each wave reads its 32 heads
+        // into the operand registers, and the ring is free for the first tile
+        wait_vm0();
+        lds_barrier();
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ht][ks] = *reinterpret_cast<const bf16x8*>(ring + (32 * hh + 16 * ht + n) * QP + 64 * ks + 16 * g);
+        lds_barrier();
+        KP_FIRST_TILE()
+    } else if (QDMA) {
+        // The first tile's rows are issued, then Q moves from LDS into the operand
+        // registers while they are in flight: the wave's Q row loads, issued before
+        // the row gathers, have landed once at most RPW loads are outstanding (a
+        // wave's loads complete in order), and a barrier makes every wave's rows
+        // visible. The second barrier publishes the first tile and frees ring tile
+        // 1 (every wave has read its Q) for the first step's gathers.
+        KP_ISSUE_TILE(0, 0)
+        wait_vm<RPW>();
+        lds_barrier();
         const uint8_t* qb = ring + TILE_B;
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qb + (32 * hh + 16 * ht + n) * QP + 64 * ks + 16 * g);
+        wait_vm0();
         lds_barrier();
+    } else {
+        KP_FIRST_TILE()
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // heads past `heads` and the columns of a zero-padded narrow latent take zero
+    // queries (a full 64-head, full-width launch has neither)
+    if (DP != D || heads < 64) {
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-        const int head = 32 * hh + 16 * ht + n;
+        for (int ht = 0; ht < 2; ++ht) {
+            const int head = 32 * hh + 16 * ht + n;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            if (!(head < heads && (DP == D || 32 * ks + 8 * g < D))) qf[ht][ks] = bf16x8{};
+            for (int ks = 0; ks < KS; ++ks)
+                if (!(head < heads && (DP == D || 32 * ks + 8 * g < D))) qf[ht][ks] = bf16x8{};
 #pragma unroll
-        for (int c = 0; c < RK; ++c)
-            if (!(head < heads)) qr[ht][c] = bf16x8{};
+            for (int c = 0; c < RK; ++c)
+                if (!(head < heads)) qr[ht][c] = bf16x8{};
+        }
     }
     // a score rose too far above its first-tile reference: the pass is dropped,
     // a sweep finds the exact max of every head, and the attention runs again with it
@@ -800,11 +848,54 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void sparse_mla_kernel(
 #undef KP_ISSUE_ROW
 #undef KP_ROWS_OF
 
+    // ---- the two-wave form: each wave finished every row of its 32 heads --------
+    // Its O is divided by the head's normaliser, rounded to bf16 and staged in the
+    // ring (free after the last step's barrier) at a pitch of SPW bytes, at which
+    // the 8-byte writes of a pass of 16 lanes (16 heads) fall in distinct banks;
+    // the wave then stores its 32 head rows of the contiguous output, one 1 KB row
+    // per instruction. No other wave reads its staged rows, so no barrier.
+    // (lane indices derived again, as below, to keep them out of the main loop)
+    if constexpr (W2) {
+        int lane_x = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        __asm__ __volatile__("" : "+v"(lane_x));
+        const int n = lane_x & 15, g = lane_x >> 4;
+        float inv[2];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const int head = 32 * wave_s + 16 * ht + n;
+            const float le = sum_over_groups(l_lse[ht]);
+            if (lse && g == 0 && head < heads)
+                lse[(size_t)i * heads + head] = (m_ref[ht] + log2f(le)) * 0.69314718055994530942f;
+            inv[ht] = 1.0f / lsum[ht][0];
+        }
+        int i_late = i;
+        __asm__ __volatile__("" : "+s"(i_late));
+        constexpr int SPW = 2 * D + 16;
+        static_assert(64 * SPW <= MLA_NBUF * TILE_B, "output staging fits the ring");
+        uint8_t* const sb = ring + (size_t)wave_s * 32 * SPW;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                bf16x4 r_;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r_[e] = (__bf16)(o[ct][ht][e] * inv[ht]);
+                *reinterpret_cast<bf16x4*>(sb + (16 * ht + n) * SPW + 2 * (16 * ct + 4 * g)) = r_;
+            }
+        uint8_t* const dst = reinterpret_cast<uint8_t*>(out + ((size_t)i_late * heads + 32 * wave_s) * D) + 16 * lane_x;
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+            if (32 * wave_s + r < heads)
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sb + r * SPW + 16 * lane_x),
+                                            reinterpret_cast<u32x4*>(dst + r * (2 * D)));
+        return;
+    }
+
     // ---- merge the two row halves and write ---------------------------------------
     // (the lane and wave indices are derived again from the lane count and the
     // scalar wave index: the values the prologue derived from the thread index would
     // otherwise stay live across the main loop, which leaves them no registers)
-    {
+    if constexpr (!W2) {
     int lane_x = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     __asm__ __volatile__("" : "+v"(lane_x));
     const int lane = lane_x, n = lane_x & 15, g = lane_x >> 4;
@@ -1062,10 +1153,14 @@ static hipError_t launch_mla_t(const uint16_t* q, const uint16_t* kv, const int3
         lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(part) + ((o + 255) & ~(size_t)255));
     }
     if (ns > 1)
-        sparse_mla_kernel<D, DR, true><<<num_q * ns, 64 * MLA_NW, 0, stream>>>(
+        sparse_mla_kernel<D, DR, true, false><<<num_q * ns, 64 * MLA_NW, 0, stream>>>(
             q, kv, indices, num_kv, heads, row_width, scale_log2, out, lse, ns, o_part, lse_part);
+    else if (D == 512 && DR == 0 && row_width <= MLA_W2_MAX_ROW)
+        // whole rows of the 512-wide latent: the two-wave form, two workgroups per CU
+        sparse_mla_kernel<512, 0, false, true><<<num_q, 128, 0, stream>>>(
+            q, kv, indices, num_kv, heads, row_width, scale_log2, out, lse, 1, nullptr, nullptr);
     else
-        sparse_mla_kernel<D, DR, false><<<num_q, 64 * MLA_NW, 0, stream>>>(
+        sparse_mla_kernel<D, DR, false, false><<<num_q, 64 * MLA_NW, 0, stream>>>(
             q, kv, indices, num_kv, heads, row_width, scale_log2, out, lse, 1, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
