@@ -97,8 +97,11 @@ __device__ __forceinline__ void lds_barrier() {
 // short rows of a causal batch spread over all of them. A bijection on
 // [0, n): the last n % (8 * MLA_XCD_RUN) workgroups keep their own index.
 #define MLA_XCD_RUN 32
+// (the two-wave attention form keeps two workgroups per CU, so an XCD holds 64
+// queries at a time: runs of 64 keep them consecutive)
+#define MLA_XCD_RUN_W2 64
+template <int R = MLA_XCD_RUN>
 __device__ __forceinline__ int xcd_query(int b, int n) {
-    constexpr int R = MLA_XCD_RUN;
     const int full = n / (8 * R) * (8 * R);
     if (b >= full) return b;
     const int slot = b >> 3, xcd = b & 7;   // slot-th workgroup that lands on this XCD

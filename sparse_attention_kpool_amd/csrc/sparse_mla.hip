@@ -179,7 +179,7 @@ __global__ __launch_bounds__(W2 ? 128 : 64 * MLA_NW, 1) void sparse_mla_kernel(
     // split sp takes the tiles [ntiles*sp/nsplit, ntiles*(sp+1)/nsplit) of the
     // compacted row and leaves a normalised partial O and its lse for the combine
     const int ns = SPLIT ? nsplit : 1;
-    const int i = SPLIT ? (int)(blockIdx.x / ns) : xcd_query(blockIdx.x, gridDim.x);
+    const int i = SPLIT ? (int)(blockIdx.x / ns) : xcd_query<W2 ? MLA_XCD_RUN_W2 : MLA_XCD_RUN>(blockIdx.x, gridDim.x);
     const int sp = SPLIT ? (int)(blockIdx.x % ns) : 0;
 
     // ---- compact the index row (valid entries, original order) ----------------
