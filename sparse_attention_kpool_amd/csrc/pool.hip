@@ -152,9 +152,19 @@ __device__ __forceinline__ void pool_vector(float (&x)[4], const uint16_t* __res
 
 // One pool per L lanes. Capacity rows (num_tokens / kpool) past the last pool
 // get pool_start -1, zero codes and a zero scale.
-template <int L, int KP>
+// LAYOUT says where the pool layout comes from:
+//   POOL_LAYOUT_READ: cu_pools in memory, written by layout_scan_kernel before;
+//   POOL_LAYOUT_ONE:  one document (cu = {0, num_tokens}): pool p starts at
+//                     token kpool*p, and no layout is read before the key rows;
+//   POOL_LAYOUT_LDS:  at most POOL_LDS_DOCS documents: every workgroup reads cu
+//                     and scans the pool counts in LDS.
+// With ONE and LDS, workgroup 0 also writes cu_pools (the launch is the whole
+// of the layout and pooling).
+enum { POOL_LAYOUT_READ = 0, POOL_LAYOUT_ONE = 1, POOL_LAYOUT_LDS = 2 };
+constexpr int POOL_LDS_DOCS = 1024;
+template <int L, int KP, int LAYOUT>
 __global__ __launch_bounds__(256) void pool_keys_kernel(
-    const int32_t* __restrict__ cu, int num_docs, const int32_t* __restrict__ cu_pools,
+    const int32_t* __restrict__ cu, int num_docs, int num_tokens, int32_t* __restrict__ cu_pools,
     const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ gate,
     const float* __restrict__ ape, int kpool, int pool_cap, float norm,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ k8, float* __restrict__ ks,
@@ -163,17 +173,62 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
     const int lane = threadIdx.x & 63;
     const int j = lane % L;
     const int p = p_base + (int)((blockIdx.x * blockDim.x + threadIdx.x) / L);
-    if (p >= pool_cap) return;
-    const int total = cu_pools[num_docs];
+    int total, d = 0, s;
+    if constexpr (LAYOUT == POOL_LAYOUT_ONE) {
+        total = num_tokens / kpool;
+        if (blockIdx.x == 0 && threadIdx.x == 0) { cu_pools[0] = 0; cu_pools[1] = total; }
+        if (p >= pool_cap) return;
+        s = kpool * p;
+    } else if constexpr (LAYOUT == POOL_LAYOUT_LDS) {
+        // cu into LDS, then an exclusive scan of floor(length / kpool): thread t
+        // owns documents 4t .. 4t+3
+        __shared__ int scu[POOL_LDS_DOCS + 1], scp[POOL_LDS_DOCS + 1];
+        __shared__ int wtot[4];
+        const int tid = threadIdx.x;
+        for (int e = tid; e <= num_docs; e += 256) scu[e] = cu[e];
+        __syncthreads();
+        int cnt[4], sum = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int dd = 4 * tid + k;
+            cnt[k] = dd < num_docs ? (scu[dd + 1] - scu[dd]) / kpool : 0;
+            sum += cnt[k];
+        }
+        const int incl = wave_incl_scan(sum);
+        if (lane == 63) wtot[tid >> 6] = incl;
+        __syncthreads();
+        int run = incl - sum;
+        for (int w = 0; w < (tid >> 6); ++w) run += wtot[w];
+        if (tid == 0) scp[0] = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            run += cnt[k];
+            if (4 * tid + k < num_docs) scp[4 * tid + k + 1] = run;
+        }
+        __syncthreads();
+        if (blockIdx.x == 0)
+            for (int e = tid; e <= num_docs; e += 256) cu_pools[e] = scp[e];
+        if (p >= pool_cap) return;
+        total = scp[num_docs];
+        if (p < total) {
+            // document of pool p: the d with cu_pools[d] <= p < cu_pools[d+1]
+            d = find_doc(scp, num_docs, p);
+            s = scu[d] + kpool * (p - scp[d]);
+        }
+    } else {
+        if (p >= pool_cap) return;
+        total = cu_pools[num_docs];
+        if (p < total) {
+            d = find_doc(cu_pools, num_docs, p);
+            s = cu[d] + kpool * (p - cu_pools[d]);
+        }
+    }
     if (p >= total) {
         if (j == 0) { pool_start[p] = -1; ks[p] = 0.0f; }
         reinterpret_cast<uint32_t*>(k8 + (size_t)p * N)[j] = 0u;
         if (kf32) reinterpret_cast<float4*>(kf32 + (size_t)p * N)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
-    // document of pool p: the d with cu_pools[d] <= p < cu_pools[d+1]
-    int d = find_doc(cu_pools, num_docs, p);
-    const int s = cu[d] + kpool * (p - cu_pools[d]);
     if (s + kpool - 1 < token_lo) return;   // a pool of the caller's cache
 
     float x[4];
@@ -268,37 +323,47 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const uint16_t* __res
 }
 
 // ------------------------------------------------------------ launchers -----
-template <int KP>
+template <int KP, int LAYOUT>
 static void launch_pool_keys(int blocks, hipStream_t stream, int d_idx, const int32_t* cu, int num_docs,
-                             const int32_t* cu_pools, const uint16_t* k_idx, const uint16_t* gate,
+                             int num_tokens, int32_t* cu_pools, const uint16_t* k_idx, const uint16_t* gate,
                              const float* ape, int kpool, int pool_cap, float norm, int32_t* pool_start,
                              uint8_t* k8, float* ks, float* kf32, int p_base, int token_lo) {
+#define KP_POOL_ARGS cu, num_docs, num_tokens, cu_pools, k_idx, gate, ape, kpool, pool_cap, norm, pool_start, k8, ks, \
+                     kf32, p_base, token_lo
     switch (d_idx) {
-        case 32:
-            pool_keys_kernel<8, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
-                                                            pool_cap, norm, pool_start, k8, ks, kf32, p_base,
-                                                            token_lo);
-            break;
-        case 64:
-            pool_keys_kernel<16, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
-                                                             pool_cap, norm, pool_start, k8, ks, kf32, p_base,
-                                                            token_lo);
-            break;
-        default:
-            pool_keys_kernel<32, KP><<<blocks, 256, 0, stream>>>(cu, num_docs, cu_pools, k_idx, gate, ape, kpool,
-                                                             pool_cap, norm, pool_start, k8, ks, kf32, p_base,
-                                                            token_lo);
-            break;
+        case 32: pool_keys_kernel<8, KP, LAYOUT><<<blocks, 256, 0, stream>>>(KP_POOL_ARGS); break;
+        case 64: pool_keys_kernel<16, KP, LAYOUT><<<blocks, 256, 0, stream>>>(KP_POOL_ARGS); break;
+        default: pool_keys_kernel<32, KP, LAYOUT><<<blocks, 256, 0, stream>>>(KP_POOL_ARGS); break;
     }
+#undef KP_POOL_ARGS
+}
+
+template <int LAYOUT>
+static void launch_pool_keys_kp(int blocks, hipStream_t stream, int d_idx, const int32_t* cu, int num_docs,
+                                int num_tokens, int32_t* cu_pools, const uint16_t* k_idx, const uint16_t* gate,
+                                const float* ape, int kpool, int pool_cap, float norm, int32_t* pool_start,
+                                uint8_t* k8, float* ks, float* kf32, int p_base, int token_lo) {
+    if (kpool == 4)
+        launch_pool_keys<4, LAYOUT>(blocks, stream, d_idx, cu, num_docs, num_tokens, cu_pools, k_idx, gate, ape,
+                                    kpool, pool_cap, norm, pool_start, k8, ks, kf32, p_base, token_lo);
+    else
+        launch_pool_keys<0, LAYOUT>(blocks, stream, d_idx, cu, num_docs, num_tokens, cu_pools, k_idx, gate, ape,
+                                    kpool, pool_cap, norm, pool_start, k8, ks, kf32, p_base, token_lo);
 }
 
 hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, const uint16_t* k_idx,
                               const uint16_t* gate, const float* ape, int d_idx, int kpool,
                               float norm, int32_t* cu_pools, int32_t* pool_start, uint8_t* k8,
                               float* ks, float* kf32, int token_lo, hipStream_t stream) {
-    layout_scan_kernel<<<1, 1024, 0, stream>>>(cu, num_docs, kpool, cu_pools);
     const int pool_cap = num_tokens / kpool;
-    if (pool_cap == 0) return hipGetLastError();
+    // (one launch does the layout and the pooling when the documents fit the
+    // in-workgroup scan; a row of more documents scans them first, in its own launch)
+    const int layout = num_docs == 1 ? POOL_LAYOUT_ONE : num_docs <= POOL_LDS_DOCS ? POOL_LAYOUT_LDS
+                                                                                  : POOL_LAYOUT_READ;
+    if (layout == POOL_LAYOUT_READ || pool_cap == 0) {
+        layout_scan_kernel<<<1, 1024, 0, stream>>>(cu, num_docs, kpool, cu_pools);
+        if (pool_cap == 0) return hipGetLastError();
+    }
     // With token_lo > 0 only pools ending at or after token_lo (and the rows past
     // the last pool) are written. Every such pool has a global number of at least
     // (token_lo - (kpool-1) - num_docs*(kpool-1)) / kpool, since each document
@@ -313,12 +378,13 @@ hipError_t launch_layout_pool(const int32_t* cu, int num_docs, int num_tokens, c
     const int L = d_idx / 4;
     const long long threads = (long long)(pool_cap - p_base) * L;
     const int blocks = (int)((threads + 255) / 256);
-    if (kpool == 4)
-        launch_pool_keys<4>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
-                            norm, pool_start, k8, ks, kf32, p_base, token_lo);
-    else
-        launch_pool_keys<0>(blocks, stream, d_idx, cu, num_docs, cu_pools, k_idx, gate, ape, kpool, pool_cap,
-                            norm, pool_start, k8, ks, kf32, p_base, token_lo);
+#define KP_POOL_LAUNCH(LAYOUT_)                                                                      \
+    launch_pool_keys_kp<LAYOUT_>(blocks, stream, d_idx, cu, num_docs, num_tokens, cu_pools, k_idx, gate, ape, \
+                                 kpool, pool_cap, norm, pool_start, k8, ks, kf32, p_base, token_lo)
+    if (layout == POOL_LAYOUT_ONE) KP_POOL_LAUNCH(POOL_LAYOUT_ONE);
+    else if (layout == POOL_LAYOUT_LDS) KP_POOL_LAUNCH(POOL_LAYOUT_LDS);
+    else KP_POOL_LAUNCH(POOL_LAYOUT_READ);
+#undef KP_POOL_LAUNCH
     return hipGetLastError();
 }
 

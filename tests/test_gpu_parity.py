@@ -78,6 +78,38 @@ def test_pooled_keys(K, oracle_mod, name):
     assert np.allclose(host(ks)[:P], kscale, rtol=1e-5)
 
 
+@pytest.mark.parametrize("ndocs,seed", [(1, 11), (1024, 12), (1025, 13), (3000, 14), (1024, 15)])
+def test_layout_and_keys_many_documents(K, oracle_mod, ndocs, seed):
+    """Rows of one document (layout known on the host), of up to 1,024 documents
+    (layout scanned inside the pooling launch) and of more (a separate layout
+    scan first): layout bit-exact and pooled keys as the oracle computes them.
+    Seed 15 gives a quarter of the 1,024 documents no tokens."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, 14, size=ndocs)
+    if seed == 15:
+        lens[rng.random(ndocs) < 0.25] = 0
+        lens[0] += 1
+    cu = np.array([0, *np.cumsum(lens).tolist()], np.int32)
+    T = int(cu[-1])
+    _log("many documents", ndocs, "T", T)
+    s = custom("many", T, cu, D_I=32)
+    wl = Workload(s)
+    cp, ps, k8, ks, kf = K.kpool_build(dev(cu), dev_bf16(wl.full("k_idx")), dev_bf16(wl.full("gate")),
+                                       dev(wl.ape()), 4, with_f32=True)
+    want_cp, want_ps = oracle_mod.layout(cu, T, 4)
+    assert host(cp).tolist() == want_cp.tolist()
+    got_ps = host(ps)
+    P = len(want_ps)
+    assert got_ps[:P].tolist() == want_ps.tolist()
+    assert np.all(got_ps[P:] == -1)
+    kc, kscale, pooled = oracle_mod.keys(wl.full("k_idx"), wl.full("gate"), wl.ape(), want_ps, 4)
+    g_pooled = host(kf)[:P]
+    assert np.all(np.abs(g_pooled - pooled) <= 1e-5 * np.abs(pooled) + 1e-6)
+    check_key_codes(host(k8)[:P], kc, "many%d" % ndocs)
+    assert np.allclose(host(ks)[:P], kscale, rtol=1e-5)
+    assert np.all(host(ks)[P:] == 0) and np.all(host(k8)[P:] == 0)
+
+
 @pytest.mark.parametrize("name", ["tiny", "2k", "packed4k"])
 def test_pooled_keys_from_token(K, name):
     """kpool_build_from rebuilds exactly the pools that end at or after token_lo
