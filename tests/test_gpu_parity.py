@@ -368,7 +368,7 @@ def test_mla_fed_oracle_rows(K, oracle_mod, name):
 
 @pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("case", ["scattered_mask", "empty_rows", "single", "duplicates", "heads40",
-                                  "rising", "rising_tail", "max_width"])
+                                  "rising", "rising_tail", "max_width", "w2_width", "above_w2_width"])
 def test_mla_edge_rows(K, oracle_mod, case, split):
     """Edge rows of the attention. "rising" and "rising_tail" put rows whose
     scores lie hundreds of log2 units above those of the first tile after it
@@ -383,6 +383,10 @@ def test_mla_edge_rows(K, oracle_mod, case, split):
         H = 40
     if case == "max_width":   # the widest index row the attention accepts: 64 tiles of rows
         W, Tq = 4096, 3
+    if case == "w2_width":    # the widest row of the two-wave form (its LDS list), whole rows
+        W, Tq = 2560, 3
+    if case == "above_w2_width":   # one 128-entry step wider: the four-wave form takes it
+        W, Tq = 2688, 3
     q = (rng.standard_normal((Tq, H, D))).astype(np.float32)
     kv = (rng.standard_normal((N, D))).astype(np.float32)
     if case.startswith("rising"):
@@ -406,7 +410,8 @@ def test_mla_edge_rows(K, oracle_mod, case, split):
         idx[np.arange(Tq), rng.integers(0, W, Tq)] = rng.integers(0, N, Tq)
     if case == "duplicates":
         idx[:, 100:] = idx[:, :W - 100][:, :W - 100]
-    if case == "max_width":   # row 0 full; rows 1, 2 with masked entries spread over the row
+    if case in ("max_width", "w2_width", "above_w2_width"):
+        # row 0 full; rows 1, 2 with masked entries spread over the row
         idx[1:][rng.random((Tq - 1, W)) < 0.3] = -1
         idx[2, W - 50:] = -1
     _log("mla edge", case, "split" if split else "whole rows")
