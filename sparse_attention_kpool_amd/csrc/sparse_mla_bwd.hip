@@ -43,6 +43,7 @@
 namespace kp {
 
 constexpr int BW_COEF = 128;   // coefficients per slot: scale*ds and p of 64 heads
+constexpr int BW_RING = 4;     // LDS operand fragments in flight ahead of the MFMAs that use them
 
 // Slot stride of the coefficient workspace rows: the index row width rounded
 // up to whole 64-slot tiles.
@@ -242,15 +243,24 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
             sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
             pacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // K fragment u (k-step u / 4, sub-tile u % 4) is read BW_RING - 1 fragments
+        // ahead of its two MFMAs; scheduling barriers keep that order (left alone, the
+        // compiler reads each fragment right before its MFMAs and waits for it there)
+        bf16x8 kr[BW_RING];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int u = 0; u < BW_RING - 1; ++u) kr[u] = *reinterpret_cast<const bf16x8*>(tb + kb[u & 3] + 64 * (u >> 2));
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tb + kb[s] + 64 * ks);
-                sacc[s] = mfma_bf16_16x16x32(kf, qf[ks], sacc[s]);
-                pacc[s] = mfma_bf16_16x16x32(kf, gf[ks], pacc[s]);
+        for (int u = 0; u < 4 * KS; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (u + BW_RING - 1 < 4 * KS) {
+                const int un = u + BW_RING - 1;
+                kr[un % BW_RING] = *reinterpret_cast<const bf16x8*>(tb + kb[un & 3] + 64 * (un >> 2));
             }
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[u & 3] = mfma_bf16_16x16x32(kr[u % BW_RING], qf[u >> 2], sacc[u & 3]);
+            pacc[u & 3] = mfma_bf16_16x16x32(kr[u % BW_RING], gf[u >> 2], pacc[u & 3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
         // p and scale*ds of the lane's rows; rows past the list's end (and heads past
         // `heads`) get zero
         bf16x8 dsb[2], pb[2];
@@ -274,16 +284,26 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
             *reinterpret_cast<bf16x8*>(crow_ds + slot) = dsb[kk];
             *reinterpret_cast<bf16x8*>(crow_p + slot) = pb[kk];
         }
-        // dQ^T[cols, heads] += K^T[cols, rows] . (scale ds)^T[rows, heads]
+        // dQ^T[cols, heads] += K^T[cols, rows] . (scale ds)^T[rows, heads]; the K^T
+        // fragment of step u (k-step u / CT, column tile u % CT) is read BW_RING - 1
+        // steps ahead of its MFMA
+        auto ktr = [&](int u) __attribute__((always_inline)) {
+            const int kk = u / CT, ct = u % CT;
+            const bf16x4 v0 = lds_read_tr16(tb + vb[kk][0] + 32 * ct);
+            const bf16x4 v1 = lds_read_tr16(tb + vb[kk][1] + 32 * ct);
+            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 vr[BW_RING];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int u = 0; u < BW_RING - 1; ++u) vr[u] = ktr(u);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const bf16x4 v0 = lds_read_tr16(tb + vb[kk][0] + 32 * ct);
-                const bf16x4 v1 = lds_read_tr16(tb + vb[kk][1] + 32 * ct);
-                acc[ct] = mfma_bf16_16x16x32(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kk],
-                                             acc[ct]);
-            }
+        for (int u = 0; u < 2 * CT; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (u + BW_RING - 1 < 2 * CT) vr[(u + BW_RING - 1) % BW_RING] = ktr(u + BW_RING - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[u % CT] = mfma_bf16_16x16x32(vr[u % BW_RING], dsb[u / CT], acc[u % CT]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // the next tile's rows have landed: every vector-memory operation but the
         // four coefficient stores issued after them is done (s_waitcnt vmcnt(4); the
         // counter retires in issue order): the stores may stay in flight across
