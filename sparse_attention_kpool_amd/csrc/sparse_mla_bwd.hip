@@ -361,6 +361,13 @@ constexpr int BW_QC = 2048;   // queries per chunk
 __device__ __forceinline__ constexpr int coef_row(int r) { return r * 176 + 16 * (r & 1); }
 constexpr int BW_CTILE_B = 128 * 176;   // bytes per coefficient tile
 
+// two floats rounded to bf16 (nearest even), the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const int32_t* __restrict__ indices,
@@ -373,7 +380,8 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
     constexpr int CTW = CW / 16;            // 16-wide column tiles per wave
     constexpr int XB = 64 * (RB + 48);      // bytes of one staged operand (64 heads)
 
-    __shared__ __align__(16) uint8_t xs[XB > MLA_NBUF * BW_CTILE_B ? XB : MLA_NBUF * BW_CTILE_B];
+    constexpr int CBUF = 3;                 // coefficient tiles in the LDS ring
+    __shared__ __align__(16) uint8_t xs[XB > CBUF * BW_CTILE_B ? XB : CBUF * BW_CTILE_B];
     __shared__ __align__(16) int32_t list[MLA_MAX_ROW];
     __shared__ __align__(16) int32_t jpos[MLA_MAX_ROW];
     __shared__ int rcnt[64];
@@ -390,33 +398,60 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
 
     // A operands of dKV^T[cols, slots] = X^T[cols, coefs] . coef[coefs, slots] with X =
     // [Q; dO] (coefficients 0..63: Q of head c, 64..127: dO of head c - 64): lane (g, n)
-    // of k-step kk holds coefficients 32*kk + 8*g .. +7 of column 16*ct + n of the
-    // wave's columns. Q, then dO + scale (delta_used - delta) Q (rounded to bf16),
+    // of k-step kk holds coefficients 32*kk + 8*g .. +7 of column
+    // 32*(ct/2) + 8*(n/4) + 4*(ct%2) + n%4 of the wave's columns. Over a pair of
+    // column tiles, lane (g, n) of the products then holds the 8 consecutive
+    // columns 32*(ct/2) + 8*g .. +7 of its slot: one 16-byte store. Q, then dO + scale (delta_used - delta) Q (rounded to bf16),
     // is staged in LDS (head h at row_base(h)) and read with the transposing read.
+    // The coefficient tile 0 and every Q and dO chunk this thread stages are
+    // loaded first, all in flight together; head h's scale (delta_used - delta)
+    // comes with them.
+    constexpr int XC = 64 * (DP / 8) / NT;   // 16-byte chunks of Q (and of dO) per thread
+    static_assert(XC * NT == 64 * (DP / 8), "whole chunks per thread");
+    const uint16_t* crow = coef + (size_t)i * BW_COEF * wc;
+    const int cr = tid >> 1, chalf = tid & 1;
+    u32x4 cpre[4];
+    auto load_tile = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            cpre[u] = *reinterpret_cast<const u32x4*>(crow + (size_t)cr * wc + kt * MLA_TK + 32 * chalf + 8 * u);
+    };
+    load_tile(0);
+    uint4 qv[XC], gv[XC];
+    float sc[XC];
+    {
+        const uint16_t* qq = q + (size_t)i * heads * D;
+        const uint16_t* gg = dout + (size_t)i * heads * D;
+#pragma unroll
+        for (int u = 0; u < XC; ++u) {
+            // 64 rows (heads) x DP columns; heads past `heads` and padded columns are zero
+            const int c = tid + NT * u, h = c / (DP / 8), col = 8 * (c % (DP / 8));
+            qv[u] = gv[u] = make_uint4(0u, 0u, 0u, 0u);
+            sc[u] = 0.f;
+            if (h < heads && col < D) {
+                qv[u] = *reinterpret_cast<const uint4*>(qq + (size_t)h * D + col);
+                gv[u] = *reinterpret_cast<const uint4*>(gg + (size_t)h * D + col);
+                sc[u] = scale * dcorr[(size_t)i * 64 + h];
+            }
+        }
+    }
     bf16x8 xf[4][CTW];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        const uint16_t* qq = q + (size_t)i * heads * D;
-        const uint16_t* gg = dout + (size_t)i * heads * D;
-        // 64 rows (heads) x DP columns; heads past `heads` and padded columns are zero
-        for (int c = tid; c < 64 * (DP / 8); c += NT) {
-            const int h = c / (DP / 8), col = 8 * (c % (DP / 8));
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (h < heads && col < D) {
-                v = *reinterpret_cast<const uint4*>(qq + (size_t)h * D + col);
-                if (half == 1) {
-                    const uint4 gv = *reinterpret_cast<const uint4*>(gg + (size_t)h * D + col);
-                    const float sc = scale * dcorr[(size_t)i * 64 + h];
-                    const uint32_t qw[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
-                    uint32_t ow[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t lo = f32_to_bf16_rne(__builtin_fmaf(sc, bf16_lo(qw[u]), bf16_lo(gw[u])));
-                        const uint32_t hi = f32_to_bf16_rne(__builtin_fmaf(sc, bf16_hi(qw[u]), bf16_hi(gw[u])));
-                        ow[u] = lo | (hi << 16);
-                    }
-                    v = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        for (int u = 0; u < XC; ++u) {
+            const int c = tid + NT * u, h = c / (DP / 8), col = 8 * (c % (DP / 8));
+            uint4 v = qv[u];
+            if (half == 1) {
+                const uint32_t qw[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+                uint32_t ow[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = f32_to_bf16_rne(__builtin_fmaf(sc[u], bf16_lo(qw[e]), bf16_lo(gw[e])));
+                    const uint32_t hi = f32_to_bf16_rne(__builtin_fmaf(sc[u], bf16_hi(qw[e]), bf16_hi(gw[e])));
+                    ow[e] = lo | (hi << 16);
                 }
+                v = make_uint4(ow[0], ow[1], ow[2], ow[3]);
             }
             *reinterpret_cast<uint4*>(xs + row_base<RB>(h) + 2 * col) = v;
         }
@@ -425,7 +460,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
         for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
             for (int ct = 0; ct < CTW; ++ct) {
-                const int colb = 2 * (CW * wave + 16 * ct) + 8 * q4;
+                const int colb = 2 * CW * wave + 64 * (ct >> 1) + 16 * q4 + 8 * (ct & 1);
                 const bf16x4 v0 = lds_read_tr16(xs + row_base<RB>(32 * kq + 8 * g + e4) + colb);
                 const bf16x4 v1 = lds_read_tr16(xs + row_base<RB>(32 * kq + 8 * g + 4 + e4) + colb);
                 xf[2 * half + kq][ct] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -433,28 +468,20 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
         __syncthreads();
     }
 
-    // coefficient tiles (128 rows x 64 slots of bf16) through an LDS double buffer:
-    // thread t copies 64 bytes of row t/2; the next tile's loads are issued before
-    // the current tile's MFMAs
-    const uint16_t* crow = coef + (size_t)i * BW_COEF * wc;
-    const int cr = tid >> 1, chalf = tid & 1;
-    uint4 cpre[4];
-    auto load_tile = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            cpre[u] = *reinterpret_cast<const uint4*>(crow + (size_t)cr * wc + kt * MLA_TK + 32 * chalf + 8 * u);
-    };
+    // coefficient tiles (128 rows x 64 slots of bf16) through a ring of CBUF LDS
+    // tiles: thread t copies 64 bytes of row t/2; the next tile's loads are issued
+    // before the current tile's MFMAs
     auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<uint4*>(xs + buf * BW_CTILE_B + coef_row(cr) + 64 * chalf + 16 * u) = cpre[u];
+            *reinterpret_cast<u32x4*>(xs + buf * BW_CTILE_B + coef_row(cr) + 64 * chalf + 16 * u) = cpre[u];
     };
-    uint16_t* part_q = part + (size_t)i * row_width * D;
-    load_tile(0);
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        part + (size_t)i * row_width * D, 0, 2 * row_width * D, 0x00020000);
     store_tile(0);
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
+        const int buf = kt % CBUF;
         if (kt + 1 < ntiles) load_tile(kt + 1);
         const uint8_t* tb = xs + buf * BW_CTILE_B;
 #pragma unroll
@@ -467,27 +494,35 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
                 const bf16x4 v1 = lds_read_tr16(tb + coef_row(32 * kk + 8 * g + 4 + e4) + 32 * rt + 8 * q4);
                 bf[kk] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            // lane (g, n) gets slot 16*rt + n, columns CW*wave + 16*ct + 4*g .. +3
+            // lane (g, n) gets slot 16*rt + n, columns CW*wave + 32*p + 8*g .. +7 from the
+            // column tiles 2p and 2p + 1. Each column tile has its own accumulator, so the
+            // products run back to back; the stores are unconditional buffer stores (a
+            // fixed count per tile, so the wait for the next coefficient tile does not
+            // cover them), and a slot past the valid ones gets an offset beyond the
+            // buffer, which drops it.
             const int slot = kt * MLA_TK + 16 * rt + n;
-            uint16_t* prow = part_q + (size_t)jpos[slot < n_valid ? slot : 0] * D + CW * wave + 4 * g;
+            const uint32_t voff = slot < n_valid ? 2u * (uint32_t)(jpos[slot] * D + CW * wave + 8 * g) : 0x80000000u;
+            f32x4 r[CTW];
 #pragma unroll
             for (int ct = 0; ct < CTW; ++ct) {
-                f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+                r[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) r = mfma_bf16_16x16x32(xf[kk][ct], bf[kk], r);
-                if (slot < n_valid && (DP == D || CW * wave + 16 * ct < D)) {
-                    bf16x4 o;
+                for (int kk = 0; kk < 4; ++kk) r[ct] = mfma_bf16_16x16x32(xf[kk][ct], bf[kk], r[ct]);
+            }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = (__bf16)r[e];
-                    *reinterpret_cast<bf16x4*>(prow + 16 * ct) = o;
+            for (int pt = 0; pt < CTW / 2; ++pt) {
+                if (DP == D || CW * wave + 32 * pt < D) {
+                    const f32x4 lo = r[2 * pt], hi = r[2 * pt + 1];
+                    const u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                     pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(o, prs, voff, 64 * pt, 0);
                 }
             }
         }
+        // tile kt + 1 goes to the ring slot last read in tile kt - 2: every wave has
+        // passed the barrier that ended tile kt - 1 since, so one barrier per tile
+        if (kt + 1 < ntiles) store_tile((kt + 1) % CBUF);
         __syncthreads();
-        if (kt + 1 < ntiles) {
-            store_tile(buf ^ 1);
-            __syncthreads();
-        }
     }
 }
 
