@@ -106,23 +106,25 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
     constexpr int RB = DP * 2;
     constexpr int CH = D / 8;               // 16-byte chunks a gathered row brings
     constexpr int KS = DP / 32;             // QK k-steps
-    constexpr int CT = DP / 16;             // dQ column tiles
     constexpr int TILE_B = MLA_TK * (RB + 48);
     constexpr int RPW = MLA_TK / MLA_NW;
+
+    constexpr int CQ = DP / 64;             // dQ column tiles per wave
+    constexpr int DSP = 144;                // bytes per head in the ds exchange (64 slots + pad)
 
     __shared__ __align__(16) uint8_t ring[MLA_NBUF * TILE_B];
     __shared__ __align__(16) int32_t list[MLA_MAX_ROW];
     __shared__ int rcnt[64];
+    __shared__ __align__(16) uint8_t dsx[64 * DSP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int head = 16 * wave + n;        // this lane's head
+    const int head = 16 * wave + n;        // this lane's head in the S, dP and ds steps
     const bool head_ok = head < heads;
     const int i = xcd_query(blockIdx.x, gridDim.x);
     const int wc = bwd_coef_stride(row_width);
 
     const int n_valid = bwd_compact(indices + (size_t)i * row_width, row_width, num_kv, list, rcnt);
-    uint16_t* dq_row = dq + ((size_t)i * heads + (head_ok ? head : 0)) * D;
     if (n_valid == 0) {
         for (int e = tid; e < heads * D; e += NT) dq[(size_t)i * heads * D + e] = 0;
         return;
@@ -212,18 +214,23 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
     int kb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) kb[s] = row_base<RB>(32 * (s >> 1) + 8 * (n >> 2) + 4 * (s & 1) + (n & 3)) + 16 * g;
-    // K^T A operand of dQ column tile ct, k-step kk: two transposing reads of rows
-    // 32*kk + 8*g + 4*b + e4, columns 16*ct + 4*q4 .. +3: byte offset vb[kk][b] + 32*ct
+    // K^T A operand of the wave's dQ column tile ct (columns DP/4*wave + 16*ct ..
+    // +15), k-step kk: two transposing reads of rows 32*kk + 8*g + 4*b + e4, columns
+    // DP/4*wave + 16*ct + 4*q4 .. +3: byte offset vb[kk][b] + 32*ct
     const int e4 = (lane >> 2) & 3, q4 = lane & 3;
     int vb[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) vb[kk][b] = row_base<RB>(32 * kk + 8 * g + 4 * b + e4) + 8 * q4;
+        for (int b = 0; b < 2; ++b) vb[kk][b] = row_base<RB>(32 * kk + 8 * g + 4 * b + e4) + 8 * q4 + DP / 2 * wave;
 
-    f32x4 acc[CT];
+    // dQ^T of the wave's DP/4 columns for all 64 heads: acc[ht][ct] holds columns
+    // DP/4*wave + 16*ct + 4*g .. +3 of head 16*ht + n
+    f32x4 acc[4][CQ];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int ct = 0; ct < CQ; ++ct) acc[ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dsum = 0.f;   // sum of p_j dp_j over the lane's rows
     uint16_t* crow_ds = coef + ((size_t)i * BW_COEF + head) * wc;        // this lane's scale*ds row
     uint16_t* crow_p = coef + ((size_t)i * BW_COEF + 64 + head) * wc;    // and its p row
@@ -284,24 +291,39 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
             *reinterpret_cast<bf16x8*>(crow_ds + slot) = dsb[kk];
             *reinterpret_cast<bf16x8*>(crow_p + slot) = pb[kk];
         }
-        // dQ^T[cols, heads] += K^T[cols, rows] . (scale ds)^T[rows, heads]; the K^T
-        // fragment of step u (k-step u / CT, column tile u % CT) is read BW_RING - 1
-        // steps ahead of its MFMA
+        // dQ^T[cols, heads] += K^T[cols, rows] . (scale ds)^T[rows, heads], the columns
+        // split over the waves: each wave's ds (its 16 heads) goes through LDS, so
+        // that a K^T fragment, read once, feeds the four head tiles. The K^T
+        // fragment of step u (k-step u / CQ, column tile u % CQ) is read BW_RING - 1
+        // steps ahead of its MFMAs.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            *reinterpret_cast<bf16x8*>(dsx + head * DSP + 2 * (32 * kk + 8 * g)) = dsb[kk];
+        lds_barrier();
+        bf16x8 dsf[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+                dsf[kk][ht] = *reinterpret_cast<const bf16x8*>(dsx + (16 * ht + n) * DSP + 2 * (32 * kk + 8 * g));
         auto ktr = [&](int u) __attribute__((always_inline)) {
-            const int kk = u / CT, ct = u % CT;
+            const int kk = u / CQ, ct = u % CQ;
             const bf16x4 v0 = lds_read_tr16(tb + vb[kk][0] + 32 * ct);
             const bf16x4 v1 = lds_read_tr16(tb + vb[kk][1] + 32 * ct);
             return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        bf16x8 vr[BW_RING];
+        constexpr int NU = 2 * CQ, RA = NU < BW_RING ? NU : BW_RING;
+        bf16x8 vr[RA];
 #pragma unroll
-        for (int u = 0; u < BW_RING - 1; ++u) vr[u] = ktr(u);
+        for (int u = 0; u < RA - 1; ++u) vr[u] = ktr(u);
 #pragma unroll
-        for (int u = 0; u < 2 * CT; ++u) {
+        for (int u = 0; u < NU; ++u) {
             __builtin_amdgcn_sched_barrier(0);
-            if (u + BW_RING - 1 < 2 * CT) vr[(u + BW_RING - 1) % BW_RING] = ktr(u + BW_RING - 1);
+            if (u + RA - 1 < NU) vr[(u + RA - 1) % RA] = ktr(u + RA - 1);
             __builtin_amdgcn_sched_barrier(0);
-            acc[u % CT] = mfma_bf16_16x16x32(vr[u % BW_RING], dsb[u / CT], acc[u % CT]);
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+                acc[ht][u % CQ] = mfma_bf16_16x16x32(vr[u % RA], dsf[u / CQ][ht], acc[ht][u % CQ]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the next tile's rows have landed: every vector-memory operation but the
@@ -314,25 +336,36 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
 #undef BW_ROWS_OF
 #undef BW_ISSUE_ROW
     // the exact delta of the lane's head (its four lane groups hold a quarter of
-    // the rows each) and the correction of dQ: + scale (delta_used - delta) O
+    // the rows each) and the correction of dQ: + scale (delta_used - delta) O, each
+    // head's correction passed to the waves that hold its columns through LDS
     dsum += shfl_xor(dsum, 16);
     dsum += shfl_xor(dsum, 32);
-    const float corr = delta - dsum;
-    if (g == 0) dcorr[(size_t)i * 64 + 16 * wave + n] = head_ok ? corr : 0.f;
-    // dQ: lane (g, n) holds columns 16*ct + 4*g .. +3 of its head
-    if (head_ok) {
-        const uint16_t* o_row = o + ((size_t)i * heads + head) * D;
-        const float sc = scale * corr;
+    const float corr = head_ok ? delta - dsum : 0.f;
+    float* corr_s = reinterpret_cast<float*>(dsx);   // the exchange buffer is free now
+    if (g == 0) {
+        dcorr[(size_t)i * 64 + head] = corr;
+        corr_s[head] = corr;
+    }
+    __syncthreads();
+    // dQ: lane (g, n) holds columns DP/4*wave + 16*ct + 4*g .. +3 of head 16*ht + n
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const int col = 16 * ct + 4 * g;
-            if (DP == D || col < D) {
-                const uint2 ov = *reinterpret_cast<const uint2*>(o_row + col);
-                const float of[4] = {bf16_lo(ov.x), bf16_hi(ov.x), bf16_lo(ov.y), bf16_hi(ov.y)};
-                bf16x4 r;
+    for (int ht = 0; ht < 4; ++ht) {
+        const int h = 16 * ht + n;
+        if (h < heads) {
+            const uint16_t* o_row = o + ((size_t)i * heads + h) * D;
+            uint16_t* dq_h = dq + ((size_t)i * heads + h) * D;
+            const float sc = scale * corr_s[h];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = (__bf16)__builtin_fmaf(sc, of[e], acc[ct][e]);
-                *reinterpret_cast<bf16x4*>(dq_row + col) = r;
+            for (int ct = 0; ct < CQ; ++ct) {
+                const int col = DP / 4 * wave + 16 * ct + 4 * g;
+                if (DP == D || col < D) {
+                    const uint2 ov = *reinterpret_cast<const uint2*>(o_row + col);
+                    const float of[4] = {bf16_lo(ov.x), bf16_hi(ov.x), bf16_lo(ov.y), bf16_hi(ov.y)};
+                    bf16x4 r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = (__bf16)__builtin_fmaf(sc, of[e], acc[ht][ct][e]);
+                    *reinterpret_cast<bf16x4*>(dq_h + col) = r;
+                }
             }
         }
     }
