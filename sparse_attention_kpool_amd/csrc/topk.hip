@@ -313,8 +313,12 @@ __global__ __launch_bounds__(64 * TW_WAVES, R > 64 ? 2 : 5) void topk_wave_kerne
     // writes of lanes with nothing to count or keep (no branch around them)
     __shared__ __align__(16) int hist_all[TW_WAVES][NB + 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i = __builtin_amdgcn_readfirstlane(blockIdx.x * TW_WAVES + wave);
-    if (i >= num_q) return;
+    // rows are taken last first: under the causal mask the later queries of a
+    // document see more pools, so the longest rows start first and the launch
+    // ends on short ones
+    const int j = __builtin_amdgcn_readfirstlane(blockIdx.x * TW_WAVES + wave);
+    if (j >= num_q) return;
+    const int i = num_q - 1 - j;
     if (KP4) kpool = 4;
     int* hist = hist_all[wave];
     const int t = q_pos ? q_pos[i] : i;
