@@ -124,6 +124,26 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
     const int i = xcd_query(blockIdx.x, gridDim.x);
     const int wc = bwd_coef_stride(row_width);
 
+    // Q, dO and O of this lane's head (the B operands of S^T = K . Q^T and
+    // dP^T = K . dO^T, k-step ks: columns 32*ks + 8*g .. +7; O for delta = <dO, O>)
+    // and its LSE, loaded before the index row is compacted so that the two
+    // memory round trips overlap
+    bf16x8 qf[KS], gf[KS], ofr[KS];
+    float lse_h;
+    {
+        const size_t rowoff = ((size_t)i * heads + (head_ok ? head : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int col = 32 * ks + 8 * g;
+            const bool in = head_ok && (DP == D || col < D);
+            const int c = DP == D ? col : min(col, D - 8);
+            qf[ks] = in ? *reinterpret_cast<const bf16x8*>(q + rowoff + c) : bf16x8{};
+            gf[ks] = in ? *reinterpret_cast<const bf16x8*>(dout + rowoff + c) : bf16x8{};
+            ofr[ks] = in ? *reinterpret_cast<const bf16x8*>(o + rowoff + c) : bf16x8{};
+        }
+        lse_h = head_ok ? lse[(size_t)i * heads + head] : 0.f;
+    }
+
     const int n_valid = bwd_compact(indices + (size_t)i * row_width, row_width, num_kv, list, rcnt);
     if (n_valid == 0) {
         for (int e = tid; e < heads * D; e += NT) dq[(size_t)i * heads * D + e] = 0;
@@ -146,29 +166,15 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
         __syncthreads();
     }
 
-    // Q and dO of this lane's head as the B operands of S^T = K . Q^T and
-    // dP^T = K . dO^T (k-step ks: columns 32*ks + 8*g .. +7); delta = <dO, O>
-    bf16x8 qf[KS], gf[KS];
-    float delta = 0.f, lse2 = 0.f;
-    {
-        const size_t rowoff = ((size_t)i * heads + (head_ok ? head : 0)) * D;
+    float delta = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int col = 32 * ks + 8 * g;
-            const bool in = head_ok && (DP == D || col < D);
-            const int c = DP == D ? col : min(col, D - 8);
-            qf[ks] = in ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + rowoff + c)) : bf16x8{};
-            gf[ks] = in ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dout + rowoff + c)) : bf16x8{};
-            const bf16x8 of = in ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(o + rowoff + c))
-                                 : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) delta += (float)gf[ks][e] * (float)of[e];
-        }
-        // the four lanes of a head (g = 0..3) hold a quarter of the columns each
-        delta += shfl_xor(delta, 16);
-        delta += shfl_xor(delta, 32);
-        lse2 = head_ok ? lse[(size_t)i * heads + head] * 1.4426950408889634f : 0.f;
-    }
+        for (int e = 0; e < 8; ++e) delta += (float)gf[ks][e] * (float)ofr[ks][e];
+    // the four lanes of a head (g = 0..3) hold a quarter of the columns each
+    delta += shfl_xor(delta, 16);
+    delta += shfl_xor(delta, 32);
+    const float lse2 = lse_h * 1.4426950408889634f;
 
     // gather: as in the forward (wave w brings rows 16w .. 16w+15 of each tile)
     const uint32_t ring_lds = lds_addr(ring);
@@ -425,20 +431,9 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
     const int i = xcd_query(blockIdx.x, gridDim.x);
     const int wc = bwd_coef_stride(row_width);
 
-    const int n_valid = bwd_compact(indices + (size_t)i * row_width, row_width, num_kv, list, rcnt, jpos);
-    if (n_valid == 0) return;
-    const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
-
-    // A operands of dKV^T[cols, slots] = X^T[cols, coefs] . coef[coefs, slots] with X =
-    // [Q; dO] (coefficients 0..63: Q of head c, 64..127: dO of head c - 64): lane (g, n)
-    // of k-step kk holds coefficients 32*kk + 8*g .. +7 of column
-    // 32*(ct/2) + 8*(n/4) + 4*(ct%2) + n%4 of the wave's columns. Over a pair of
-    // column tiles, lane (g, n) of the products then holds the 8 consecutive
-    // columns 32*(ct/2) + 8*g .. +7 of its slot: one 16-byte store. Q, then dO + scale (delta_used - delta) Q (rounded to bf16),
-    // is staged in LDS (head h at row_base(h)) and read with the transposing read.
     // The coefficient tile 0 and every Q and dO chunk this thread stages are
-    // loaded first, all in flight together; head h's scale (delta_used - delta)
-    // comes with them.
+    // loaded first, all in flight together and before the index row is compacted
+    // (the round trips overlap); head h's scale (delta_used - delta) comes with them.
     constexpr int XC = 64 * (DP / 8) / NT;   // 16-byte chunks of Q (and of dO) per thread
     static_assert(XC * NT == 64 * (DP / 8), "whole chunks per thread");
     const uint16_t* crow = coef + (size_t)i * BW_COEF * wc;
@@ -450,7 +445,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
             cpre[u] = *reinterpret_cast<const u32x4*>(crow + (size_t)cr * wc + kt * MLA_TK + 32 * chalf + 8 * u);
     };
     load_tile(0);
-    uint4 qv[XC], gv[XC];
+    u32x4 qv[XC], gv[XC];
     float sc[XC];
     {
         const uint16_t* qq = q + (size_t)i * heads * D;
@@ -459,22 +454,33 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
         for (int u = 0; u < XC; ++u) {
             // 64 rows (heads) x DP columns; heads past `heads` and padded columns are zero
             const int c = tid + NT * u, h = c / (DP / 8), col = 8 * (c % (DP / 8));
-            qv[u] = gv[u] = make_uint4(0u, 0u, 0u, 0u);
+            qv[u] = gv[u] = u32x4{0u, 0u, 0u, 0u};
             sc[u] = 0.f;
             if (h < heads && col < D) {
-                qv[u] = *reinterpret_cast<const uint4*>(qq + (size_t)h * D + col);
-                gv[u] = *reinterpret_cast<const uint4*>(gg + (size_t)h * D + col);
+                qv[u] = *reinterpret_cast<const u32x4*>(qq + (size_t)h * D + col);
+                gv[u] = *reinterpret_cast<const u32x4*>(gg + (size_t)h * D + col);
                 sc[u] = scale * dcorr[(size_t)i * 64 + h];
             }
         }
     }
+    const int n_valid = bwd_compact(indices + (size_t)i * row_width, row_width, num_kv, list, rcnt, jpos);
+    if (n_valid == 0) return;
+    const int ntiles = (n_valid + MLA_TK - 1) / MLA_TK;
+
+    // A operands of dKV^T[cols, slots] = X^T[cols, coefs] . coef[coefs, slots] with X =
+    // [Q; dO] (coefficients 0..63: Q of head c, 64..127: dO of head c - 64): lane (g, n)
+    // of k-step kk holds coefficients 32*kk + 8*g .. +7 of column
+    // 32*(ct/2) + 8*(n/4) + 4*(ct%2) + n%4 of the wave's columns. Over a pair of
+    // column tiles, lane (g, n) of the products then holds the 8 consecutive
+    // columns 32*(ct/2) + 8*g .. +7 of its slot: one 16-byte store. Q, then dO + scale (delta_used - delta) Q (rounded to bf16),
+    // is staged in LDS (head h at row_base(h)) and read with the transposing read.
     bf16x8 xf[4][CTW];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int u = 0; u < XC; ++u) {
             const int c = tid + NT * u, h = c / (DP / 8), col = 8 * (c % (DP / 8));
-            uint4 v = qv[u];
+            u32x4 v = qv[u];
             if (half == 1) {
                 const uint32_t qw[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
                 uint32_t ow[4];
@@ -484,9 +490,9 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dkv_part_kernel(
                     const uint32_t hi = f32_to_bf16_rne(__builtin_fmaf(sc[u], bf16_hi(qw[e]), bf16_hi(gw[e])));
                     ow[e] = lo | (hi << 16);
                 }
-                v = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                v = u32x4{ow[0], ow[1], ow[2], ow[3]};
             }
-            *reinterpret_cast<uint4*>(xs + row_base<RB>(h) + 2 * col) = v;
+            *reinterpret_cast<u32x4*>(xs + row_base<RB>(h) + 2 * col) = v;
         }
         __syncthreads();
 #pragma unroll
