@@ -21,16 +21,19 @@
 // the same difference).
 //
 // Two kernels, one workgroup (4 waves, one per SIMD) per query each:
-//  * mla_bwd_dq_kernel: wave w owns heads 16w .. 16w+15 and every row of a
-//    64-row tile. The rows are gathered into LDS exactly as in the forward. Per
-//    tile: S^T = K . Q^T and dP^T = K . dO^T (each K fragment feeds both MFMAs),
-//    then p and scale*ds in registers, then dQ^T += K^T . (scale ds)^T over all
-//    columns (K^T read with the transposing LDS read). The K rows enter the QK
-//    MFMAs in a permuted order so that each lane's S values are the ones it
-//    feeds to the dQ MFMA. dQ stays in registers for the whole row (no merge:
-//    a wave owns its heads). scale*ds and p of every valid slot are written to
-//    the workspace, head-major: coef[query][h][slot] (h < 64: scale*ds,
-//    64 + h: p), bf16.
+//  * mla_bwd_dq_kernel: for S, dP and ds, wave w owns heads 16w .. 16w+15 and
+//    every row of a 64-row tile. The rows are gathered into LDS exactly as in
+//    the forward. Per tile: S^T = K . Q^T and dP^T = K . dO^T (each K fragment
+//    feeds both MFMAs), then p and scale*ds in registers; the ds values go
+//    through LDS, and wave w adds dQ^T += K^T . (scale ds)^T for the w-th
+//    quarter of the latent columns (padded to at least 128) of all 64 heads
+//    (K^T read with the transposing LDS read, each fragment feeding four head
+//    tiles). The K rows enter the QK
+//    MFMAs in a permuted order so that each lane's ds values are the B operand
+//    layout of the dQ MFMA. dQ stays in registers for the whole row (no merge:
+//    the waves own disjoint columns). scale*ds and p of every valid slot are
+//    written to the workspace, head-major: coef[query][h][slot] (h < 64:
+//    scale*ds, 64 + h: p), bf16.
 //  * dKV (below): each valid slot's dKV row is coef^T . [Q; dO], a product
 //    over its 128 coefficients (mla_bwd_dkv_part_kernel, MFMA); the rows are
 //    then summed per latent row in a fixed order (a stable sort of the slots
