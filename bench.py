@@ -297,7 +297,7 @@ def main():
         bwd = {"ms_median": bmed, "ms_min": float(min(bt)), "tflops": btf, "frac_bf16_peak": btf / BF16_PEAK_TFLOPS,
                "algorithmic": f"10*H*D = {10 * s.H * s.D} flop per valid slot x {wc['sum_n_valid']} slots",
                "workspace_bytes": bws,
-               "kernels": "per chunk of 2048 queries: mla_bwd_dq_kernel, mla_bwd_dkv_part_kernel, a radix sort of "
+               "kernels": "per chunk of 8192 queries: mla_bwd_dq_kernel, mla_bwd_dkv_part_kernel, a radix sort of "
                           "the slots by row, the ordered dKV reduction (+ dKV zero fill)"}
         log(f"sparse MLA backward: {bmed:.3f} ms median, {btf:.1f} TFLOP/s ({100 * btf / BF16_PEAK_TFLOPS:.1f}% "
             f"bf16 peak)")

@@ -394,7 +394,7 @@ size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t d_latent, int32_t row_w
  * bf16 inputs, fp32 accumulation; p and ds enter the products rounded to bf16,
  * and so does each (query, entry) term of d_kv before the sum over queries.
  * d_kv is written in full; its sum over queries runs in a fixed order (queries
- * in chunks of 2048, within a chunk by position in the index rows), so d_q and
+ * in chunks of 8192, within a chunk by position in the index rows), so d_q and
  * d_kv are bit-reproducible. A row with no valid entry gives d_q = 0.
  *
  *   q, kv, indices  as passed to sparse_mla_fwd
@@ -404,10 +404,10 @@ size_t kp_mla_bwd_workspace_bytes(int32_t num_q, int32_t d_latent, int32_t row_w
  *   d_q             device bf16 [num_q, heads, d_latent]   (out)
  *   d_kv            device fp32 [num_kv, d_latent]         (out)
  *   workspace       device memory of kp_mla_bwd_workspace_bytes(num_q, d_latent,
- *                   row_width) bytes, 256-byte aligned: per chunk of up to 2048
+ *                   row_width) bytes, 256-byte aligned: per chunk of up to 8192
  *                   queries, the per-slot softmax coefficients, the per-slot
  *                   d_kv terms (bf16), the sort of the slots by row and the
- *                   reduction's carries (about 5.9 GB at 2048 x 2176 x 512)
+ *                   reduction's carries (about 23.7 GB at 8192 x 2176 x 512)
  */
 kp_status sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
                          const uint16_t* out, const float* lse, const uint16_t* d_out,

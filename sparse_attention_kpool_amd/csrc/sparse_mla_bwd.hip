@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64 * MLA_NW, 1) void mla_bwd_dq_kernel(
 //     adds each into dKV; a run that crosses a tile boundary leaves per-tile
 //     partial sums that bwd_dkv_fixup_kernel adds in tile order.
 // The chunks run in order, so dKV is bit-reproducible.
-constexpr int BW_QC = 2048;   // queries per chunk
+constexpr int BW_QC = 8192;   // queries per chunk
 
 // LDS layout of a coefficient tile (128 rows of 64 slots, 128 bytes each): row
 // r at byte r*176 + 16*(r & 1); the transposing reads of the B operand (two

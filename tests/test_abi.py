@@ -63,14 +63,16 @@ def test_workspace_size(L):
     pw = L.kp_indexer_paged_workspace_bytes(64, 3, 32, 128)
     assert pw % 256 == 0 and fused < pw <= fused + 256
     assert L.kp_indexer_paged_workspace_bytes(0, 3, 32, 128) == 0
-    # the backward: one chunk of at most 2048 queries (coefficients, bf16 d_kv terms,
+    # the backward: one chunk of at most 8192 queries (coefficients, bf16 d_kv terms,
     # the sort's keys and positions, carries, delta corrections), the same for any larger num_q
-    bw = L.kp_mla_bwd_workspace_bytes(2048, 512, 2176)
-    E = 2048 * 2176
+    QC = 8192
+    bw = L.kp_mla_bwd_workspace_bytes(QC, 512, 2176)
+    E = QC * 2176
     assert bw % 256 == 0
-    assert 2048 * 128 * 2176 * 2 + E * 512 * 2 + 4 * E * 4 <= bw < 2048 * 128 * 2176 * 2 + E * 512 * 2 + 4 * E * 4 \
-        + (E // 128 + 1) * (2 * 512 * 4 + 8) + 256 * (E // 4096 + 2) * 4 + 2048 * 64 * 4 + 4096
+    assert QC * 128 * 2176 * 2 + E * 512 * 2 + 4 * E * 4 <= bw < QC * 128 * 2176 * 2 + E * 512 * 2 + 4 * E * 4 \
+        + (E // 128 + 1) * (2 * 512 * 4 + 8) + 256 * (E // 4096 + 2) * 4 + QC * 64 * 4 + 4096
     assert L.kp_mla_bwd_workspace_bytes(32768, 512, 2176) == bw
+    assert L.kp_mla_bwd_workspace_bytes(2048, 512, 2176) < bw
     assert L.kp_mla_bwd_workspace_bytes(24, 64, 256) < L.kp_mla_bwd_workspace_bytes(24, 512, 256)
     assert L.kp_mla_bwd_workspace_bytes(24, 576, 256) == 0
     assert L.kp_mla_bwd_workspace_bytes(0, 512, 256) == 0

@@ -153,9 +153,9 @@ def test_bwd_workload_rows(K, oracle_mod, name):
 
 
 def test_bwd_query_chunks(K, oracle_mod):
-    """More queries than one chunk of the dKV sum (2048): the chunks' sums are
+    """More queries than one chunk of the dKV sum (8192): the chunks' sums are
     added in order; rows named by queries of both chunks, long runs included."""
-    q, kv, idx, d_out = _rand_case(31, 2100, 8, 64, 300, 64, "heavy")
+    q, kv, idx, d_out = _rand_case(31, 8300, 8, 64, 300, 64, "heavy")
     _log("bwd chunks", q.shape, idx.shape)
     _run(K, oracle_mod, q, kv, idx, d_out, 1 / 8, "chunks")
 
